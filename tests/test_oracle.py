@@ -1,0 +1,510 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each test ties an oracle function to a value the pages print, a closed form
+derived by hand, a special case that reduces to a library routine, an
+invariant, or exact brute force on tiny inputs.  The cases are chosen so that
+a plausible slip (wrong rounding tie, dropped term, wrong summation order or
+start, wrong shard bound, transposed word, off-by-one slot) fails at least one.
+
+Sources: [SGLv1] "SGLang Custom AllReduce v1 thread model" (todaynews.cc);
+[NCCL14] "NCCL expert course 14: Simple, LL, LL128 wire formats"
+(blog.cptz.space); [JITAR] "0-custom-all-reduce" (obnotes-4iw.pages.dev);
+[TRIAR] "Triton + Symmetric Memory fused AllReduce + RMSNorm" (riverclouds.net).
+"""
+import math
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+BF16_ONE = 0x3F80
+BF16_2P24 = 0x4B80       # 2^24
+BF16_M2P24 = 0xCB80      # -2^24
+
+
+def f32_bits(v: float) -> int:
+    return struct.unpack("<I", struct.pack("<f", v))[0]
+
+
+def bf16_value(b: int) -> Fraction:
+    return Fraction(struct.unpack("<f", struct.pack("<I", b << 16))[0])
+
+
+# ---------------------------------------------------------------------------
+# bf16 rounding  ([JITAR] section 4: widen to fp32, narrow once, nearest)
+# ---------------------------------------------------------------------------
+def test_bf16_rne_matches_torch_cast_exhaustively_on_low_halves():
+    """fp32 -> bf16 must equal torch's CPU cast (an IEEE round-to-nearest-even
+    library routine) on every low half-word under 263 high half-words."""
+    his = sorted(set(range(0, 65536, 257)) |
+                 {0x0000, 0x0080, 0x3F80, 0x7F7F, 0x7F80, 0x7FC0, 0x8000, 0xFF80})
+    lo = np.arange(65536, dtype=np.uint32)
+    bits = (np.array(his, np.uint32)[:, None] << 16 | lo[None, :]).reshape(-1)
+    x = bits.view(np.float32)
+    got = orc.bf16_rne(x)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], want[~nan])
+    # NaN stays NaN (exponent all ones, nonzero fraction) and keeps its sign.
+    g = got[nan]
+    assert np.all((g & 0x7F80) == 0x7F80) and np.all((g & 0x7F) != 0)
+    assert np.array_equal(g >> 15, (bits[nan] >> 31).astype(np.uint16))
+
+
+@pytest.mark.parametrize("bits,want", [
+    (0x3F808000, 0x3F80),   # exact tie, even kept part -> stays
+    (0x3F818000, 0x3F82),   # exact tie, odd kept part -> rounds up to even
+    (0x3F808001, 0x3F81),   # just above the tie
+    (0x3F807FFF, 0x3F80),   # just below the tie
+    (0x7F7FFFFF, 0x7F80),   # overflow to +inf
+    (0xFF7FFFFF, 0xFF80),   # overflow to -inf
+    (0x807FFFFF, 0x8080),   # largest negative denormal rounds to -min normal
+    (0x00008000, 0x0000),   # tie at the bottom, even -> zero
+    (0x00018000, 0x0002),   # denormal tie, odd -> up
+    (0x7F800000, 0x7F80),   # +inf
+    (0x80000000, 0x8000),   # -0.0 kept
+])
+def test_bf16_rne_hand_cases(bits, want):
+    x = np.array([bits], np.uint32).view(np.float32)
+    assert int(orc.bf16_rne(x)[0]) == want
+
+
+def _nearest_even_check(x: Fraction, b: int):
+    """b is the correct round-to-nearest-even bf16 of x (exact rationals)."""
+    sign = -1 if x < 0 else 1
+    assert (b >> 15) == (1 if sign < 0 else 0)
+    mag = b & 0x7FFF
+    ax = abs(x)
+    maxf = bf16_value(0x7F7F)
+    if mag == 0x7F80:
+        # overflow: x lies at or beyond the midpoint of max and 2^128
+        assert ax >= (maxf + Fraction(2) ** 128) / 2
+        return
+    v = bf16_value(mag)
+    d = abs(ax - v)
+    for nb in (mag - 1, mag + 1):
+        if nb < 0 or nb >= 0x7F80:
+            continue
+        dn = abs(ax - bf16_value(nb))
+        assert d <= dn
+        if d == dn:                        # tie: the kept code is even
+            assert mag % 2 == 0
+
+
+def test_bf16_from_f64_is_nearest_even_by_exact_brute_force():
+    g = np.random.default_rng(7)
+    xs = []
+    for _ in range(3000):
+        m = g.uniform(1.0, 2.0)
+        e = int(g.integers(-140, 129))
+        xs.append(math.ldexp(m, e) * (1 if g.random() < 0.5 else -1))
+    # exact ties and near-ties: bf16 midpoints, and a hair either side
+    for _ in range(1000):
+        b = int(g.integers(0x0001, 0x7F7F))
+        mid = (bf16_value(b) + bf16_value(b + 1)) / 2
+        xs += [float(mid), math.nextafter(float(mid), 0), math.nextafter(float(mid), math.inf)]
+    xs += [3.3961e38, 3.3958e38, -3.4e38, 1e-45, 9.2e-41, 2.0 ** -133, 2.0 ** -134,
+           3 * 2.0 ** -135]
+    got = orc.bf16_from_f64(np.array(xs))
+    for x, b in zip(xs, got):
+        _nearest_even_check(Fraction(x), int(b))
+
+
+def test_bf16_from_f64_agrees_with_fp32_rounding_on_floats():
+    g = np.random.default_rng(8)
+    bits = g.integers(0, 2 ** 32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x)]
+    assert np.array_equal(orc.bf16_from_f64(x.astype(np.float64)), orc.bf16_rne(x))
+
+
+# ---------------------------------------------------------------------------
+# one-stage reduce  ([SGLv1] "1stage: full kernel and timeline")
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("W", range(2, 9))
+def test_1stage_closed_forms(W):
+    n = 64
+    ones = [np.full(n, BF16_ONE, np.uint16) for _ in range(W)]
+    assert np.all(orc.bf16_to_f32(orc.reduce_1stage(ones)) == W)
+    # x_r = r + 1  ->  W (W + 1) / 2 exactly
+    xs = [np.full(n, f32_bits(r + 1.0) >> 16, np.uint16) for r in range(W)]
+    assert np.all(orc.bf16_to_f32(orc.reduce_1stage(xs)) == W * (W + 1) // 2)
+    # all -0.0 -> -0.0: the sum starts from rank 0's value, not from +0.0
+    negz = [np.full(n, 0x8000, np.uint16) for _ in range(W)]
+    assert np.all(orc.reduce_1stage(negz) == 0x8000)
+    # one +0.0 among -0.0 -> +0.0
+    mixed = negz[:-1] + [np.zeros(n, np.uint16)]
+    assert np.all(orc.reduce_1stage(mixed) == 0x0000)
+
+
+def test_1stage_rank_order_is_revealed_by_absorption():
+    """x = (1, 2^24, 1, -2^24): in fp32, 1 + 2^24 is a tie that rounds back to
+    2^24, so the rank-order sum ((1 + 2^24) + 1) - 2^24 is 0.  A tree order
+    (1 + 2^24) + (1 - 2^24) gives 1 and the reverse order gives 2."""
+    vals = [BF16_ONE, BF16_2P24, BF16_ONE, BF16_M2P24]
+    xs = [np.full(16, v, np.uint16) for v in vals]
+    assert np.all(orc.reduce_1stage(xs) == 0x0000)
+    assert np.all(orc.bf16_to_f32(orc.reduce_1stage(xs[::-1])) == 2.0)
+
+
+def test_1stage_w2_equals_rounded_exact_sum():
+    """For two bf16 values whose exponents differ by at most 15 the fp32 sum
+    is exact, so the result is the exact sum rounded once; torch's CPU cast
+    (float64 -> float32 exact here, then RNE to bf16) supplies the rounding."""
+    g = np.random.default_rng(11)
+    x0 = orc.bf16_rne(g.standard_normal(50_000).astype(np.float32))
+    x1 = orc.bf16_rne((g.standard_normal(50_000) * 10.0 ** g.integers(-3, 4, 50_000))
+                      .astype(np.float32))
+    a, b = orc.bf16_to_f32(x0).astype(np.float64), orc.bf16_to_f32(x1).astype(np.float64)
+    ea = np.frexp(a)[1]
+    eb = np.frexp(b)[1]
+    keep = (np.abs(ea - eb) <= 15) & (a != 0) & (b != 0)
+    exact = torch.from_numpy((a + b)[keep])
+    want = exact.float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = orc.reduce_1stage([x0, x1])[keep]
+    assert keep.sum() > 40_000
+    assert np.array_equal(got, want)
+
+
+def test_1stage_error_within_bound_of_exact_sum():
+    """The fp32 chain of W-1 adds then one bf16 rounding is within
+    (W-1) * 2^-24 * sum|x| + half a bf16 ulp of the exact sum."""
+    g = np.random.default_rng(12)
+    W, n = 8, 20_000
+    xs = [orc.bf16_rne(g.standard_normal(n).astype(np.float32)) for _ in range(W)]
+    got = orc.bf16_to_f32(orc.reduce_1stage(xs)).astype(np.float64)
+    vals = np.stack([orc.bf16_to_f32(x).astype(np.float64) for x in xs])
+    exact = vals.sum(0)                     # float64 sum of 8 bf16: exact
+    bound = (W - 1) * 2.0 ** -24 * np.abs(vals).sum(0) * 1.0001
+    half_ulp = np.abs(exact + bound) * 2.0 ** -8
+    assert np.all(np.abs(got - exact) <= bound + half_ulp + 1e-45)
+
+
+# ---------------------------------------------------------------------------
+# two-stage reduce  ([SGLv1] "2stage: sharding, rotation, no exit barrier")
+# ---------------------------------------------------------------------------
+def test_2stage_partition_numbers_printed_on_the_page():
+    # 512 KB of bf16 at W=8: 32768 packs, part = 4096 ([SGLv1] worked example)
+    n = 512 * 1024 // 2
+    assert orc.shard_range(n, 8, 0) == (0, 4096)
+    assert orc.shard_range(n, 8, 7) == (7 * 4096, 32768)
+    # the 8 MB cap: 524288 packs, part = 65536
+    assert orc.shard_range(4_194_304, 8, 3) == (3 * 65536, 4 * 65536)
+    # remainder goes to the last shard: 45 packs over 8 -> part 5, last 10
+    assert orc.shard_range(45 * 8, 8, 6) == (30, 35)
+    assert orc.shard_range(45 * 8, 8, 7) == (35, 45)
+    # fewer packs than shards: everything is the last shard's
+    assert orc.shard_range(3 * 8, 4, 0) == (0, 0)
+    assert orc.shard_range(3 * 8, 4, 3) == (0, 3)
+
+
+def test_2stage_rotated_order_hand_derived():
+    """x = (1, 2^24, 1, -2^24) at every element, W=4, 4 packs (one per shard).
+    Owner s sums from x_s onwards:
+      s=0: ((1 + 2^24) + 1) - 2^24 = 0
+      s=1: ((2^24 + 1) - 2^24) + 1 = 1
+      s=2: ((1 - 2^24) + 1) + 2^24 = 2
+      s=3: ((-2^24 + 1) + 2^24) + 1 = 2
+    and with the rank order every shard is 0."""
+    vals = [BF16_ONE, BF16_2P24, BF16_ONE, BF16_M2P24]
+    xs = [np.full(32, v, np.uint16) for v in vals]
+    got = orc.bf16_to_f32(orc.reduce_2stage(xs)).reshape(4, 8)
+    assert np.array_equal(got, np.repeat(np.array([[0.0], [1.0], [2.0], [2.0]]), 8, 1))
+    assert np.all(orc.reduce_2stage(xs, rank_order=True) == 0)
+    # the scatter/gather pieces compose to the same result
+    tmps = [orc.reduce_scatter(xs, s) for s in range(4)]
+    assert [t.size for t in tmps] == [8, 8, 8, 8]
+    assert np.array_equal(orc.all_gather(tmps, 32), orc.reduce_2stage(xs))
+
+
+@pytest.mark.parametrize("P", [5, 45, 64, 1027])
+def test_2stage_w2_equals_1stage(P):
+    """With two ranks the rotated order is x0+x1 or x1+x0, equal by fp32
+    commutativity, so the two-stage result is the one-stage result."""
+    g = np.random.default_rng(P)
+    xs = [orc.bf16_rne(g.standard_normal(P * 8).astype(np.float32)) for _ in range(2)]
+    assert np.array_equal(orc.reduce_2stage(xs), orc.reduce_1stage(xs))
+
+
+@pytest.mark.parametrize("W", [3, 4, 8])
+def test_2stage_rank_order_flag_equals_1stage_and_ones(W):
+    g = np.random.default_rng(W)
+    xs = [orc.bf16_rne(g.standard_normal(45 * 8).astype(np.float32)) for _ in range(W)]
+    assert np.array_equal(orc.reduce_2stage(xs, rank_order=True), orc.reduce_1stage(xs))
+    ones = [np.full(45 * 8, BF16_ONE, np.uint16) for _ in range(W)]
+    assert np.all(orc.bf16_to_f32(orc.reduce_2stage(ones)) == W)
+
+
+# ---------------------------------------------------------------------------
+# fused all-reduce + residual + RMSNorm  ([TRIAR] "what this operator computes")
+# ---------------------------------------------------------------------------
+def _fused(xs, res, w, eps=1e-6):
+    return orc.fused_residual_rmsnorm(xs, res, w, eps)
+
+
+@pytest.mark.parametrize("c,W", [(1.0, 4), (-1.0, 4), (3.0, 2), (0.25, 8)])
+def test_fused_constant_row_returns_weight(c, W):
+    """h = c at every position: rms = 1/sqrt(c^2 + eps), (h*rms) differs from
+    sign(c) by ~eps/(2c^2) << half a bf16 ulp, so norm_out = sign(c) * w."""
+    M, N = 3, 2048
+    g = np.random.default_rng(5)
+    w = orc.bf16_rne(g.normal(1.0, 0.1, N).astype(np.float32))
+    xs = [np.full((M, N), f32_bits(c) >> 16, np.uint16)] + \
+         [np.zeros((M, N), np.uint16) for _ in range(W - 1)]
+    res = np.zeros((M, N), np.uint16)
+    ro, no, ne = _fused(xs, res, w)
+    assert np.all(ro == (f32_bits(c) >> 16))
+    want = w if c > 0 else (w ^ 0x8000)
+    assert np.array_equal(no, np.broadcast_to(want, (M, N)))
+
+
+def test_fused_all_ones_w4():
+    M, N, W = 2, 1024, 4
+    w = orc.bf16_rne(np.linspace(0.5, 1.5, N).astype(np.float32))
+    xs = [np.full((M, N), BF16_ONE, np.uint16) for _ in range(W)]
+    res = np.zeros((M, N), np.uint16)
+    ro, no, _ = _fused(xs, res, w)
+    assert np.all(orc.bf16_to_f32(ro) == 4.0)
+    assert np.array_equal(no, np.broadcast_to(w, (M, N)))
+
+
+@pytest.mark.parametrize("c", [2.0 ** -12, 2.0 ** -10, 1e-3])
+def test_fused_constant_row_where_eps_matters(c):
+    """Closed form y = c / sqrt(c^2 + eps) * w_j; at these c, eps is 1..16x
+    c^2, so a dropped or misplaced eps changes the value visibly."""
+    M, N, W, eps = 1, 256, 2, 1e-6
+    cb = orc.bf16_rne(np.array([c], np.float32))[0]
+    cv = float(orc.bf16_to_f32(np.array([cb]))[0])
+    w = orc.bf16_rne(np.linspace(-2, 2, N).astype(np.float32))
+    xs = [np.full((M, N), cb, np.uint16), np.zeros((M, N), np.uint16)]
+    _, no, ne = _fused(xs, np.zeros((M, N), np.uint16), w, eps)
+    want = cv / math.sqrt(cv * cv + eps) * orc.bf16_to_f32(w).astype(np.float64)
+    assert np.allclose(ne[0], want, rtol=1e-13, atol=0)
+
+
+def test_fused_reduces_to_torch_rms_norm_when_peers_are_zero():
+    """With x_1..x_{W-1} = 0 the all-reduce is x_0 exactly, so the operator is
+    h = fp32(x_0 + residual) followed by torch's rms_norm (library routine)."""
+    W, M, N, eps = 4, 16, 2048, 1e-6
+    g = np.random.default_rng(21)
+    x0 = orc.bf16_rne(g.standard_normal((M, N)).astype(np.float32))
+    res = orc.bf16_rne(g.standard_normal((M, N)).astype(np.float32))
+    w = orc.bf16_rne(g.normal(1.0, 0.1, N).astype(np.float32))
+    xs = [x0] + [np.zeros((M, N), np.uint16) for _ in range(W - 1)]
+    ro, no, ne = _fused(xs, res, w, eps)
+    h = torch.from_numpy(orc.bf16_to_f32(x0)) + torch.from_numpy(orc.bf16_to_f32(res))
+    want_ro = h.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ro, want_ro)
+    wt = torch.from_numpy(orc.bf16_to_f32(w)).double()
+    want = torch.nn.functional.rms_norm(h.double(), (N,), wt, eps).numpy()
+    assert np.allclose(ne, want, rtol=1e-12, atol=1e-300)
+    # norm_out is the nearest bf16 of the exact value
+    assert np.array_equal(no, orc.bf16_from_f64(ne))
+
+
+def test_fused_power_of_two_scale_invariance_eps0():
+    """Scaling x and residual by 2^k scales residual_out by 2^k exactly and,
+    with eps = 0, leaves norm_out unchanged."""
+    W, M, N = 4, 4, 512
+    g = np.random.default_rng(22)
+    xs = [orc.bf16_rne(g.standard_normal((M, N)).astype(np.float32)) for _ in range(W)]
+    res = orc.bf16_rne(g.standard_normal((M, N)).astype(np.float32))
+    w = orc.bf16_rne(g.normal(1.0, 0.1, N).astype(np.float32))
+    ro, no, _ = _fused(xs, res, w, 0.0)
+    k = 5
+    sc = lambda a: np.where((a & 0x7F80) != 0, a + (k << 7), a).astype(np.uint16)  # noqa: E731
+    ro2, no2, _ = _fused([sc(x) for x in xs], sc(res), w, 0.0)
+    r1, r2 = orc.bf16_to_f32(ro), orc.bf16_to_f32(ro2)
+    assert np.array_equal(r2, r1 * np.float32(2 ** k))
+    assert np.array_equal(no2, no)
+
+
+def test_fused_residual_out_equals_1stage_plus_residual():
+    """residual_out is the one-stage sum (kept in fp32) plus the residual: for
+    a zero residual it is the one-stage result exactly."""
+    W, M, N = 4, 8, 2048
+    g = np.random.default_rng(23)
+    xs = [orc.bf16_rne(g.standard_normal((M, N)).astype(np.float32)) for _ in range(W)]
+    ro, _, _ = _fused(xs, np.zeros((M, N), np.uint16),
+                      np.full(N, BF16_ONE, np.uint16))
+    assert np.array_equal(ro.reshape(-1), orc.reduce_1stage([x.reshape(-1) for x in xs]))
+
+
+# ---------------------------------------------------------------------------
+# LL / LL128 wire formats ([NCCL14])
+# ---------------------------------------------------------------------------
+def _read_golden(name):
+    meta, rows = {}, {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            parts = line.split()
+            if parts[0].isdigit():
+                rows[int(parts[0])] = [int(p, 16) for p in parts[1:]]
+            else:
+                meta[parts[0]] = parts[1:]
+    return meta, rows
+
+
+def test_ll_pack_golden_bytes():
+    meta, rows = _read_golden("ll_pack_n5.txt")
+    src = np.array([float(v) for v in meta["payload_f32"]], np.float32)
+    fifo = np.full(8 * 16, 0xEE, np.uint8)
+    orc.ll_pack(src, fifo, int(meta["step_lines"][0]), int(meta["first_step"][0]))
+    words = fifo.view("<u4").reshape(8, 4)
+    for i in range(8):
+        assert list(words[i]) == rows[i], i
+
+
+def test_ll128_pack_golden_bytes():
+    meta, rows = _read_golden("ll128_pack_n31.txt")
+    a, b = (int(v) for v in meta["payload_f32_range"])
+    src = np.arange(a, b + 1, dtype=np.float32)
+    fifo = np.full(8 * 128, 0xEE, np.uint8)
+    orc.ll128_pack(src, fifo, int(meta["step_lines"][0]), int(meta["first_step"][0]))
+    words = fifo.view("<u4").reshape(8, 32)
+    for i in range(8):
+        assert list(words[i]) == rows[i], i
+
+
+def test_wire_geometry_matches_printed_buffer_table():
+    """[NCCL14] "default buffers and effective data per step": LL 524288 B
+    wire buffer -> 65536 B per step -> 32768 data B; LL128 4915200 B ->
+    614400 B per step -> 576000 data B; payload efficiency 8/16 and 120/128."""
+    ll_step_lines = 524288 // 8 // 16
+    ll128_step_lines = 4915200 // 8 // 128
+    assert (ll_step_lines, ll128_step_lines) == (4096, 4800)
+    # a step's worth of data fills exactly one step's worth of lines
+    assert orc.ll_lines(32768 // 4) == ll_step_lines
+    assert orc.ll128_lines(576000 // 4) == ll128_step_lines
+    assert orc.ll_lines(32768 // 4 + 1) == ll_step_lines + 1
+    assert orc.ll128_lines(576000 // 4 + 1) == ll128_step_lines + 1
+    # efficiency measured on the packed bytes: flags and data of one step
+    n = 32768 // 4
+    fifo = np.zeros(8 * ll_step_lines * 16, np.uint8)
+    orc.ll_pack(np.ones(n, np.float32), fifo, ll_step_lines)
+    used = fifo[: ll_step_lines * 16].view("<u4").reshape(-1, 4)
+    assert np.all(used[:, 1] == 1) and np.all(used[:, 3] == 1)
+    assert Fraction(n * 4, ll_step_lines * 16) == Fraction(8, 16)
+    n = 576000 // 4
+    fifo = np.zeros(8 * ll128_step_lines * 128, np.uint8)
+    orc.ll128_pack(np.ones(n, np.float32), fifo, ll128_step_lines)
+    used = fifo[: ll128_step_lines * 128].view("<u8").reshape(-1, 16)
+    assert np.all(used[:, 15] == 1)
+    assert Fraction(n * 4, ll128_step_lines * 128) == Fraction(120, 128)
+
+
+@pytest.mark.parametrize("fmt", ["ll", "ll128"])
+@pytest.mark.parametrize("n,step_lines,first_step", [
+    (1, 1, 0), (2, 1, 5), (29, 1, 0), (30, 2, 3), (31, 1, 7), (1000, 200, 0),
+    (1013, 127, 9), (4096, 512, 2 ** 32 - 3)])
+def test_round_trip_single_fifo(fmt, n, step_lines, first_step):
+    pack = orc.ll_pack if fmt == "ll" else orc.ll128_pack
+    unpack = orc.ll_unpack_reduce if fmt == "ll" else orc.ll128_unpack_reduce
+    lines = (orc.ll_lines if fmt == "ll" else orc.ll128_lines)(n)
+    size = 16 if fmt == "ll" else 128
+    step_lines = max(step_lines, -(-lines // 8))   # one call spans <= 8 steps
+    g = np.random.default_rng(n)
+    src = g.standard_normal(n).astype(np.float32)
+    src[::7] = -0.0
+    fifo = np.zeros(8 * step_lines * size, np.uint8)
+    pack(src, fifo, step_lines, first_step)
+    out, valid, bad = unpack([fifo], n, step_lines, first_step)
+    assert bad == 0 and valid.all()
+    assert np.array_equal(out.view(np.uint32), src.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", ["ll", "ll128"])
+def test_decode_reduce_small_integers_and_order(fmt):
+    pack = orc.ll_pack if fmt == "ll" else orc.ll128_pack
+    unpack = orc.ll_unpack_reduce if fmt == "ll" else orc.ll128_unpack_reduce
+    size = 16 if fmt == "ll" else 128
+    n, sl = 301, 64
+    g = np.random.default_rng(3)
+    x = g.integers(-100, 100, n).astype(np.float32)
+    W = 4
+    fifos = []
+    for _ in range(W):
+        f = np.zeros(8 * sl * size, np.uint8)
+        pack(x, f, sl)
+        fifos.append(f)
+    out, valid, bad = unpack(fifos, n, sl)
+    assert bad == 0 and np.array_equal(out, W * x)
+    # FIFO order: (1, 2^24, 1, -2^24) sums to 0 in order 0..3 (see 1stage)
+    vals = [1.0, 2.0 ** 24, 1.0, -(2.0 ** 24)]
+    fifos = []
+    for v in vals:
+        f = np.zeros(8 * sl * size, np.uint8)
+        pack(np.full(n, v, np.float32), f, sl)
+        fifos.append(f)
+    out, _, _ = unpack(fifos, n, sl)
+    assert np.all(out == 0.0)
+    out, _, _ = unpack(fifos[::-1], n, sl)
+    assert np.all(out == 2.0)
+
+
+@pytest.mark.parametrize("fmt", ["ll", "ll128"])
+def test_decode_counts_planted_corruption(fmt):
+    """[NCCL14]: a line is ready only when its flag(s) equal step + 1; LL needs
+    both flags.  Bad (FIFO, line) pairs are counted exactly."""
+    pack = orc.ll_pack if fmt == "ll" else orc.ll128_pack
+    unpack = orc.ll_unpack_reduce if fmt == "ll" else orc.ll128_unpack_reduce
+    nlines = orc.ll_lines if fmt == "ll" else orc.ll128_lines
+    size = 16 if fmt == "ll" else 128
+    per_line = 2 if fmt == "ll" else 30
+    n, sl, W = 997, 80, 3
+    L = nlines(n)
+    assert L <= 8 * sl
+    g = np.random.default_rng(4)
+    fifos = []
+    for _ in range(W):
+        f = np.zeros(8 * sl * size, np.uint8)
+        pack(g.standard_normal(n).astype(np.float32), f, sl, 1)
+        fifos.append(f)
+    # one flag word wrong in FIFO 1, line 5 (LL: flag2 only; flag1 stays right)
+    bad_fifo = [f.copy() for f in fifos]
+    wire5 = ((1 + 5 // sl) % 8) * sl + 5 % sl     # where logical line 5 sits
+    if fmt == "ll":
+        bad_fifo[1][wire5 * 16 + 12] ^= 0x01
+    else:
+        bad_fifo[1][wire5 * 128 + 120] ^= 0x01
+    out, valid, bad = unpack(bad_fifo, n, sl, 1)
+    assert bad == 1
+    assert not valid[5 * per_line:6 * per_line].any()
+    assert valid[:5 * per_line].all() and valid[6 * per_line:].all()
+    # a stale round: expected flags one lap (8 steps) ahead -> all bad
+    _, valid, bad = unpack(fifos, n, sl, 1 + 8)
+    assert bad == W * L and not valid.any()
+    # a zeroed FIFO never validates (flags are step + 1 >= 1)
+    zeros = [np.zeros_like(f) for f in fifos]
+    _, _, bad = unpack(zeros, n, sl, 0)
+    assert bad == W * L
+
+
+@pytest.mark.parametrize("fmt", ["ll", "ll128"])
+@pytest.mark.parametrize("offset", [4, 8, 12])
+def test_pack_from_unaligned_source_gives_same_wire(fmt, offset):
+    pack = orc.ll_pack if fmt == "ll" else orc.ll128_pack
+    size = 16 if fmt == "ll" else 128
+    n, sl = 1013, 200
+    g = np.random.default_rng(offset)
+    x = g.standard_normal(n).astype(np.float32)
+    raw = np.zeros(4 * n + 64, np.uint8)
+    base = (-raw.ctypes.data) % 16
+    view = raw[base + offset: base + offset + 4 * n].view(np.float32)
+    view[:] = x
+    assert view.ctypes.data % 16 == offset
+    a = np.zeros(8 * sl * size, np.uint8)
+    b = np.zeros(8 * sl * size, np.uint8)
+    pack(x, a, sl)
+    pack(view, b, sl)
+    assert np.array_equal(a, b)
