@@ -1,0 +1,38 @@
+// Kernel launchers behind the C ABI (internal C++ interface of libar).
+// Each launcher assumes its arguments were validated by the C entry point
+// and returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ar {
+
+hipError_t launch_reduce_1stage(const void *const *inputs, int W, void *out,
+                                int64_t packs, hipStream_t s);
+
+// order[i] = index of the input summed i-th; tmps absolute per shard owner.
+hipError_t launch_reduce_2stage(const void *const *inputs, const int *order,
+                                void *const *tmps, int W, int rank, void *out,
+                                int64_t packs, bool rs, bool ag, hipStream_t s);
+
+hipError_t launch_fused_rmsnorm(const void *const *inputs, int W,
+                                const void *residual, const void *weight,
+                                void *residual_out, void *norm_out, int64_t M,
+                                int64_t N, float eps, hipStream_t s);
+
+hipError_t launch_ll_pack(const float *src, int64_t n, void *fifo,
+                          int64_t step_lines, uint64_t first_step, hipStream_t s);
+hipError_t launch_ll_unpack_reduce(const void *const *fifos, int W, float *out,
+                                   int64_t n, int64_t step_lines,
+                                   uint64_t first_step, uint32_t max_spins,
+                                   uint32_t *bad_lines, hipStream_t s);
+hipError_t launch_ll128_pack(const float *src, int64_t n, void *fifo,
+                             int64_t step_lines, uint64_t first_step,
+                             hipStream_t s);
+hipError_t launch_ll128_unpack_reduce(const void *const *fifos, int W,
+                                      float *out, int64_t n, int64_t step_lines,
+                                      uint64_t first_step, uint32_t max_spins,
+                                      uint32_t *bad_lines, hipStream_t s);
+
+}  // namespace ar

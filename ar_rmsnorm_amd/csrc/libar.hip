@@ -1,0 +1,294 @@
+// C entry points of libar: argument validation, then one kernel launch on the
+// caller's stream.  Every check runs before anything is enqueued, so a call
+// that returns an error code has touched no buffer.  See include/libar.h for
+// the contract of each entry point.
+#include "../../include/libar.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+#define LIBAR_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+ar_status_t from_hip(hipError_t e)
+{
+    if (e == hipSuccess)
+        return AR_OK;
+    g_last_hip_error = (int)e;
+    return AR_ERR_HIP;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Do the byte ranges [a, a + na) and [b, b + nb) share a byte?
+bool overlaps(const void *a, int64_t na, const void *b, int64_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return na > 0 && nb > 0 && x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+// Overlap that is not exact identity of the two ranges.
+bool overlaps_partially(const void *a, const void *b, int64_t nbytes)
+{
+    return a != b && overlaps(a, nbytes, b, nbytes);
+}
+
+constexpr int64_t kMaxLines = (int64_t)1 << 31;
+constexpr int64_t kMaxElems = (int64_t)1 << 40;   // keeps every grid in range
+
+}  // namespace
+
+LIBAR_EXPORT const char *ar_status_str(ar_status_t status)
+{
+    switch (status) {
+    case AR_OK: return "ok";
+    case AR_ERR_NULL: return "a required pointer is NULL";
+    case AR_ERR_ARG: return "invalid size, flag or buffer aliasing";
+    case AR_ERR_ALIGN: return "pointer not aligned as required";
+    case AR_ERR_WORLD: return "number of rank buffers W out of range";
+    case AR_ERR_CAPACITY: return "payload does not fit the 8 steps of the FIFO";
+    case AR_ERR_HIP: return "HIP runtime rejected the launch";
+    default: return "unknown status";
+    }
+}
+
+LIBAR_EXPORT int ar_last_hip_error(void) { return g_last_hip_error; }
+
+// ---------------------------------------------------------------------------
+LIBAR_EXPORT ar_status_t ar_reduce_1stage(const void *const *inputs, int W, void *out,
+                                          int64_t n, ar_stream_t stream)
+{
+    if (!inputs || !out)
+        return AR_ERR_NULL;
+    if (W < 2 || W > AR_MAX_WORLD)
+        return AR_ERR_WORLD;
+    for (int r = 0; r < W; ++r)
+        if (!inputs[r])
+            return AR_ERR_NULL;
+    if (n < 0 || n % 8 != 0 || n > kMaxElems)
+        return AR_ERR_ARG;
+    if (!aligned(out, 16))
+        return AR_ERR_ALIGN;
+    for (int r = 0; r < W; ++r)
+        if (!aligned(inputs[r], 16))
+            return AR_ERR_ALIGN;
+    for (int r = 0; r < W; ++r)
+        if (overlaps_partially(out, inputs[r], 2 * n))
+            return AR_ERR_ARG;
+    if (n == 0)
+        return AR_OK;
+    return from_hip(ar::launch_reduce_1stage(inputs, W, out, n / 8,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+LIBAR_EXPORT ar_status_t ar_reduce_2stage(const void *const *inputs, void *const *tmps,
+                                          int W, int rank, void *out, int64_t n,
+                                          unsigned flags, ar_stream_t stream)
+{
+    if (!inputs || !tmps)
+        return AR_ERR_NULL;
+    if (W < 2 || W > AR_MAX_WORLD)
+        return AR_ERR_WORLD;
+    if (flags & ~(AR_STAGE_RS | AR_STAGE_AG | AR_ORDER_RANK))
+        return AR_ERR_ARG;
+    if ((flags & (AR_STAGE_RS | AR_STAGE_AG)) == 0)
+        flags |= AR_STAGE_RS | AR_STAGE_AG;
+    const bool rs = flags & AR_STAGE_RS, ag = flags & AR_STAGE_AG;
+    for (int r = 0; r < W; ++r)
+        if (!inputs[r] || !tmps[r])
+            return AR_ERR_NULL;
+    if (ag && !out)
+        return AR_ERR_NULL;
+    if (rank < 0 || rank >= W || n < 0 || n % 8 != 0 || n > kMaxElems)
+        return AR_ERR_ARG;
+    for (int r = 0; r < W; ++r)
+        if (!aligned(inputs[r], 16) || !aligned(tmps[r], 16))
+            return AR_ERR_ALIGN;
+    if (ag && !aligned(out, 16))
+        return AR_ERR_ALIGN;
+    const int64_t packs = n / 8;
+    const int64_t tmp_bytes = (packs / W + packs % W) * 16;
+    for (int r = 0; r < W; ++r) {
+        if (ag && (overlaps(out, 2 * n, inputs[r], 2 * n) ||
+                   overlaps(out, 2 * n, tmps[r], tmp_bytes)))
+            return AR_ERR_ARG;
+        if (rs && overlaps(tmps[rank], tmp_bytes, inputs[r], 2 * n))
+            return AR_ERR_ARG;
+        if (rs && ag && r != rank && overlaps(tmps[rank], tmp_bytes, tmps[r], tmp_bytes))
+            return AR_ERR_ARG;
+    }
+    if (n == 0)
+        return AR_OK;
+    // The owner's summation order: its own buffer first, then the next ranks
+    // round the ring, or plain rank order on request.
+    int order[AR_MAX_WORLD];
+    for (int i = 0; i < W; ++i)
+        order[i] = (flags & AR_ORDER_RANK) ? i : (rank + i) % W;
+    return from_hip(ar::launch_reduce_2stage(inputs, order, tmps, W, rank, out, packs,
+                                             rs, ag, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+LIBAR_EXPORT ar_status_t ar_fused_residual_rmsnorm(const void *const *inputs, int W,
+                                                   const void *residual, const void *weight,
+                                                   void *residual_out, void *norm_out,
+                                                   int64_t M, int64_t N, float eps,
+                                                   ar_stream_t stream)
+{
+    if (!inputs || !residual || !weight || !residual_out || !norm_out)
+        return AR_ERR_NULL;
+    if (W < 2 || W > AR_MAX_WORLD)
+        return AR_ERR_WORLD;
+    for (int r = 0; r < W; ++r)
+        if (!inputs[r])
+            return AR_ERR_NULL;
+    if (M < 0 || N < 8 || N > AR_FUSED_MAX_N || N % 8 != 0 || M > 0x7FFFFFFF)
+        return AR_ERR_ARG;
+    if (!(eps >= 0.0f) || eps > 3.0e38f)   // rejects NaN, negatives and inf
+        return AR_ERR_ARG;
+    if (!aligned(residual, 16) || !aligned(weight, 16) || !aligned(residual_out, 16) ||
+        !aligned(norm_out, 16))
+        return AR_ERR_ALIGN;
+    for (int r = 0; r < W; ++r)
+        if (!aligned(inputs[r], 16))
+            return AR_ERR_ALIGN;
+    const int64_t mat = 2 * M * N, vec = 2 * N;
+    if (overlaps_partially(residual_out, residual, mat) ||
+        overlaps(residual_out, mat, weight, vec) ||
+        overlaps(norm_out, mat, residual, mat) || overlaps(norm_out, mat, weight, vec) ||
+        overlaps(norm_out, mat, residual_out, mat))
+        return AR_ERR_ARG;
+    for (int r = 0; r < W; ++r)
+        if (overlaps(norm_out, mat, inputs[r], mat) ||
+            overlaps(residual_out, mat, inputs[r], mat))
+            return AR_ERR_ARG;
+    if (M == 0)
+        return AR_OK;
+    return from_hip(ar::launch_fused_rmsnorm(inputs, W, residual, weight, residual_out,
+                                             norm_out, M, N, eps,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// wire formats
+// ---------------------------------------------------------------------------
+LIBAR_EXPORT int64_t ll_lines(int64_t n) { return n > 0 ? (4 * n + 7) / 8 : 0; }
+LIBAR_EXPORT int64_t ll128_lines(int64_t n) { return n > 0 ? (4 * n + 119) / 120 : 0; }
+LIBAR_EXPORT int64_t ll_fifo_bytes(int64_t step_lines)
+{
+    return step_lines > 0 ? AR_FIFO_STEPS * step_lines * 16 : 0;
+}
+LIBAR_EXPORT int64_t ll128_fifo_bytes(int64_t step_lines)
+{
+    return step_lines > 0 ? AR_FIFO_STEPS * step_lines * 128 : 0;
+}
+LIBAR_EXPORT int64_t ll_default_step_lines(void) { return 4096; }
+LIBAR_EXPORT int64_t ll128_default_step_lines(void) { return 4800; }
+
+namespace {
+
+// Checks common to the pack entry points.
+ar_status_t check_pack(const float *src, int64_t n, void *fifo, int64_t step_lines,
+                       int64_t lines, int64_t line_bytes)
+{
+    if (!src || !fifo)
+        return AR_ERR_NULL;
+    if (n < 0 || step_lines < 1 || step_lines > kMaxLines / AR_FIFO_STEPS)
+        return AR_ERR_ARG;
+    if (lines > AR_FIFO_STEPS * step_lines)
+        return AR_ERR_CAPACITY;
+    if (!aligned(src, 4) || !aligned(fifo, line_bytes == 16 ? 16 : 128))
+        return AR_ERR_ALIGN;
+    if (overlaps(src, 4 * n, fifo, AR_FIFO_STEPS * step_lines * line_bytes))
+        return AR_ERR_ARG;
+    return AR_OK;
+}
+
+ar_status_t check_unpack(const void *const *fifos, int W, float *out, int64_t n,
+                         int64_t step_lines, int64_t lines, int64_t line_bytes,
+                         uint32_t max_spins, uint32_t *bad_lines)
+{
+    if (!fifos || !out)
+        return AR_ERR_NULL;
+    if (W < 1 || W > AR_MAX_WORLD)
+        return AR_ERR_WORLD;
+    for (int r = 0; r < W; ++r)
+        if (!fifos[r])
+            return AR_ERR_NULL;
+    if (n < 0 || step_lines < 1 || step_lines > kMaxLines / AR_FIFO_STEPS ||
+        max_spins > AR_MAX_SPINS)
+        return AR_ERR_ARG;
+    if (lines > AR_FIFO_STEPS * step_lines)
+        return AR_ERR_CAPACITY;
+    if (!aligned(out, 4) || (bad_lines && !aligned(bad_lines, 4)))
+        return AR_ERR_ALIGN;
+    for (int r = 0; r < W; ++r)
+        if (!aligned(fifos[r], line_bytes == 16 ? 16 : 128))
+            return AR_ERR_ALIGN;
+    const int64_t fifo_bytes = AR_FIFO_STEPS * step_lines * line_bytes;
+    for (int r = 0; r < W; ++r)
+        if (overlaps(out, 4 * n, fifos[r], fifo_bytes) ||
+            (bad_lines && overlaps(bad_lines, 4, fifos[r], fifo_bytes)))
+            return AR_ERR_ARG;
+    if (bad_lines && overlaps(bad_lines, 4, out, 4 * n))
+        return AR_ERR_ARG;
+    return AR_OK;
+}
+
+}  // namespace
+
+LIBAR_EXPORT ar_status_t ll_pack(const float *src, int64_t n, void *fifo,
+                                 int64_t step_lines, uint64_t first_step,
+                                 ar_stream_t stream)
+{
+    const ar_status_t st = check_pack(src, n, fifo, step_lines, ll_lines(n), 16);
+    if (st != AR_OK || n == 0)
+        return st;
+    return from_hip(ar::launch_ll_pack(src, n, fifo, step_lines, first_step,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+LIBAR_EXPORT ar_status_t ll128_pack(const float *src, int64_t n, void *fifo,
+                                    int64_t step_lines, uint64_t first_step,
+                                    ar_stream_t stream)
+{
+    const ar_status_t st = check_pack(src, n, fifo, step_lines, ll128_lines(n), 128);
+    if (st != AR_OK || n == 0)
+        return st;
+    return from_hip(ar::launch_ll128_pack(src, n, fifo, step_lines, first_step,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+LIBAR_EXPORT ar_status_t ll_unpack_reduce(const void *const *fifos, int W, float *out,
+                                          int64_t n, int64_t step_lines,
+                                          uint64_t first_step, uint32_t max_spins,
+                                          uint32_t *bad_lines, ar_stream_t stream)
+{
+    const ar_status_t st = check_unpack(fifos, W, out, n, step_lines, ll_lines(n), 16,
+                                        max_spins, bad_lines);
+    if (st != AR_OK || n == 0)
+        return st;
+    return from_hip(ar::launch_ll_unpack_reduce(fifos, W, out, n, step_lines, first_step,
+                                                max_spins, bad_lines,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+LIBAR_EXPORT ar_status_t ll128_unpack_reduce(const void *const *fifos, int W, float *out,
+                                             int64_t n, int64_t step_lines,
+                                             uint64_t first_step, uint32_t max_spins,
+                                             uint32_t *bad_lines, ar_stream_t stream)
+{
+    const ar_status_t st = check_unpack(fifos, W, out, n, step_lines, ll128_lines(n), 128,
+                                        max_spins, bad_lines);
+    if (st != AR_OK || n == 0)
+        return st;
+    return from_hip(ar::launch_ll128_unpack_reduce(fifos, W, out, n, step_lines,
+                                                   first_step, max_spins, bad_lines,
+                                                   static_cast<hipStream_t>(stream)));
+}

@@ -1,0 +1,173 @@
+// One-stage and two-stage reduce of W bf16 rank buffers on one GPU.
+//
+// Sources (web pages; cited by tag and section):
+//   [SGLv1] "SGLang Custom AllReduce v1 线程模型和工作原理细节" (todaynews.cc)
+//   [JITAR] "0-custom-all-reduce" (obnotes-4iw.pages.dev, sglang jit_kernel)
+//
+// Both forms are pure streams over 16-byte packs: every byte is read once and
+// written once, with ~1 fp32 add per 2 bytes, so they are bound by HBM
+// bandwidth (8 TB/s on MI355X), not by the vector ALUs, and there is no
+// contraction to put on the matrix cores.  The launch shape differs from the
+// pages' (512 threads x at most 36 blocks, tuned for NVLink-era parts): here
+// one 256-lane workgroup covers 256 consecutive packs and the grid grows
+// with the message, so an 8 MB x 8 reduce fills all 256 CUs with thousands
+// of wavefronts, each lane keeping its W loads in flight at once.
+#include "device.h"
+#include "launch.h"
+
+namespace ar {
+
+constexpr int kReduceThreads = 256;
+
+// Sum of the W packs of one 16-byte column, in table order, rounded once
+// ([SGLv1] "1stage: full kernel and timeline": fp32 accumulation starting
+// from the first buffer's value; [JITAR] section 4).
+template <int W>
+__device__ __forceinline__ u32x4 reduce_column(const u32x4 (&v)[W])
+{
+    float acc[8];
+    widen8(v[0], acc);
+#pragma unroll
+    for (int r = 1; r < W; ++r) {
+        float t[8];
+        widen8(v[r], t);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            acc[k] = acc[k] + t[k];
+    }
+    return narrow8(acc);
+}
+
+// out[i] = bf16(sum_r in[r][i]) for every pack i.  out may be one of the
+// inputs: each lane loads all W packs of column i before storing column i.
+template <int W>
+__global__ __launch_bounds__(kReduceThreads) void reduce_1stage_kernel(
+    InTable<W> in, u32x4 *out, int64_t packs)
+{
+    const int64_t i = (int64_t)blockIdx.x * kReduceThreads + threadIdx.x;
+    if (i >= packs)
+        return;
+    u32x4 v[W];
+#pragma unroll
+    for (int r = 0; r < W; ++r)
+        v[r] = in.p[r][i];
+    out[i] = reduce_column<W>(v);
+}
+
+// Two-stage reduce for one rank ([SGLv1] "2stage: sharding, rotation, and
+// why no exit barrier").  Grid: x covers the packs of the largest shard,
+// y selects i = blockIdx.y and the shard g = (rank + i) mod W it moves.
+//   i == 0, RS   : reduce this rank's shard (inputs in `in` order, i.e. the
+//                  owner's rotation), store to tmps[rank], and with AG also
+//                  to out.  The value goes from registers to out, and each
+//                  lane gathers exactly the packs it reduced, which is the
+//                  pages' same-thread mapping, so no barrier is needed.
+//   i == 0, AG only: copy tmps[rank] to out.
+//   i >  0, AG   : copy shard g from tmps[g] to out.
+template <int W, bool RS, bool AG>
+__global__ __launch_bounds__(kReduceThreads) void reduce_2stage_kernel(
+    InTable<W> in, OutTable<W> tmps, int rank, u32x4 *out, int64_t part,
+    int64_t rem)
+{
+    const int64_t idx = (int64_t)blockIdx.x * kReduceThreads + threadIdx.x;
+    const int i = blockIdx.y;
+    int g = rank + i;
+    if (g >= W)
+        g -= W;
+    const int64_t size = part + (g == W - 1 ? rem : 0);
+    if (idx >= size)
+        return;
+    const int64_t dst = (int64_t)g * part + idx;
+    if (RS && i == 0) {
+        u32x4 v[W];
+#pragma unroll
+        for (int r = 0; r < W; ++r)
+            v[r] = in.p[r][dst];
+        const u32x4 s = reduce_column<W>(v);
+        tmps.p[g][idx] = s;
+        if (AG)
+            out[dst] = s;
+    } else {
+        out[dst] = tmps.p[g][idx];
+    }
+}
+
+template <int W>
+static hipError_t launch_1stage_w(const void *const *inputs, void *out,
+                                  int64_t packs, hipStream_t s)
+{
+    InTable<W> t;
+    for (int r = 0; r < W; ++r)
+        t.p[r] = static_cast<const u32x4 *>(inputs[r]);
+    const int64_t blocks = (packs + kReduceThreads - 1) / kReduceThreads;
+    reduce_1stage_kernel<W><<<dim3((unsigned)blocks), dim3(kReduceThreads), 0, s>>>(
+        t, static_cast<u32x4 *>(out), packs);
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce_1stage(const void *const *inputs, int W, void *out,
+                                int64_t packs, hipStream_t s)
+{
+    switch (W) {
+    case 2: return launch_1stage_w<2>(inputs, out, packs, s);
+    case 3: return launch_1stage_w<3>(inputs, out, packs, s);
+    case 4: return launch_1stage_w<4>(inputs, out, packs, s);
+    case 5: return launch_1stage_w<5>(inputs, out, packs, s);
+    case 6: return launch_1stage_w<6>(inputs, out, packs, s);
+    case 7: return launch_1stage_w<7>(inputs, out, packs, s);
+    case 8: return launch_1stage_w<8>(inputs, out, packs, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int W, bool RS, bool AG>
+static hipError_t launch_2stage_mode(const InTable<W> &in, const OutTable<W> &tmps,
+                                     int rank, void *out, int64_t part,
+                                     int64_t rem, hipStream_t s)
+{
+    const int64_t span = AG ? part + rem : part + (rank == W - 1 ? rem : 0);
+    const int64_t blocks = (span + kReduceThreads - 1) / kReduceThreads;
+    if (blocks == 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)blocks, AG ? W : 1);
+    reduce_2stage_kernel<W, RS, AG><<<grid, dim3(kReduceThreads), 0, s>>>(
+        in, tmps, rank, static_cast<u32x4 *>(out), part, rem);
+    return hipGetLastError();
+}
+
+template <int W>
+static hipError_t launch_2stage_w(const void *const *inputs, const int *order,
+                                  void *const *tmps, int rank, void *out,
+                                  int64_t packs, bool rs, bool ag, hipStream_t s)
+{
+    InTable<W> in;
+    OutTable<W> tp;
+    for (int r = 0; r < W; ++r) {
+        in.p[r] = static_cast<const u32x4 *>(inputs[order[r]]);
+        tp.p[r] = static_cast<u32x4 *>(tmps[r]);
+    }
+    const int64_t part = packs / W, rem = packs % W;
+    if (rs && ag)
+        return launch_2stage_mode<W, true, true>(in, tp, rank, out, part, rem, s);
+    if (rs)
+        return launch_2stage_mode<W, true, false>(in, tp, rank, out, part, rem, s);
+    return launch_2stage_mode<W, false, true>(in, tp, rank, out, part, rem, s);
+}
+
+hipError_t launch_reduce_2stage(const void *const *inputs, const int *order,
+                                void *const *tmps, int W, int rank, void *out,
+                                int64_t packs, bool rs, bool ag, hipStream_t s)
+{
+    switch (W) {
+    case 2: return launch_2stage_w<2>(inputs, order, tmps, rank, out, packs, rs, ag, s);
+    case 3: return launch_2stage_w<3>(inputs, order, tmps, rank, out, packs, rs, ag, s);
+    case 4: return launch_2stage_w<4>(inputs, order, tmps, rank, out, packs, rs, ag, s);
+    case 5: return launch_2stage_w<5>(inputs, order, tmps, rank, out, packs, rs, ag, s);
+    case 6: return launch_2stage_w<6>(inputs, order, tmps, rank, out, packs, rs, ag, s);
+    case 7: return launch_2stage_w<7>(inputs, order, tmps, rank, out, packs, rs, ag, s);
+    case 8: return launch_2stage_w<8>(inputs, order, tmps, rank, out, packs, rs, ag, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace ar

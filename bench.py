@@ -1,0 +1,328 @@
+#!/usr/bin/env python3
+"""Bench of the per-GPU reduction hot path on one MI355X.
+
+Headline (`value`): achieved HBM GB/s of the two-stage reduce at the 8 MB
+message cap, W=8 rank buffers of 4,194,304 bf16, as run by one rank
+(reduce-scatter of its 1/8 shard + all-gather of all 8 shards), with all
+buffers resident in HBM and rotated over enough buffer sets that every launch
+reads from HBM rather than the 256 MB Infinity Cache.  One step = one launch.
+
+Timing: K launches are captured in a HIP graph (no host launch overhead in
+the timed region) and replayed between two HIP events on the launch stream;
+ms_per_step = elapsed / K.  The same events time every other row of the hot
+path (one-stage reduce, fused all-reduce + residual + RMSNorm, LL / LL128
+pack and decode), reported under "rows"; the fused M=1 latency is also
+reported per call.
+
+`roofline.traffic` comes from the rocprofv3 counter summary committed under
+profiles/ (FETCH_SIZE + WRITE_SIZE per dispatch, scaled by a plain copy of
+known size) and is null when the kernel source changed since it was taken.
+
+`cpu_baseline` times the CPU oracle (single-threaded plain C) on the same
+per-rank two-stage work, repeated for about 10 s.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+                       [--rows all|none] [--calib-copy]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("achieved HBM GB/s (% of peak) for W=8 8MB reduce; "
+          "µs/call M=1 fused AR+RMSNorm")
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "reduce_2stage_w8_8MiB_counters.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "ar_rmsnorm_amd", "csrc", f)
+                  for f in ("reduce.hip", "device.h")]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=240)
+    p.add_argument("--warmup", type=int, default=24)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--rows", choices=["all", "none"], default="all")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run a plain 256 MiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(source_hash: str):
+    """HBM bytes per launch from the committed counter summary, or None."""
+    try:
+        text = open(PROFILE_COUNTERS).read()
+    except OSError:
+        return None
+    m = re.search(r"^source_hash:\s*(\S+)", text, re.M)
+    t = re.search(r"^hbm_bytes_per_launch:\s*([0-9.]+)", text, re.M)
+    if not m or not t or m.group(1) != source_hash:
+        return None
+    return float(t.group(1))
+
+
+def log(msg: str) -> None:
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+              "supported (the W rank buffers all live in one GPU's HBM)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py: no GPU visible")
+    from ar_rmsnorm_amd import libar as ar
+    from ar_rmsnorm_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    def graph_time(fns, steps, warmup):
+        """Average ms per call of the calls fns[i % len(fns)], timed over a
+        HIP graph of `steps` back-to-back launches replayed between events."""
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(max(warmup, len(fns))):
+                fns[i % len(fns)]()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                fns[i % len(fns)]()
+        g.replay()                     # warm the graph itself
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record()
+        g.replay()
+        stop.record()
+        stop.synchronize()
+        ms = start.elapsed_time(stop) / steps
+        del g
+        return ms
+
+    def sets_for(touched_bytes):
+        """Buffer sets so that one rotation touches > 2x the Infinity Cache."""
+        return max(2, -(-2 * MALL_BYTES // max(touched_bytes, 1)) + 1)
+
+    # ------------------------------------------------------------------
+    # headline: two-stage reduce, W=8 x 8 MiB, per rank (rank 0: RS + AG)
+    # ------------------------------------------------------------------
+    cfg = synth.REDUCE_CAP
+    W, n = cfg["W"], cfg["n"]
+    xs = synth.reduce_cap()
+    P = n // 8
+    part, rem = P // W, P % W
+    # bytes the launch must move: RS reads W slices of `part` packs and writes
+    # the own shard to tmp and out; AG reads the W-1 peer shards and writes
+    # them to out (the own shard goes from registers to out).
+    shard = part * 16
+    bytes_2stage = W * shard + 2 * shard + (W - 1) * shard + (W - 1) * shard
+    touched = bytes_2stage
+    nsets = sets_for(touched)
+    base = [to_dev(x) for x in xs]
+    sets = []
+    for k in range(nsets):
+        ins = base if k == 0 else [b.clone() for b in base]
+        tmps = [torch.empty((part + rem) * 8, dtype=torch.int16, device=dev) for _ in range(W)]
+        out = torch.empty(n, dtype=torch.int16, device=dev)
+        for r in range(1, W):               # the peers' shards, staged untimed
+            ar.ar_reduce_2stage(ins, tmps, r, None, flags=ar.AR_STAGE_RS)
+        sets.append((ins, tmps, out))
+    torch.cuda.synchronize()
+    calls = [(lambda s=s: ar.ar_reduce_2stage(s[0], s[1], 0, s[2])) for s in sets]
+    steps = max(args.steps, nsets)
+    steps -= steps % nsets
+    log(f"two-stage W=8 8MiB: {nsets} buffer sets staged, timing {steps} launches")
+    ms = graph_time(calls, steps, args.warmup)
+    gbps = bytes_2stage / (ms * 1e-3) / 1e9
+    log(f"two-stage: {ms * 1e3:.3f} us/launch, {gbps:.1f} GB/s")
+    src_hash = kernel_source_hash()
+    traffic = traffic_from_profile(src_hash)
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "storage_dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "two-stage reduce at the 8 MB cap: W=8 rank buffers of "
+                        "4,194,304 bf16 ~U(-1,1), one rank's reduce-scatter of its 1/8 "
+                        "shard + all-gather of the 8 shards, HBM-resident, cold",
+            "W": W, "n": n, "bytes_per_launch": bytes_2stage,
+            "buffer_sets_rotated": nsets,
+        },
+        "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "reduce_2stage_kernel<8,true,true>",
+            "kernel_us": round(ms * 1e3, 3),
+            "source_hash": src_hash,
+        },
+    }
+    del sets, calls
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------------
+    # the other rows of the hot path
+    # ------------------------------------------------------------------
+    rows = {}
+
+    def row(name, nbytes, fns, steps=None, extra=None):
+        k = steps or max(60, len(fns))
+        k -= k % len(fns)
+        t = graph_time(fns, k, args.warmup)
+        r = {"us_per_call": round(t * 1e3, 3), "bytes": nbytes,
+             "GBps": round(nbytes / (t * 1e-3) / 1e9, 1),
+             "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        if extra:
+            r.update(extra)
+        rows[name] = r
+        log(f"row {name}: {r['us_per_call']} us, {r['GBps']} GB/s")
+        return r
+
+    if args.rows == "all":
+        # fused all-reduce + residual + RMSNorm, W=4, N=2048, M in {1, 16, 128}
+        fc = synth.FUSED
+        for M in fc["Ms"]:
+            fx, fr, fw = synth.fused(M)
+            nb = (fc["W"] + 3) * M * fc["N"] * 2 + 2 * fc["N"]
+            d = [to_dev(x) for x in fx]
+            dr, dw = to_dev(fr), to_dev(fw)
+            ro = torch.empty_like(dr)
+            no = torch.empty_like(dr)
+            call = (lambda d=d, dr=dr, dw=dw, ro=ro, no=no:
+                    ar.ar_fused_residual_rmsnorm(d, dr, dw, ro, no, fc["eps"]))
+            row(f"fused_W4_M{M}_N2048", nb, [call], steps=200)
+        result["fused_m1_us_per_call"] = rows["fused_W4_M1_N2048"]["us_per_call"]
+
+        # one-stage reduce: small, decode shape, and the cap message
+        for name, maker in (("1stage_W2_n8192", synth.reduce_small),
+                            ("1stage_W8_n8192", synth.reduce_decode)):
+            xx = maker()
+            d = [to_dev(x) for x in xx]
+            o = torch.empty_like(d[0])
+            row(name, (len(d) + 1) * d[0].numel() * 2,
+                [lambda d=d, o=o: ar.ar_reduce_1stage(d, o)], steps=200)
+        nb = (W + 1) * n * 2
+        k1 = sets_for(nb)
+        s1 = []
+        for k in range(k1):
+            ins = [b.clone() for b in base]
+            s1.append((ins, torch.empty(n, dtype=torch.int16, device=dev)))
+        row("1stage_W8_n4194304", nb,
+            [lambda s=s: ar.ar_reduce_1stage(s[0], s[1]) for s in s1], steps=8 * k1)
+        del s1
+
+        # wire formats: W=4 fp32 payloads of 16 Mi values (and the +13 tail)
+        wc = synth.WIRE
+        for nn in (wc["n"], wc["n"] + wc["tail"]):
+            payloads = [torch.from_numpy(p).to(dev) for p in synth.wire(nn)]
+            for fmt, lsize, lines_fn, pack, unpack in (
+                    ("ll128", 128, ar.ll128_lines, ar.ll128_pack, ar.ll128_unpack_reduce),
+                    ("ll", 16, ar.ll_lines, ar.ll_pack, ar.ll_unpack_reduce)):
+                L = lines_fn(nn)
+                sl = -(-L // 8)
+                fifos = [torch.empty(8 * sl * lsize, dtype=torch.uint8, device=dev)
+                         for _ in range(wc["W"])]
+                for p, f in zip(payloads, fifos):
+                    pack(p, f, sl)
+                out = torch.empty(nn, dtype=torch.float32, device=dev)
+                tag = f"{fmt}_W4_n{nn}"
+                row(f"{tag}_decode", wc["W"] * L * lsize + 4 * nn,
+                    [lambda f=fifos, o=out, sl=sl: unpack(f, o, sl)], steps=40)
+                row(f"{fmt}_n{nn}_pack", 4 * nn + L * lsize,
+                    [lambda p=payloads[0], f=fifos[0], sl=sl: pack(p, f, sl)], steps=40)
+                if nn == wc["n"]:
+                    # source at a 4-byte offset: same wire bytes, cost of misalignment
+                    raw = torch.empty(nn + 4, dtype=torch.float32, device=dev)
+                    src = raw[1:1 + nn]
+                    src.copy_(payloads[0])
+                    row(f"{fmt}_n{nn}_pack_src_offset4", 4 * nn + L * lsize,
+                        [lambda p=src, f=fifos[0], sl=sl: pack(p, f, sl)], steps=40)
+                del fifos, out
+            del payloads
+            torch.cuda.empty_cache()
+        result["rows"] = rows
+
+    if args.calib_copy:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    # ------------------------------------------------------------------
+    # CPU baseline: the oracle on the same per-rank two-stage work
+    # ------------------------------------------------------------------
+    if not args.no_cpu:
+        log("CPU oracle baseline (~10 s)")
+        import oracle as orc
+        tmps = [orc.reduce_scatter(xs, s) for s in range(W)]
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            own = orc.reduce_scatter(xs, 0)
+            orc.all_gather([own] + tmps[1:], n)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= 10.0:
+                break
+        result["cpu_baseline"] = {
+            "value": round(bytes_2stage * reps / el / 1e9, 3),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"the full per-rank two-stage work of the headline workload "
+                      f"(reduce-scatter of shard 0 + all-gather of the 8 shards, "
+                      f"8 x 4,194,304 bf16), {reps} repetitions in {el:.1f} s, "
+                      f"single-threaded C",
+            "ms_per_step": round(el / reps * 1e3, 3),
+        }
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,220 @@
+/*
+ * libar — the per-GPU reduction at the heart of a custom all-reduce, for
+ * AMD Instinct MI355X (gfx950).  C ABI: plain pointers and sizes only.
+ *
+ * All W "peer" rank buffers are ordinary device buffers of one GPU; nothing
+ * here talks to another GPU.  The operations follow these pages (cited by tag
+ * and section below):
+ *   [SGLv1]  "SGLang Custom AllReduce v1 线程模型和工作原理细节" (todaynews.cc)
+ *   [NCCL14] "NCCL 专家课程 14：Simple、LL、LL128 的线格式、同步与真实性能边界"
+ *            (blog.cptz.space)
+ *   [JITAR]  "0-custom-all-reduce" (obnotes-4iw.pages.dev, sglang jit_kernel)
+ *   [TRIAR]  "用 Triton + Symmetric Memory 写一个 AllReduce + RMSNorm 融合算子"
+ *            (riverclouds.net)
+ *
+ * Conventions shared by every entry point
+ *   Ownership  The caller owns every buffer.  The library never allocates,
+ *              frees or synchronizes, and keeps no state between calls except
+ *              a thread-local copy of the last HIP error.
+ *   Pointers   Data pointers are device pointers.  Pointer tables (inputs,
+ *              tmps, fifos) are HOST arrays of W device pointers; they are
+ *              read during the call and copied into the kernel arguments, so
+ *              the table may be reused as soon as the call returns.
+ *   Streams    Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *              stream) and the call returns without waiting.
+ *   Errors     Argument errors are detected before anything is enqueued and
+ *              leave every buffer untouched.  AR_ERR_HIP means a launch was
+ *              rejected by the HIP runtime; ar_last_hip_error() gives its
+ *              hipError_t code.
+ *   Sizes      Counts are elements (bf16 for the reduce forms, fp32 for the
+ *              wire formats).  A count of 0 is valid and enqueues nothing.
+ *   bf16       Raw bfloat16 bit patterns (upper half of an IEEE binary32).
+ *              Sums are formed in fp32 and rounded once to bf16, to nearest,
+ *              ties to even; fp32 denormals are kept ([JITAR] section 4).
+ */
+#ifndef LIBAR_H
+#define LIBAR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *ar_stream_t;
+typedef int ar_status_t;
+
+#define AR_OK 0
+#define AR_ERR_NULL 1      /* a required pointer is NULL */
+#define AR_ERR_ARG 2       /* a size, flag or aliasing rule is violated */
+#define AR_ERR_ALIGN 3     /* a pointer lacks the required alignment */
+#define AR_ERR_WORLD 4     /* W outside the supported range */
+#define AR_ERR_CAPACITY 5  /* the payload does not fit the FIFO's 8 steps */
+#define AR_ERR_HIP 6       /* the HIP runtime rejected a launch */
+
+#define AR_MAX_WORLD 8          /* W <= 8 rank buffers */
+#define AR_FUSED_MAX_N 16384    /* longest row of the fused form */
+#define AR_MAX_SPINS 65536u     /* bound on flag re-reads per line */
+#define AR_FIFO_STEPS 8         /* slots in a wire FIFO ring */
+
+/* Flags of ar_reduce_2stage. */
+#define AR_STAGE_RS 1u     /* run the reduce-scatter of this rank's shard */
+#define AR_STAGE_AG 2u     /* run the all-gather into out */
+#define AR_ORDER_RANK 4u   /* sum 0..W-1 instead of the owner's rotation */
+
+/* Short English text for a status code (static storage). */
+const char *ar_status_str(ar_status_t status);
+
+/* hipError_t of the last failed launch on the calling thread (0 if none). */
+int ar_last_hip_error(void);
+
+/*
+ * One-stage reduce ([SGLv1] "1stage: full kernel and timeline"; [JITAR]
+ * sections 1-5).  For every element j:
+ *     acc = fp32(inputs[0][j]); acc += fp32(inputs[r][j]) for r = 1..W-1;
+ *     out[j] = bf16(acc)
+ * in this order, so the result is the same bits on every rank.  Each lane
+ * moves whole 16-byte packs (8 bf16).
+ *   inputs  host table of W device pointers, each to n bf16
+ *   W       2 <= W <= 8                                 else AR_ERR_WORLD
+ *   out     n bf16; may be one of the inputs (in place), must not partially
+ *           overlap any input                            else AR_ERR_ARG
+ *   n       multiple of 8 (whole 16-byte packs), >= 0   else AR_ERR_ARG
+ *   every data pointer 16-byte aligned                   else AR_ERR_ALIGN
+ */
+ar_status_t ar_reduce_1stage(const void *const *inputs, int W, void *out,
+                             int64_t n, ar_stream_t stream);
+
+/*
+ * Two-stage reduce = reduce-scatter + all-gather, as run by one rank
+ * ([SGLv1] "2stage: sharding, rotation, and why no exit barrier").
+ * The message is P = n/8 packs; part = P / W; shard s is packs
+ * [s*part, (s+1)*part), the last shard also taking the P mod W remainder.
+ *   RS: tmps[rank][q] = bf16(sum of inputs[(rank+i) mod W][s*part*8 + q],
+ *       i = 0..W-1, in that rotated order) for the elements q of shard rank.
+ *       With AR_ORDER_RANK the order is 0..W-1.
+ *   AG: out[s*part*8 + q] = tmps[s][q] for every shard s.
+ * On one GPU the peers' shards are whatever tmps[s != rank] hold: run the
+ * RS stage for every other rank first (flags = AR_STAGE_RS).  With both
+ * stages, this rank's shard goes from registers to both tmps[rank] and out,
+ * each lane gathering the same packs it reduced (the pages' same-thread
+ * mapping), so no barrier is needed inside the launch.
+ *   inputs  host table of W device pointers, each to n bf16
+ *   tmps    host table of W device pointers, each to at least
+ *           (part + P mod W) * 8 bf16
+ *   W       2 <= W <= 8                                 else AR_ERR_WORLD
+ *   rank    0 <= rank < W                                else AR_ERR_ARG
+ *   out     n bf16 (may be NULL when AG is not run); must not overlap any
+ *           input or tmp buffer                          else AR_ERR_ARG
+ *   n       multiple of 8, >= 0                          else AR_ERR_ARG
+ *   flags   AR_STAGE_RS | AR_STAGE_AG | AR_ORDER_RANK; no stage bit means
+ *           both stages; other bits                      -> AR_ERR_ARG
+ *   every data pointer 16-byte aligned                   else AR_ERR_ALIGN
+ */
+ar_status_t ar_reduce_2stage(const void *const *inputs, void *const *tmps,
+                             int W, int rank, void *out, int64_t n,
+                             unsigned flags, ar_stream_t stream);
+
+/*
+ * Fused all-reduce + residual add + RMSNorm ([TRIAR] "what this operator
+ * computes" and "overall design").  For every row m and column j:
+ *     a    = one-stage sum of inputs[r][m, j] (fp32, order 0..W-1)
+ *     h    = a + fp32(residual[m, j])               (fp32)
+ *     residual_out[m, j] = bf16(h)
+ *     rms  = 1 / sqrt(sum_j h^2 / N + eps)          (fp32, per row)
+ *     norm_out[m, j] = bf16((h * rms) * fp32(weight[j]))
+ * One workgroup owns a whole row, so h stays in registers between the sum
+ * and the norm.  residual_out is bit-exact; norm_out matches the exact value
+ * to within 2 bf16 ulp.
+ *   inputs       host table of W device pointers, each to bf16 [M, N]
+ *                row-major
+ *   W            2 <= W <= 8                            else AR_ERR_WORLD
+ *   residual     bf16 [M, N]
+ *   weight       bf16 [N]
+ *   residual_out bf16 [M, N]; may equal residual (in place)
+ *   norm_out     bf16 [M, N]; must not overlap any other buffer
+ *   M >= 0; 8 <= N <= 16384 and N multiple of 8; eps finite and >= 0
+ *                                                       else AR_ERR_ARG
+ *   every data pointer 16-byte aligned                   else AR_ERR_ALIGN
+ */
+ar_status_t ar_fused_residual_rmsnorm(const void *const *inputs, int W,
+                                      const void *residual, const void *weight,
+                                      void *residual_out, void *norm_out,
+                                      int64_t M, int64_t N, float eps,
+                                      ar_stream_t stream);
+
+/*
+ * LL wire format ([NCCL14] "LL's 16-byte FIFO line", "How LL publishes and
+ * waits for flags", "Prerequisite mental model").
+ * A FIFO is a ring of 8 steps of step_lines 16-byte lines.  The payload
+ * (the 4n bytes of n fp32 values, zero-padded to a multiple of 8) is cut
+ * into 8-byte pieces; piece i becomes the line
+ *     { u32 bytes[8i..8i+4), u32 flag, u32 bytes[8i+4..8i+8), u32 flag }
+ * of step k = first_step + i / step_lines, stored at line
+ * (k mod 8) * step_lines + (i mod step_lines), with flag = (uint32)(k + 1).
+ * FIFO lines not covered by the payload are left untouched.
+ *   src         n fp32, 4-byte aligned (any offset)      else AR_ERR_ALIGN
+ *   fifo        ll_fifo_bytes(step_lines) bytes, 16-byte aligned
+ *   step_lines  >= 1, and ll_lines(n) <= 8 * step_lines  else AR_ERR_CAPACITY
+ *               ll_lines(n) and 8 * step_lines below 2^31 else AR_ERR_ARG
+ */
+ar_status_t ll_pack(const float *src, int64_t n, void *fifo, int64_t step_lines,
+                    uint64_t first_step, ar_stream_t stream);
+
+/*
+ * LL decode + reduce.  For each line and each FIFO r (in order 0..W-1) the
+ * line is accepted only when both flags equal (uint32)(k + 1); otherwise it
+ * is re-read up to max_spins times (a bounded wait, never a hang) and, if
+ * still not accepted, counted as bad.  Element e (line e / 2, half e mod 2)
+ * of the output is the fp32 sum over FIFOs in order 0..W-1 starting from
+ * FIFO 0's value.  out[e] is unspecified where a line was bad in any FIFO.
+ *   fifos       host table of W device pointers (16-byte aligned)
+ *   W           1 <= W <= 8                               else AR_ERR_WORLD
+ *   out         n fp32, 4-byte aligned; only out[0..n) is written
+ *   max_spins   <= AR_MAX_SPINS                           else AR_ERR_ARG
+ *   bad_lines   device u32 (4-byte aligned) the caller zeroes; the library
+ *               adds the number of bad (FIFO, line) pairs.  NULL: not counted.
+ */
+ar_status_t ll_unpack_reduce(const void *const *fifos, int W, float *out,
+                             int64_t n, int64_t step_lines, uint64_t first_step,
+                             uint32_t max_spins, uint32_t *bad_lines,
+                             ar_stream_t stream);
+
+/*
+ * LL128 wire format ([NCCL14] "LL128's 128-byte line", "LL128's warp-level
+ * ready check", "Why LL128 alignment matters").  A 128-byte line is 16 u64
+ * words: words 0..14 carry payload bytes [120l, 120l + 120) in order (zero
+ * past the end), word 15 carries the flag (uint64)(k + 1).  Steps, slots and
+ * placement as for LL with 128-byte lines.  src may sit at any 4-byte offset.
+ *   fifo        ll128_fifo_bytes(step_lines) bytes, 128-byte aligned
+ *   other arguments and errors as ll_pack
+ */
+ar_status_t ll128_pack(const float *src, int64_t n, void *fifo,
+                       int64_t step_lines, uint64_t first_step,
+                       ar_stream_t stream);
+
+/*
+ * LL128 decode + reduce: a line is accepted when its flag word equals
+ * (uint64)(k + 1); re-reads, bad-line counting and the reduction are as for
+ * ll_unpack_reduce, with 30 fp32 values per line.
+ */
+ar_status_t ll128_unpack_reduce(const void *const *fifos, int W, float *out,
+                                int64_t n, int64_t step_lines,
+                                uint64_t first_step, uint32_t max_spins,
+                                uint32_t *bad_lines, ar_stream_t stream);
+
+/* Geometry helpers ([NCCL14] "Default buffers and effective data per
+ * step": the default buffers give 4096 LL lines and 4800 LL128 lines per
+ * step).  Negative arguments give 0. */
+int64_t ll_lines(int64_t n);                  /* ceil(4n / 8)   */
+int64_t ll128_lines(int64_t n);               /* ceil(4n / 120) */
+int64_t ll_fifo_bytes(int64_t step_lines);    /* 8 * step_lines * 16  */
+int64_t ll128_fifo_bytes(int64_t step_lines); /* 8 * step_lines * 128 */
+int64_t ll_default_step_lines(void);          /* 4096 */
+int64_t ll128_default_step_lines(void);       /* 4800 */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBAR_H */

@@ -17,6 +17,9 @@ def _ensure_built():
     import oracle
     if not os.path.exists(oracle.LIB):
         oracle.build()
+    from ar_rmsnorm_amd import build as arbuild
+    if not os.path.exists(arbuild.LIB):
+        arbuild.build()
 
 
 _ensure_built()

@@ -1,0 +1,159 @@
+"""The C-ABI library loads, exports every symbol include/libar.h declares, and
+its host-side logic (geometry helpers, argument checks) behaves as the header
+says.  No test here launches a kernel.
+
+The argument-error cases pass fake device addresses and rely on each check
+returning before anything is enqueued; to make sure no stray launch can ever
+reach a GPU with such addresses, this module only runs where no GPU is
+visible.  The same rejections with real device buffers are in the GPU tests.
+"""
+import os
+import re
+
+import pytest
+import torch
+
+from ar_rmsnorm_amd import libar as ar
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "libar.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\([^;{]*\)\s*;", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == sorted(ar.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ar.raw()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_geometry_helpers_match_printed_buffer_table():
+    # LL: 524288-byte default buffer / 8 steps / 16 B lines = 4096 lines, 32768
+    # payload bytes per step; LL128: 4915200 / 8 / 128 = 4800 lines, 576000 B.
+    assert ar.ll_default_step_lines() == 4096
+    assert ar.ll128_default_step_lines() == 4800
+    assert ar.ll_fifo_bytes(4096) == 524288
+    assert ar.ll128_fifo_bytes(4800) == 4915200
+    assert ar.ll_lines(32768 // 4) == 4096
+    assert ar.ll128_lines(576000 // 4) == 4800
+    assert ar.ll_lines(16_777_216) == 8_388_608
+    assert ar.ll_lines(16_777_229) == 8_388_615
+    assert ar.ll128_lines(16_777_216) == 559_241
+    assert ar.ll128_fifo_bytes(69_906) // 8 * 8 == 71_583_744
+    assert ar.ll128_lines(16_777_216) * 128 == 71_582_848
+    assert (ar.ll_lines(0), ar.ll_lines(-3), ar.ll_fifo_bytes(0)) == (0, 0, 0)
+
+
+def test_status_strings():
+    for s in range(7):
+        assert ar.status_str(s)
+    assert ar.status_str(0) == "ok"
+    assert ar.status_str(99) == "unknown status"
+
+
+# --------------------------------------------------------------------------
+# argument errors with fake addresses (never dereferenced)
+# --------------------------------------------------------------------------
+gpu_visible = torch.cuda.is_available()
+cpu_only = pytest.mark.skipif(gpu_visible, reason="fake-address error paths run only "
+                              "where no GPU can receive a launch")
+
+A = 0x7F0000000000          # 16-byte (and 128-byte) aligned fake addresses
+B = A + (1 << 30)
+C = A + (2 << 30)
+D = A + (3 << 30)
+E = A + (4 << 30)
+F = A + (5 << 30)
+
+
+def st(fn, *args):
+    try:
+        fn(*args)
+    except ar.ArError as e:
+        return e.status
+    return ar.AR_OK
+
+
+@cpu_only
+def test_reduce_1stage_argument_errors():
+    f = ar.ar_reduce_1stage
+    assert st(f, [A], B, 8, 0) == ar.AR_ERR_WORLD
+    assert st(f, [A] * 9, B, 8, 0) == ar.AR_ERR_WORLD
+    assert st(f, [A, None], B, 8, 0) == ar.AR_ERR_NULL
+    assert st(f, [A, B], None, 8, 0) == ar.AR_ERR_NULL
+    assert st(f, [A, B], C, 12, 0) == ar.AR_ERR_ARG
+    assert st(f, [A, B], C, -8, 0) == ar.AR_ERR_ARG
+    assert st(f, [A, B + 8], C, 8, 0) == ar.AR_ERR_ALIGN
+    assert st(f, [A, B], C + 4, 8, 0) == ar.AR_ERR_ALIGN
+    assert st(f, [A, B], A + 16, 64, 0) == ar.AR_ERR_ARG      # partial overlap
+    assert st(f, [A, B], C, 0, 0) == ar.AR_OK                 # empty: no launch
+
+
+@cpu_only
+def test_reduce_2stage_argument_errors():
+    f = ar.ar_reduce_2stage
+    ins, tms = [A, B], [C, D]
+    assert st(f, [A], [C], 0, E, 0, 8, 0) == ar.AR_ERR_WORLD
+    assert st(f, ins, tms, 2, E, 0, 8, 0) == ar.AR_ERR_ARG     # rank out of range
+    assert st(f, ins, tms, -1, E, 0, 8, 0) == ar.AR_ERR_ARG
+    assert st(f, ins, tms, 0, E, 8, 8, 0) == ar.AR_ERR_ARG     # unknown flag bit
+    assert st(f, ins, tms, 0, None, 0, 8, 0) == ar.AR_ERR_NULL  # AG needs out
+    assert st(f, ins, [C, None], 0, E, 0, 8, 0) == ar.AR_ERR_NULL
+    assert st(f, ins, tms, 0, E, 0, 9, 0) == ar.AR_ERR_ARG
+    assert st(f, ins, [C, D + 4], 0, E, 0, 8, 0) == ar.AR_ERR_ALIGN
+    assert st(f, ins, tms, 0, A, 0, 64, 0) == ar.AR_ERR_ARG    # out aliases input
+    assert st(f, ins, tms, 0, D, 0, 64, 0) == ar.AR_ERR_ARG    # out aliases tmp
+    assert st(f, ins, [A, D], 0, E, ar.AR_STAGE_RS, 64, 0) == ar.AR_ERR_ARG
+    assert st(f, ins, [C, C], 0, E, 0, 64, 0) == ar.AR_ERR_ARG  # own tmp = peer tmp
+    assert st(f, ins, tms, 0, E, 0, 0, 0) == ar.AR_OK
+
+
+@cpu_only
+def test_fused_argument_errors():
+    f = ar.ar_fused_residual_rmsnorm
+    ins = [A, B]
+    assert st(f, [A], C, D, E, F, 1e-6, 1, 2048, 0) == ar.AR_ERR_WORLD
+    assert st(f, ins, None, D, E, F, 1e-6, 1, 2048, 0) == ar.AR_ERR_NULL
+    assert st(f, ins, C, D, E, F, 1e-6, 1, 2044, 0) == ar.AR_ERR_ARG
+    assert st(f, ins, C, D, E, F, 1e-6, 1, 16392, 0) == ar.AR_ERR_ARG
+    assert st(f, ins, C, D, E, F, 1e-6, -1, 2048, 0) == ar.AR_ERR_ARG
+    assert st(f, ins, C, D, E, F, float("nan"), 1, 2048, 0) == ar.AR_ERR_ARG
+    assert st(f, ins, C, D, E, F, -1.0, 1, 2048, 0) == ar.AR_ERR_ARG
+    assert st(f, ins, C, D + 2, E, F, 1e-6, 1, 2048, 0) == ar.AR_ERR_ALIGN
+    assert st(f, ins, C, D, E, A, 1e-6, 1, 2048, 0) == ar.AR_ERR_ARG   # norm_out = input
+    assert st(f, ins, C, D, E, E, 1e-6, 1, 2048, 0) == ar.AR_ERR_ARG   # norm = res_out
+    assert st(f, ins, C, D, C + 16, F, 1e-6, 1, 2048, 0) == ar.AR_ERR_ARG
+    assert st(f, ins, C, D, C, F, 1e-6, 0, 2048, 0) == ar.AR_OK        # in place, M=0
+
+
+@cpu_only
+def test_wire_argument_errors():
+    assert st(ar.ll_pack, A, B, 0, 0, 9, 0) == ar.AR_ERR_ARG            # step_lines 0
+    assert st(ar.ll_pack, A, B, 1, 0, 17, 0) == ar.AR_ERR_CAPACITY      # 9 lines > 8
+    assert st(ar.ll_pack, A + 2, B, 1, 0, 8, 0) == ar.AR_ERR_ALIGN
+    assert st(ar.ll_pack, B + 4, B, 1, 0, 8, 0) == ar.AR_ERR_ARG        # src in fifo
+    assert st(ar.ll_pack, A + 4, B + 8, 1, 0, 8, 0) == ar.AR_ERR_ALIGN
+    assert st(ar.ll128_pack, A, B + 64, 1, 0, 8, 0) == ar.AR_ERR_ALIGN  # 128 B lines
+    assert st(ar.ll128_pack, A, B, 1, 0, 241, 0) == ar.AR_ERR_CAPACITY
+    assert st(ar.ll_pack, None, B, 1, 0, 8, 0) == ar.AR_ERR_NULL
+    assert st(ar.ll_pack, A, B, 1, 0, 0, 0) == ar.AR_OK
+    u = ar.ll_unpack_reduce
+    assert st(u, [], C, 1, 0, 0, None, 8, 0) == ar.AR_ERR_WORLD
+    assert st(u, [A] * 9, C, 1, 0, 0, None, 8, 0) == ar.AR_ERR_WORLD
+    assert st(u, [A, None], C, 1, 0, 0, None, 8, 0) == ar.AR_ERR_NULL
+    assert st(u, [A], C, 1, 0, ar.AR_MAX_SPINS + 1, None, 8, 0) == ar.AR_ERR_ARG
+    assert st(u, [A], C, 1, 0, 0, None, 17, 0) == ar.AR_ERR_CAPACITY
+    assert st(u, [A], C + 2, 1, 0, 0, None, 8, 0) == ar.AR_ERR_ALIGN
+    assert st(u, [A], C, 1, 0, 0, D + 2, 8, 0) == ar.AR_ERR_ALIGN
+    assert st(u, [A], A + 16, 1, 0, 0, None, 8, 0) == ar.AR_ERR_ARG     # out in fifo
+    assert st(u, [A], C, 1, 0, 0, C + 4, 8, 0) == ar.AR_ERR_ARG         # counter in out
+    assert st(ar.ll128_unpack_reduce, [A + 16], C, 1, 0, 0, None, 8, 0) == ar.AR_ERR_ALIGN
+    assert st(u, [A], C, 1, 0, 0, None, 0, 0) == ar.AR_OK

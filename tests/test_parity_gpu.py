@@ -1,0 +1,386 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, on the
+same seeded inputs, element by element.
+
+Bar: the reduce forms, the copies, the wire encodings and decodings and the
+fused residual_out are bit-exact; the fused norm_out is within 2 bf16 ulp of
+the oracle's exact value (or 1e-2 absolute).  Sizes span several workgroups
+and ragged tails; the workloads' full sizes are checked in full (the C oracle
+finishes them in well under a second each).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from ar_rmsnorm_amd import libar as ar
+from ar_rmsnorm_amd import synth
+from tests.util import dev_f32, dev_u8, dev_u16, host_u16, norm_within_tolerance
+
+pytestmark = pytest.mark.gpu
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+def run_1stage(xs, device, n=None):
+    n = xs[0].size if n is None else n
+    d = [dev_u16(x, device) for x in xs]
+    out = torch.empty(n + 64, dtype=torch.int16, device=device).fill_(0x5A5A)
+    ar.ar_reduce_1stage(d, out, n=n)
+    sync()
+    h = host_u16(out)
+    assert np.all(h[n:] == 0x5A5A), "wrote past n"
+    return h[:n]
+
+
+# ---------------------------------------------------------------------------
+# one-stage
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("maker", ["reduce_small", "reduce_decode"])
+def test_1stage_workloads(gpu, maker):
+    xs = getattr(synth, maker)()
+    assert np.array_equal(run_1stage(xs, gpu), orc.reduce_1stage(xs))
+
+
+@pytest.mark.parametrize("W", range(2, 9))
+def test_1stage_ragged_all_world_sizes(gpu, W):
+    n = 8 * (256 * 5 + 37)           # 5 full workgroups and a ragged one
+    xs = synth.reduce_inputs(W, n, [77, W])
+    assert np.array_equal(run_1stage(xs, gpu), orc.reduce_1stage(xs))
+
+
+def test_1stage_at_the_cap_full_compare(gpu):
+    xs = synth.reduce_cap()
+    assert np.array_equal(run_1stage(xs, gpu), orc.reduce_1stage(xs))
+
+
+def test_1stage_single_pack_and_empty(gpu):
+    xs = synth.reduce_inputs(3, 8, [78])
+    assert np.array_equal(run_1stage(xs, gpu), orc.reduce_1stage(xs))
+    d = [dev_u16(x, gpu) for x in xs]
+    out = torch.full((8,), 7, dtype=torch.int16, device=gpu)
+    ar.ar_reduce_1stage(d, out, n=0)
+    sync()
+    assert torch.all(out == 7)
+
+
+def test_1stage_in_place(gpu):
+    xs = synth.reduce_inputs(4, 8 * 1000, [79])
+    d = [dev_u16(x, gpu) for x in xs]
+    ar.ar_reduce_1stage(d, d[0])
+    sync()
+    assert np.array_equal(host_u16(d[0]), orc.reduce_1stage(xs))
+
+
+def test_1stage_rounding_ties_and_specials(gpu):
+    """Ties of the final rounding (x0 + half an ulp of x0, both signs, odd and
+    even kept parts), absorption (order), zeros, denormals, inf and NaN."""
+    g = np.random.default_rng(80)
+    n = 8 * 4096
+    x0 = synth.normal_bf16(g, n)
+    e = (x0.astype(np.int32) >> 7) & 0xFF
+    e = np.clip(e, 10, 240)
+    # half an ulp of x0: exponent e - 8, mantissa 0 -> 2^(e-127-8)
+    half = ((e - 8) << 7).astype(np.uint16)
+    sgn = g.integers(0, 2, n).astype(np.uint16) << 15
+    x0 = ((x0 & 0x807F) | (e << 7).astype(np.uint16)).astype(np.uint16)
+    x1 = (half | sgn).astype(np.uint16)
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x7F80, 0xFF80,
+                         0x7FC0, 0x7F7F, 0xFF7F, 0x3F80, 0x4B80, 0xCB80], np.uint16)
+    k = specials.size
+    x0[:k * k] = np.repeat(specials, k)
+    x1[:k * k] = np.tile(specials, k)
+    got = run_1stage([x0, x1], gpu)
+    want = orc.reduce_1stage([x0, x1])
+    nan_w = ((want & 0x7F80) == 0x7F80) & ((want & 0x7F) != 0)
+    nan_g = ((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)
+    assert np.array_equal(nan_g, nan_w)
+    assert np.array_equal(got[~nan_w], want[~nan_w])
+    # the order case of the oracle pins: (1, 2^24, 1, -2^24) -> 0
+    xs = [np.full(64, v, np.uint16) for v in (0x3F80, 0x4B80, 0x3F80, 0xCB80)]
+    assert np.all(run_1stage(xs, gpu) == 0)
+
+
+# ---------------------------------------------------------------------------
+# two-stage
+# ---------------------------------------------------------------------------
+def run_2stage_all_ranks(xs, device, flags_extra=0):
+    """Every rank's RS (rank order of launches 1..W-1, 0), then each rank's
+    all-gather; returns (outs per rank, tmps per shard)."""
+    W, n = len(xs), xs[0].size
+    P = n // 8
+    part, rem = P // W, P % W
+    d = [dev_u16(x, device) for x in xs]
+    cap = (part + rem) * 8
+    tmps = [torch.full((cap + 64,), 0x3C3C, dtype=torch.int16, device=device) for _ in range(W)]
+    for r in range(1, W):
+        ar.ar_reduce_2stage(d, tmps, r, None, flags=ar.AR_STAGE_RS | flags_extra)
+    outs = []
+    for r in range(W):
+        out = torch.full((n + 64,), 0x5A5A, dtype=torch.int16, device=device)
+        if r == 0:           # rank 0 runs both stages in one launch
+            ar.ar_reduce_2stage(d, tmps, 0, out, flags=flags_extra)
+        else:
+            ar.ar_reduce_2stage(d, tmps, r, out, flags=ar.AR_STAGE_AG | flags_extra)
+        outs.append(out)
+    sync()
+    ho = [host_u16(o) for o in outs]
+    for h in ho:
+        assert np.all(h[n:] == 0x5A5A)
+    ht = [host_u16(t) for t in tmps]
+    for s in range(W):
+        size = (part + (rem if s == W - 1 else 0)) * 8
+        assert np.all(ht[s][size:] == 0x3C3C), "tmp written past its shard"
+    return [h[:n] for h in ho], [ht[s] for s in range(W)]
+
+
+def test_2stage_cap_workload_full_compare(gpu):
+    xs = synth.reduce_cap()
+    outs, tmps = run_2stage_all_ranks(xs, gpu)
+    want = orc.reduce_2stage(xs)
+    for r, o in enumerate(outs):
+        assert np.array_equal(o, want), f"rank {r}"
+    for s in range(8):
+        ts = orc.reduce_scatter(xs, s)
+        assert np.array_equal(tmps[s][:ts.size], ts), f"shard {s}"
+
+
+@pytest.mark.parametrize("W,P", [(2, 1027), (3, 8 * 300 + 5), (4, 3), (5, 5 * 256 + 4),
+                                 (7, 7 * 1000 + 6), (8, 8 * 1000 + 5), (8, 8)])
+def test_2stage_partitions_and_remainders(gpu, W, P):
+    xs = synth.reduce_inputs(W, 8 * P, [81, W, P])
+    outs, _ = run_2stage_all_ranks(xs, gpu)
+    want = orc.reduce_2stage(xs)
+    for o in outs:
+        assert np.array_equal(o, want)
+    if W == 2:
+        assert np.array_equal(outs[0], orc.reduce_1stage(xs))
+
+
+def test_2stage_rank_order_flag(gpu):
+    xs = synth.reduce_inputs(6, 8 * 6 * 500, [82])
+    outs, _ = run_2stage_all_ranks(xs, gpu, ar.AR_ORDER_RANK)
+    want = orc.reduce_2stage(xs, rank_order=True)
+    assert np.array_equal(want, orc.reduce_1stage(xs))
+    for o in outs:
+        assert np.array_equal(o, want)
+
+
+def test_2stage_rotation_hand_case(gpu):
+    xs = [np.full(32, v, np.uint16) for v in (0x3F80, 0x4B80, 0x3F80, 0xCB80)]
+    outs, _ = run_2stage_all_ranks(xs, gpu)
+    vals = orc.bf16_to_f32(outs[2]).reshape(4, 8)[:, 0]
+    assert list(vals) == [0.0, 1.0, 2.0, 2.0]
+
+
+# ---------------------------------------------------------------------------
+# fused all-reduce + residual + RMSNorm
+# ---------------------------------------------------------------------------
+def run_fused(xs, res, w, eps, device, in_place=False):
+    M, N = res.shape
+    d = [dev_u16(x, device) for x in xs]
+    dr = dev_u16(res, device)
+    dw = dev_u16(w, device)
+    ro = dr if in_place else torch.full((M, N), 0x1111, dtype=torch.int16, device=device)
+    no = torch.full((M * N + 64,), 0x5A5A, dtype=torch.int16, device=device)
+    ar.ar_fused_residual_rmsnorm(d, dr, dw, ro, no, eps, M=M, N=N)
+    sync()
+    hn = host_u16(no)
+    assert np.all(hn[M * N:] == 0x5A5A)
+    return host_u16(ro).reshape(M, N), hn[:M * N].reshape(M, N)
+
+
+def check_fused(xs, res, w, eps, device, in_place=False):
+    ro, no = run_fused(xs, res, w, eps, device, in_place)
+    wro, wno, exact = orc.fused_residual_rmsnorm(xs, res, w, eps)
+    assert np.array_equal(ro, wro), "residual_out not bit-exact"
+    ok, worst = norm_within_tolerance(no, exact)
+    assert ok.all(), f"norm_out outside tolerance at {np.argwhere(~ok)[:5]}"
+    return worst
+
+
+@pytest.mark.parametrize("M", [1, 16, 128])
+def test_fused_workloads(gpu, M):
+    xs, res, w = synth.fused(M)
+    worst = check_fused(xs, res, w, synth.FUSED["eps"], gpu)
+    assert worst <= 2.0
+
+
+@pytest.mark.parametrize("W,M,N", [(2, 3, 8), (8, 2, 512), (3, 5, 1000),
+                                   (4, 4, 1024), (5, 2, 4096), (6, 2, 8192), (8, 2, 16384),
+                                   (7, 3, 2056), (2, 1, 520)])
+def test_fused_shapes(gpu, W, M, N):
+    xs, res, w = synth.fused_inputs(W, M, N, [83, W, M, N])
+    check_fused(xs, res, w, 1e-6, gpu)
+
+
+def test_fused_in_place_and_constant_rows(gpu):
+    xs, res, w = synth.fused_inputs(4, 8, 2048, [84])
+    check_fused(xs, res, w, 1e-6, gpu, in_place=True)
+    M, N = 3, 2048
+    one = [np.full((M, N), 0x3F80, np.uint16)] + [np.zeros((M, N), np.uint16)] * 3
+    _, no = run_fused(one, np.zeros((M, N), np.uint16), w, 1e-6, gpu)
+    assert np.array_equal(no, np.broadcast_to(w, (M, N)))
+
+
+# ---------------------------------------------------------------------------
+# LL / LL128 wire formats
+# ---------------------------------------------------------------------------
+FMT = {
+    "ll": dict(pack=ar.ll_pack, unpack=ar.ll_unpack_reduce, lines=ar.ll_lines, size=16,
+               opack=orc.ll_pack, ounpack=orc.ll_unpack_reduce),
+    "ll128": dict(pack=ar.ll128_pack, unpack=ar.ll128_unpack_reduce, lines=ar.ll128_lines,
+                  size=128, opack=orc.ll128_pack, ounpack=orc.ll128_unpack_reduce),
+}
+
+
+def gpu_pack(fmt, x, step_lines, first_step, device, src_offset=0, fill=0xEE):
+    f = FMT[fmt]
+    n = x.size
+    raw = torch.zeros(n + 8, dtype=torch.float32, device=device)
+    src = raw[src_offset // 4: src_offset // 4 + n]
+    src.copy_(torch.from_numpy(x))
+    fifo = torch.full((8 * step_lines * f["size"],), fill, dtype=torch.uint8, device=device)
+    f["pack"](src, fifo, step_lines, first_step)
+    return fifo
+
+
+def gpu_unpack(fmt, fifos, n, step_lines, first_step, device, max_spins=0):
+    f = FMT[fmt]
+    out = torch.full((n + 16,), 12345.0, dtype=torch.float32, device=device)
+    bad = torch.zeros(1, dtype=torch.int32, device=device)
+    f["unpack"](fifos, out, step_lines, first_step, max_spins, bad, n=n)
+    sync()
+    o = out.cpu().numpy()
+    assert np.all(o[n:] == 12345.0), "wrote past n"
+    return o[:n], int(bad.item())
+
+
+@pytest.mark.parametrize("fmt", ["ll", "ll128"])
+@pytest.mark.parametrize("n", [synth.WIRE["n"], synth.WIRE["n"] + synth.WIRE["tail"]])
+def test_wire_workload_full_compare(gpu, fmt, n):
+    f = FMT[fmt]
+    xs = synth.wire(n)
+    L = f["lines"](n)
+    sl = -(-L // 8)
+    fifos = []
+    for x in xs:
+        g = gpu_pack(fmt, x, sl, 0, gpu)
+        want = np.full(8 * sl * f["size"], 0xEE, np.uint8)
+        f["opack"](x, want, sl, 0)
+        assert np.array_equal(g.cpu().numpy(), want), "wire bytes differ"
+        fifos.append(g)
+    out, bad = gpu_unpack(fmt, fifos, n, sl, 0, gpu)
+    wout, valid, wbad = f["ounpack"]([fi.cpu().numpy() for fi in fifos], n, sl, 0)
+    assert bad == 0 and wbad == 0 and valid.all()
+    assert np.array_equal(out.view(np.uint32), wout.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", ["ll", "ll128"])
+@pytest.mark.parametrize("n,sl,first", [(1, 1, 0), (2, 1, 7), (29, 1, 6), (31, 2, 3),
+                                        (997, 64, 5), (4096 + 13, 300, 2 ** 32 - 2),
+                                        (30 * 8 * 40, 40, 11)])
+def test_wire_small_geometries(gpu, fmt, n, sl, first):
+    f = FMT[fmt]
+    sl = max(sl, -(-f["lines"](n) // 8))
+    g = np.random.default_rng([85, n])
+    xs = [g.standard_normal(n).astype(np.float32) for _ in range(3)]
+    fifos = []
+    for x in xs:
+        gf = gpu_pack(fmt, x, sl, first, gpu)
+        want = np.full(8 * sl * f["size"], 0xEE, np.uint8)
+        f["opack"](x, want, sl, first)
+        assert np.array_equal(gf.cpu().numpy(), want)
+        fifos.append(gf)
+    out, bad = gpu_unpack(fmt, fifos, n, sl, first, gpu)
+    wout, _, wbad = f["ounpack"]([fi.cpu().numpy() for fi in fifos], n, sl, first)
+    assert bad == wbad == 0
+    assert np.array_equal(out.view(np.uint32), wout.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", ["ll", "ll128"])
+@pytest.mark.parametrize("offset", [4, 8, 12])
+def test_wire_pack_unaligned_source(gpu, fmt, offset):
+    n, sl = 30 * 1000 + 13, 4000
+    x = np.random.default_rng(offset).standard_normal(n).astype(np.float32)
+    a = gpu_pack(fmt, x, sl, 0, gpu)
+    b = gpu_pack(fmt, x, sl, 0, gpu, src_offset=offset)
+    sync()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("fmt", ["ll", "ll128"])
+def test_wire_decode_counts_host_planted_corruption(gpu, fmt):
+    """Flags corrupted from the host; the kernel's bounded re-reads end and
+    the bad (FIFO, line) pairs are counted exactly, as by the oracle."""
+    f = FMT[fmt]
+    n, W, first = 30 * 2000 + 7, 4, 1
+    L = f["lines"](n)
+    sl = -(-L // 8)
+    xs = synth.wire_payloads(W, n, [86])
+    fifos = [gpu_pack(fmt, x, sl, first, gpu) for x in xs]
+    host = [fi.cpu().numpy() for fi in fifos]
+    flag_byte = 12 if fmt == "ll" else 120
+    g = np.random.default_rng(87)
+    planted = 0
+    for r in range(W):
+        for line in g.choice(L, size=5 + r, replace=False):
+            k = first + line // sl
+            wire = (k % 8) * sl + line % sl
+            host[r][wire * f["size"] + flag_byte] ^= 0x40
+            planted += 1
+    bad_fifos = [dev_u8(h, gpu) for h in host]
+    out, bad = gpu_unpack(fmt, bad_fifos, n, sl, first, gpu, max_spins=3)
+    wout, valid, wbad = f["ounpack"](host, n, sl, first)
+    assert bad == wbad == planted
+    assert np.array_equal(out[valid].view(np.uint32), wout[valid].view(np.uint32))
+    # a stale round (one lap ahead) and a zeroed FIFO: every pair is bad
+    _, bad = gpu_unpack(fmt, fifos, n, sl, first + 8, gpu, max_spins=1)
+    assert bad == W * L
+    zeros = [torch.zeros_like(fi) for fi in fifos]
+    _, bad = gpu_unpack(fmt, zeros, n, sl, 0, gpu, max_spins=0)
+    assert bad == W * L
+
+
+@pytest.mark.parametrize("fmt", ["ll", "ll128"])
+def test_wire_cross_oracle_packed_fifo(gpu, fmt):
+    """The GPU decoder reads FIFOs the oracle encoded."""
+    f = FMT[fmt]
+    n, W = 30 * 777 + 19, 5
+    L = f["lines"](n)
+    sl = -(-L // 8) + 3
+    xs = synth.wire_payloads(W, n, [88])
+    host = []
+    for x in xs:
+        h = np.zeros(8 * sl * f["size"], np.uint8)
+        f["opack"](x, h, sl, 4)
+        host.append(h)
+    out, bad = gpu_unpack(fmt, [dev_u8(h, gpu) for h in host], n, sl, 4, gpu)
+    wout, _, wbad = f["ounpack"](host, n, sl, 4)
+    assert bad == wbad == 0
+    assert np.array_equal(out.view(np.uint32), wout.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# argument errors with real device buffers (any launch would stay in bounds)
+# ---------------------------------------------------------------------------
+def test_argument_errors_with_device_buffers(gpu):
+    a = torch.zeros(4096, dtype=torch.int16, device=gpu)
+    b = torch.zeros(4096, dtype=torch.int16, device=gpu)
+    o = torch.zeros(4096, dtype=torch.int16, device=gpu)
+    with pytest.raises(ar.ArError) as e:
+        ar.ar_reduce_1stage([a, b], o, n=12)
+    assert e.value.status == ar.AR_ERR_ARG
+    with pytest.raises(ar.ArError) as e:
+        ar.ar_reduce_1stage([a[1:], b], o, n=8)
+    assert e.value.status == ar.AR_ERR_ALIGN
+    with pytest.raises(ar.ArError) as e:
+        ar.ar_reduce_1stage([a], o, n=8)
+    assert e.value.status == ar.AR_ERR_WORLD
+    fifo = torch.zeros(8 * 16, dtype=torch.uint8, device=gpu)
+    src = torch.zeros(64, dtype=torch.float32, device=gpu)
+    with pytest.raises(ar.ArError) as e:
+        ar.ll_pack(src, fifo, 1, n=17)
+    assert e.value.status == ar.AR_ERR_CAPACITY
+    sync()
