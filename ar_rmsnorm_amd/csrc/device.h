@@ -22,6 +22,38 @@ typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// Streaming accesses for data touched exactly once per launch (the rank
+// buffers, staging shards, wire FIFOs and outputs): the nontemporal hint
+// sets the nt cache policy on gfx950 so these streams do not displace other
+// lines in L2 / Infinity Cache and their writes drain during the kernel
+// rather than at its end.
+__device__ __forceinline__ u32x4 ld_stream(const u32x4 *p)
+{
+    return __builtin_nontemporal_load(p);
+}
+__device__ __forceinline__ void st_stream(u32x4 *p, u32x4 v)
+{
+    __builtin_nontemporal_store(v, p);
+}
+// Forms for addresses that are only 4-byte aligned (fp32 payloads): the cast
+// to the aligned(4) vector types keeps that alignment visible to the compiler.
+__device__ __forceinline__ u32x4 ld4_stream_a4(const uint32_t *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_a4 *>(p));
+}
+__device__ __forceinline__ u32x2 ld2_stream_a4(const uint32_t *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2_a4 *>(p));
+}
+__device__ __forceinline__ void st4_stream_a4(uint32_t *p, u32x4 v)
+{
+    __builtin_nontemporal_store(u32x4_a4(v), reinterpret_cast<u32x4_a4 *>(p));
+}
+__device__ __forceinline__ void st2_stream_a4(uint32_t *p, u32x2 v)
+{
+    __builtin_nontemporal_store(u32x2_a4(v), reinterpret_cast<u32x2_a4 *>(p));
+}
+
 // Kernel-argument pointer tables, passed by value so no device-side
 // indirection is needed (the W pointers land in SGPRs).
 template <int W>

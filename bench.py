@@ -22,7 +22,7 @@ known size) and is null when the kernel source changed since it was taken.
 per-rank two-stage work, repeated for about 10 s.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                       [--rows all|none] [--calib-copy]
+                       [--rows all|none] [--eager] [--calib-copy]
 """
 from __future__ import annotations
 
@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=24)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--rows", choices=["all", "none"], default="all")
+    p.add_argument("--eager", action="store_true",
+                   help="time eager launches instead of a HIP graph replay")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (counter calibration)")
     return p.parse_args()
@@ -113,6 +115,15 @@ def main():
                 fns[i % len(fns)]()
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
+        if args.eager:
+            start = torch.cuda.Event(enable_timing=True)
+            stop = torch.cuda.Event(enable_timing=True)
+            start.record()
+            for i in range(steps):
+                fns[i % len(fns)]()
+            stop.record()
+            stop.synchronize()
+            return start.elapsed_time(stop) / steps
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(steps):
