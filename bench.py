@@ -267,7 +267,8 @@ def main():
             [lambda s=s: ar.ar_reduce_1stage(s[0], s[1]) for s in s1], steps=8 * k1)
         del s1
 
-        # wire formats: W=4 fp32 payloads of 16 Mi values (and the +13 tail)
+        # wire formats: W=4 fp32 payloads of 16 Mi values (and the +13 tail);
+        # every row rotates buffer sets so each call streams from HBM
         wc = synth.WIRE
         for nn in (wc["n"], wc["n"] + wc["tail"]):
             payloads = [torch.from_numpy(p).to(dev) for p in synth.wire(nn)]
@@ -276,24 +277,34 @@ def main():
                     ("ll", 16, ar.ll_lines, ar.ll_pack, ar.ll_unpack_reduce)):
                 L = lines_fn(nn)
                 sl = -(-L // 8)
-                fifos = [torch.empty(8 * sl * lsize, dtype=torch.uint8, device=dev)
-                         for _ in range(wc["W"])]
-                for p, f in zip(payloads, fifos):
-                    pack(p, f, sl)
-                out = torch.empty(nn, dtype=torch.float32, device=dev)
                 tag = f"{fmt}_W4_n{nn}"
-                row(f"{tag}_decode", wc["W"] * L * lsize + 4 * nn,
-                    [lambda f=fifos, o=out, sl=sl: unpack(f, o, sl)], steps=40)
-                row(f"{fmt}_n{nn}_pack", 4 * nn + L * lsize,
-                    [lambda p=payloads[0], f=fifos[0], sl=sl: pack(p, f, sl)], steps=40)
-                if nn == wc["n"]:
-                    # source at a 4-byte offset: same wire bytes, cost of misalignment
-                    raw = torch.empty(nn + 4, dtype=torch.float32, device=dev)
-                    src = raw[1:1 + nn]
-                    src.copy_(payloads[0])
-                    row(f"{fmt}_n{nn}_pack_src_offset4", 4 * nn + L * lsize,
-                        [lambda p=src, f=fifos[0], sl=sl: pack(p, f, sl)], steps=40)
-                del fifos, out
+                dec_bytes = wc["W"] * L * lsize + 4 * nn
+                dsets = []
+                for _ in range(sets_for(dec_bytes)):
+                    fifos = [torch.empty(8 * sl * lsize, dtype=torch.uint8, device=dev)
+                             for _ in range(wc["W"])]
+                    for p, f in zip(payloads, fifos):
+                        pack(p, f, sl)
+                    dsets.append((fifos, torch.empty(nn, dtype=torch.float32, device=dev)))
+                row(f"{tag}_decode", dec_bytes,
+                    [lambda d=d, sl=sl: unpack(d[0], d[1], sl) for d in dsets],
+                    steps=8 * len(dsets))
+                del dsets
+                pack_bytes = 4 * nn + L * lsize
+                offsets = (0, 1) if nn == wc["n"] else (0,)
+                for off in offsets:
+                    psets = []
+                    for _ in range(sets_for(pack_bytes)):
+                        raw = torch.empty(nn + 4, dtype=torch.float32, device=dev)
+                        src = raw[off:off + nn]
+                        src.copy_(payloads[0])
+                        psets.append((raw, src, torch.empty(8 * sl * lsize, dtype=torch.uint8,
+                                                            device=dev)))
+                    name = f"{fmt}_n{nn}_pack" + ("_src_offset4" if off else "")
+                    row(name, pack_bytes,
+                        [lambda q=q, sl=sl: pack(q[1], q[2], sl) for q in psets],
+                        steps=8 * len(psets))
+                    del psets
             del payloads
             torch.cuda.empty_cache()
         result["rows"] = rows
