@@ -13,14 +13,16 @@
 //
 // All four kernels are streams (LL moves 16 wire bytes per 8 payload bytes,
 // LL128 128 per 120), so they are bound by HBM bandwidth.  Every lane moves
-// 16-byte chunks: LL gives a lane one whole line; LL128 gives eight lanes one
-// 128-byte line, lane 7 of each group holding the line's last payload word
-// and its flag word (the flag-lane arrangement of [NCCL14] "LL128's
-// warp-level ready check").  The payload side of LL128 is 120 bytes per line,
-// so its addresses are only 8-byte aligned; gfx950 accepts dwordx4 accesses
-// at dword alignment, so no staging through LDS is needed for that, nor for
-// sources at a 4/8/12-byte offset ([NCCL14] "why LL128 alignment matters"
-// stages misaligned sources through shared memory on its hardware).
+// 16-byte chunks: LL gives a lane one whole line; the LL128 decoder gives
+// eight lanes one 128-byte line, lane 7 of each group holding the line's last
+// payload word and its flag word (the flag-lane arrangement of [NCCL14]
+// "LL128's warp-level ready check"); the LL128 encoder gives sixteen lanes
+// two lines so that its payload loads stay 16-byte aligned.  Where payload
+// addresses are only 4- or 8-byte aligned (the decoder's 120-byte output
+// spans, sources at a 4/8/12-byte offset) gfx950's dwordx4 accesses at dword
+// alignment are used directly; no staging through LDS is needed
+// ([NCCL14] "why LL128 alignment matters" stages misaligned sources through
+// shared memory on its hardware).
 #include "device.h"
 #include "launch.h"
 
@@ -55,7 +57,9 @@ __global__ __launch_bounds__(kWireThreads) void ll_pack_kernel(
     const int64_t e = 2 * (int64_t)i;
     uint32_t lo, hi;
     if (e + 1 < n) {
-        const u32x2 d = ld2_stream_a4(src + e);
+        // a plain load: measured faster than a streaming one for these
+        // 8-byte source reads, while the 16-byte FIFO stores stream
+        const u32x2 d = *reinterpret_cast<const u32x2_a4 *>(src + e);
         lo = d.x;
         hi = d.y;
     } else {           // last line of an odd count: zero padding
@@ -118,45 +122,59 @@ __global__ __launch_bounds__(kWireThreads) void ll_unpack_reduce_kernel(
 
 // ---------------------------------------------------------------------------
 // LL128 ([NCCL14] "LL128's 128-byte line"): 15 payload u64 + 1 flag u64.
-// Lane j of a group of 8 owns bytes [16j, 16j + 16) of the line, i.e.
-// payload fp32 words 30l + 4j .. +3; lane 7 owns words 28, 29 and the flag.
+// Wire chunk j (16 bytes) of a line: payload fp32 words 30l + 4j .. +3 for
+// j < 7; chunk 7 holds words 28, 29 and the flag.
+//
+// Encode: sixteen lanes (one DPP row) build two consecutive lines from their
+// 240-byte payload span.  Lane c < 15 loads the c-th 16-byte chunk of the
+// span, so every payload load is a whole, aligned dwordx4 (when src is
+// 16-byte aligned).  Line A's chunks are those loads as they are; line B
+// starts 8 bytes into chunk 7, so its chunk j is the high half of span chunk
+// 7 + j (held by the lane to the left, fetched with DPP row_shr:1) followed
+// by the low half of span chunk 8 + j.  Lanes 7 and 15 put the flags in.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kWireThreads) void ll128_pack_kernel(
     const uint32_t *src, int64_t n, u32x4 *fifo, uint32_t lines,
     uint32_t step_lines, uint64_t first_step)
 {
     const uint64_t t = (uint64_t)blockIdx.x * kWireThreads + threadIdx.x;
-    const uint32_t l = (uint32_t)(t >> 3);
-    const int j = (int)(t & 7);
-    if (l >= lines)
-        return;
-    const StepPos sp = step_pos(l, step_lines, first_step);
-    const int64_t e0 = 30 * (int64_t)l + 4 * j;
-    u32x4 d;
-    if (j < 7) {
+    const uint32_t pair = (uint32_t)(t >> 4);
+    const int c = (int)(t & 15);
+    const uint32_t la = 2 * pair, lb = la + 1;
+    const bool live = la < lines;          // the same for all 16 lanes of a pair
+    const int64_t e0 = 60 * (int64_t)pair + 4 * c;
+    u32x4 d = {0u, 0u, 0u, 0u};
+    if (live && c < 15) {
         if (e0 + 3 < n) {
             d = ld4_stream_a4(src + e0);
         } else {
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                d[c] = e0 + c < n ? src[e0 + c] : 0u;
+            for (int k = 0; k < 4; ++k)
+                d[k] = e0 + k < n ? src[e0 + k] : 0u;
         }
-    } else {
-        const uint64_t flag = sp.step + 1;
-        if (e0 + 1 < n) {
-            const u32x2 p = ld2_stream_a4(src + e0);
-            d.x = p.x;
-            d.y = p.y;
-        } else {
-            d.x = e0 < n ? src[e0] : 0u;
-            d.y = 0u;
-        }
-        d.z = (uint32_t)flag;
-        d.w = (uint32_t)(flag >> 32);
     }
-    st_stream(fifo + sp.line * 8 + j, d);
+    // Every lane takes part in the row shift; lane 0 of a row receives 0.
+    const uint32_t hz = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)d.z, 0x111, 0xF, 0xF, false);
+    const uint32_t hw = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)d.w, 0x111, 0xF, 0xF, false);
+    if (!live || (c >= 8 && lb >= lines))
+        return;
+    const uint32_t line = c < 8 ? la : lb;
+    const StepPos sp = step_pos(line, step_lines, first_step);
+    const uint64_t flag = sp.step + 1;
+    u32x4 o;
+    if (c < 7)
+        o = d;
+    else if (c == 7)
+        o = u32x4{d.x, d.y, (uint32_t)flag, (uint32_t)(flag >> 32)};
+    else if (c < 15)
+        o = u32x4{hz, hw, d.x, d.y};
+    else
+        o = u32x4{hz, hw, (uint32_t)flag, (uint32_t)(flag >> 32)};
+    st_stream(fifo + sp.line * 8 + (c & 7), o);
 }
 
+// Decode: eight lanes per line, lane j owning wire chunk j (an aligned
+// dwordx4 load from each FIFO); lane 7 also holds the flag.
 template <int W>
 __global__ __launch_bounds__(kWireThreads) void ll128_unpack_reduce_kernel(
     InTable<W> fifos, float *out, int64_t n, uint32_t lines, uint32_t step_lines,
@@ -247,7 +265,8 @@ hipError_t launch_ll128_pack(const float *src, int64_t n, void *fifo,
                              hipStream_t s)
 {
     const uint32_t lines = (uint32_t)((n + 29) / 30);
-    ll128_pack_kernel<<<blocks_for((uint64_t)lines * 8), kWireThreads, 0, s>>>(
+    const uint64_t pairs = ((uint64_t)lines + 1) / 2;
+    ll128_pack_kernel<<<blocks_for(pairs * 16), kWireThreads, 0, s>>>(
         reinterpret_cast<const uint32_t *>(src), n, static_cast<u32x4 *>(fifo),
         lines, (uint32_t)step_lines, first_step);
     return hipGetLastError();
