@@ -57,41 +57,52 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_1stage_kernel(
 }
 
 // Two-stage reduce for one rank ([SGLv1] "2stage: sharding, rotation, and
-// why no exit barrier").  Grid: x covers the packs of the largest shard,
-// y selects i = blockIdx.y and the shard g = (rank + i) mod W it moves.
-//   i == 0, RS   : reduce this rank's shard (inputs in `in` order, i.e. the
-//                  owner's rotation), store to tmps[rank], and with AG also
-//                  to out.  The value goes from registers to out, and each
-//                  lane gathers exactly the packs it reduced, which is the
-//                  pages' same-thread mapping, so no barrier is needed.
-//   i == 0, AG only: copy tmps[rank] to out.
-//   i >  0, AG   : copy shard g from tmps[g] to out.
+// why no exit barrier").  One-dimensional grid, reduce blocks first:
+//   blocks [0, rs_blocks) (RS): reduce this rank's shard, inputs in `in`
+//       order (the owner's rotation), store to tmps[rank] and, with AG, to
+//       out.  The value goes from registers to out and each lane gathers
+//       exactly the packs it reduced (the pages' same-thread mapping), so no
+//       barrier is needed inside the launch.
+//   the remaining blocks (AG): cp_blocks per shard, copying shard
+//       g = (rank + i) mod W from tmps[g] to out, for i = 1..W-1 after an RS,
+//       or i = 0..W-1 for an all-gather alone.
+// The gather reads use plain loads and everything else streams: on cold
+// data that measured fastest among the cache-policy combinations.
 template <int W, bool RS, bool AG>
 __global__ __launch_bounds__(kReduceThreads) void reduce_2stage_kernel(
     InTable<W> in, OutTable<W> tmps, int rank, u32x4 *out, int64_t part,
-    int64_t rem)
+    int64_t rem, uint32_t rs_blocks, uint32_t cp_blocks)
 {
-    const int64_t idx = (int64_t)blockIdx.x * kReduceThreads + threadIdx.x;
-    const int i = blockIdx.y;
+    const uint32_t b = blockIdx.x;
+    const int t = threadIdx.x;
+    if (RS && b < rs_blocks) {
+        const int64_t idx = (int64_t)b * kReduceThreads + t;
+        const int64_t own = part + (rank == W - 1 ? rem : 0);
+        if (idx >= own)
+            return;
+        const int64_t dst = (int64_t)rank * part + idx;
+        u32x4 v[W];
+#pragma unroll
+        for (int r = 0; r < W; ++r)
+            v[r] = ld_stream(in.p[r] + dst);
+        const u32x4 s = reduce_column<W>(v);
+        st_stream(tmps.p[rank] + idx, s);
+        if (AG)
+            st_stream(out + dst, s);
+        return;
+    }
+    if (!AG)
+        return;
+    const uint32_t k = RS ? b - rs_blocks : b;
+    const int i = (RS ? 1 : 0) + (int)(k / cp_blocks);
+    const int64_t idx = (int64_t)(k % cp_blocks) * kReduceThreads + t;
     int g = rank + i;
     if (g >= W)
         g -= W;
     const int64_t size = part + (g == W - 1 ? rem : 0);
     if (idx >= size)
         return;
-    const int64_t dst = (int64_t)g * part + idx;
-    if (RS && i == 0) {
-        u32x4 v[W];
-#pragma unroll
-        for (int r = 0; r < W; ++r)
-            v[r] = ld_stream(in.p[r] + dst);
-        const u32x4 s = reduce_column<W>(v);
-        st_stream(tmps.p[g] + idx, s);
-        if (AG)
-            st_stream(out + dst, s);
-    } else {
-        st_stream(out + dst, ld_stream(tmps.p[g] + idx));
-    }
+    st_stream(out + (int64_t)g * part + idx, tmps.p[g][idx]);
 }
 
 template <int W>
@@ -127,13 +138,15 @@ static hipError_t launch_2stage_mode(const InTable<W> &in, const OutTable<W> &tm
                                      int rank, void *out, int64_t part,
                                      int64_t rem, hipStream_t s)
 {
-    const int64_t span = AG ? part + rem : part + (rank == W - 1 ? rem : 0);
-    const int64_t blocks = (span + kReduceThreads - 1) / kReduceThreads;
+    const int64_t own = part + (rank == W - 1 ? rem : 0);
+    const int64_t rs_blocks = RS ? (own + kReduceThreads - 1) / kReduceThreads : 0;
+    const int64_t cp_blocks = (part + rem + kReduceThreads - 1) / kReduceThreads;
+    const int64_t blocks = rs_blocks + (AG ? (RS ? W - 1 : W) * cp_blocks : 0);
     if (blocks == 0)
         return hipSuccess;
-    const dim3 grid((unsigned)blocks, AG ? W : 1);
-    reduce_2stage_kernel<W, RS, AG><<<grid, dim3(kReduceThreads), 0, s>>>(
-        in, tmps, rank, static_cast<u32x4 *>(out), part, rem);
+    reduce_2stage_kernel<W, RS, AG><<<dim3((unsigned)blocks), dim3(kReduceThreads), 0, s>>>(
+        in, tmps, rank, static_cast<u32x4 *>(out), part, rem, (uint32_t)rs_blocks,
+        (uint32_t)cp_blocks);
     return hipGetLastError();
 }
 
