@@ -221,7 +221,9 @@ def main():
     # ------------------------------------------------------------------
     rows = {}
 
-    def row(name, nbytes, fns, steps=None, extra=None):
+    def row(name, nbytes, fns, steps=None, extra=None, oracle_fn=None):
+        """Time one row on the GPU; with the CPU leg on, also time the oracle
+        doing the same work (repeated until ~0.3 s, single-threaded)."""
         k = steps or max(60, len(fns))
         k -= k % len(fns)
         t = graph_time(fns, k, args.warmup)
@@ -230,9 +232,24 @@ def main():
              "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
         if extra:
             r.update(extra)
+        if oracle_fn is not None and not args.no_cpu:
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                oracle_fn()
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= 0.3 or reps >= 50:
+                    break
+            r["oracle_ms"] = round(el / reps * 1e3, 3)
+            r["oracle_GBps"] = round(nbytes * reps / el / 1e9, 3)
         rows[name] = r
-        log(f"row {name}: {r['us_per_call']} us, {r['GBps']} GB/s")
+        log(f"row {name}: {r['us_per_call']} us, {r['GBps']} GB/s"
+            + (f"; oracle {r['oracle_ms']} ms" if "oracle_ms" in r else ""))
         return r
+
+    orc = None
+    if not args.no_cpu:
+        import oracle as orc
 
     if args.rows == "all":
         # fused all-reduce + residual + RMSNorm, W=4, N=2048, M in {1, 16, 128}
@@ -246,7 +263,9 @@ def main():
             no = torch.empty_like(dr)
             call = (lambda d=d, dr=dr, dw=dw, ro=ro, no=no:
                     ar.ar_fused_residual_rmsnorm(d, dr, dw, ro, no, fc["eps"]))
-            row(f"fused_W4_M{M}_N2048", nb, [call], steps=200)
+            row(f"fused_W4_M{M}_N2048", nb, [call], steps=200,
+                oracle_fn=orc and (lambda fx=fx, fr=fr, fw=fw:
+                                   orc.fused_residual_rmsnorm(fx, fr, fw, fc["eps"])))
         result["fused_m1_us_per_call"] = rows["fused_W4_M1_N2048"]["us_per_call"]
 
         # one-stage reduce: small, decode shape, and the cap message
@@ -256,7 +275,13 @@ def main():
             d = [to_dev(x) for x in xx]
             o = torch.empty_like(d[0])
             row(name, (len(d) + 1) * d[0].numel() * 2,
-                [lambda d=d, o=o: ar.ar_reduce_1stage(d, o)], steps=200)
+                [lambda d=d, o=o: ar.ar_reduce_1stage(d, o)], steps=200,
+                oracle_fn=orc and (lambda xx=xx: orc.reduce_1stage(xx)))
+        # the per-launch floor: a one-stage reduce of a single 16-byte pack
+        d = [to_dev(x[:8]) for x in synth.reduce_small()]
+        o = torch.empty_like(d[0])
+        row("launch_floor_1stage_W2_n8", 48, [lambda d=d, o=o: ar.ar_reduce_1stage(d, o)],
+            steps=200)
         nb = (W + 1) * n * 2
         k1 = sets_for(nb)
         s1 = []
@@ -264,17 +289,41 @@ def main():
             ins = [b.clone() for b in base]
             s1.append((ins, torch.empty(n, dtype=torch.int16, device=dev)))
         row("1stage_W8_n4194304", nb,
-            [lambda s=s: ar.ar_reduce_1stage(s[0], s[1]) for s in s1], steps=8 * k1)
+            [lambda s=s: ar.ar_reduce_1stage(s[0], s[1]) for s in s1], steps=8 * k1,
+            oracle_fn=orc and (lambda: orc.reduce_1stage(xs)))
         del s1
+
+        # the same per-rank two-stage call on 4x larger buffers (W=8 x 32 MiB):
+        # separates the kernel's streaming rate from the per-launch floor
+        n4 = 4 * n
+        part4 = n4 // 8 // W
+        nb4 = (W + 2 + 2 * (W - 1)) * part4 * 16
+        big = [torch.cat([b] * 4) for b in base]
+        s4 = []
+        for k in range(sets_for(nb4)):
+            ins = big if k == 0 else [b.clone() for b in big]
+            tmps = [torch.empty(part4 * 8, dtype=torch.int16, device=dev) for _ in range(W)]
+            for r in range(1, W):
+                ar.ar_reduce_2stage(ins, tmps, r, None, flags=ar.AR_STAGE_RS)
+            s4.append((ins, tmps, torch.empty(n4, dtype=torch.int16, device=dev)))
+        row("2stage_W8_n16777216_per_rank", nb4,
+            [lambda s=s: ar.ar_reduce_2stage(s[0], s[1], 0, s[2]) for s in s4],
+            steps=8 * len(s4))
+        del s4, big
+        torch.cuda.empty_cache()
 
         # wire formats: W=4 fp32 payloads of 16 Mi values (and the +13 tail);
         # every row rotates buffer sets so each call streams from HBM
         wc = synth.WIRE
         for nn in (wc["n"], wc["n"] + wc["tail"]):
-            payloads = [torch.from_numpy(p).to(dev) for p in synth.wire(nn)]
+            host_payloads = synth.wire(nn)
+            payloads = [torch.from_numpy(p).to(dev) for p in host_payloads]
             for fmt, lsize, lines_fn, pack, unpack in (
                     ("ll128", 128, ar.ll128_lines, ar.ll128_pack, ar.ll128_unpack_reduce),
                     ("ll", 16, ar.ll_lines, ar.ll_pack, ar.ll_unpack_reduce)):
+                opack = orc and (orc.ll128_pack if fmt == "ll128" else orc.ll_pack)
+                ounpack = orc and (orc.ll128_unpack_reduce if fmt == "ll128"
+                                   else orc.ll_unpack_reduce)
                 L = lines_fn(nn)
                 sl = -(-L // 8)
                 tag = f"{fmt}_W4_n{nn}"
@@ -286,9 +335,15 @@ def main():
                     for p, f in zip(payloads, fifos):
                         pack(p, f, sl)
                     dsets.append((fifos, torch.empty(nn, dtype=torch.float32, device=dev)))
+                hfifos = None
+                if orc:
+                    hfifos = [np.zeros(8 * sl * lsize, np.uint8) for _ in host_payloads]
+                    for hp, hf in zip(host_payloads, hfifos):
+                        opack(hp, hf, sl)
                 row(f"{tag}_decode", dec_bytes,
                     [lambda d=d, sl=sl: unpack(d[0], d[1], sl) for d in dsets],
-                    steps=8 * len(dsets))
+                    steps=8 * len(dsets),
+                    oracle_fn=orc and (lambda hf=hfifos, nn=nn, sl=sl: ounpack(hf, nn, sl)))
                 del dsets
                 pack_bytes = 4 * nn + L * lsize
                 offsets = (0, 1) if nn == wc["n"] else (0,)
@@ -303,8 +358,12 @@ def main():
                     name = f"{fmt}_n{nn}_pack" + ("_src_offset4" if off else "")
                     row(name, pack_bytes,
                         [lambda q=q, sl=sl: pack(q[1], q[2], sl) for q in psets],
-                        steps=8 * len(psets))
+                        steps=8 * len(psets),
+                        oracle_fn=(orc and not off and
+                                   (lambda hp=host_payloads[0], hf=hfifos[0], sl=sl:
+                                    opack(hp, hf, sl))) or None)
                     del psets
+                del hfifos
             del payloads
             torch.cuda.empty_cache()
         result["rows"] = rows
@@ -321,7 +380,6 @@ def main():
     # ------------------------------------------------------------------
     if not args.no_cpu:
         log("CPU oracle baseline (~10 s)")
-        import oracle as orc
         tmps = [orc.reduce_scatter(xs, s) for s in range(W)]
         reps, t0 = 0, time.perf_counter()
         while True:

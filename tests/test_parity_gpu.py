@@ -384,3 +384,52 @@ def test_argument_errors_with_device_buffers(gpu):
         ar.ll_pack(src, fifo, 1, n=17)
     assert e.value.status == ar.AR_ERR_CAPACITY
     sync()
+
+
+# ---------------------------------------------------------------------------
+# HIP graph capture: the bench times graph replays, so replays must equal
+# eager calls (several replays, with eager work and syncs in between)
+# ---------------------------------------------------------------------------
+def test_graph_replays_match_eager(gpu):
+    xs = synth.reduce_decode()
+    d = [dev_u16(x, gpu) for x in xs]
+    fx, fr, fw = synth.fused(16)
+    fd = [dev_u16(x, gpu) for x in fx]
+    dr, dw = dev_u16(fr, gpu), dev_u16(fw, gpu)
+    n = 30 * 500 + 13
+    payload = torch.from_numpy(synth.wire_payloads(1, n, [89])[0]).to(gpu)
+    sl = -(-ar.ll128_lines(n) // 8)
+    outs = {
+        "r1": torch.empty_like(d[0]),
+        "ro": torch.empty_like(dr), "no": torch.empty_like(dr),
+        "fifo": torch.zeros(8 * sl * 128, dtype=torch.uint8, device=gpu),
+        "dec": torch.empty(n, dtype=torch.float32, device=gpu),
+    }
+
+    def work():
+        ar.ar_reduce_1stage(d, outs["r1"])
+        ar.ar_fused_residual_rmsnorm(fd, dr, dw, outs["ro"], outs["no"], 1e-6)
+        ar.ll128_pack(payload, outs["fifo"], sl)
+        ar.ll128_unpack_reduce([outs["fifo"], outs["fifo"]], outs["dec"], sl)
+
+    work()
+    sync()
+    ref = {k: v.clone() for k, v in outs.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()
+    torch.cuda.current_stream().wait_stream(s)
+    sync()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    for rep in range(3):
+        for v in outs.values():
+            v.zero_()                      # eager work between replays
+        sync()
+        g.replay()
+        sync()
+        for k in outs:
+            assert torch.equal(outs[k], ref[k]), f"replay {rep}: {k} differs"
+    assert torch.equal(ref["dec"], payload + payload)
