@@ -73,6 +73,14 @@ def lib():
             getattr(L, name).restype = _i64
         for name in ("orc_ll_pack", "orc_ll128_pack"):
             getattr(L, name).argtypes = [_p, _i64, _p, _i64, _u64]
+        L.orc_lamport_pack.argtypes = [ctypes.c_uint16, ctypes.c_uint16]
+        L.orc_lamport_pack.restype = ctypes.c_uint32
+        L.orc_lamport_push.argtypes = [_p, ctypes.c_int, ctypes.c_int, _p, _i64, _i64,
+                                       ctypes.c_uint32]
+        L.orc_lamport_fused_residual_rmsnorm.argtypes = [_p, ctypes.c_int, _p, _p, _p, _p, _p,
+                                                         _i64, _i64, ctypes.c_double,
+                                                         ctypes.c_uint32]
+        L.orc_lamport_fused_residual_rmsnorm.restype = _i64
         for name in ("orc_ll_unpack_reduce", "orc_ll128_unpack_reduce"):
             getattr(L, name).argtypes = [_p, ctypes.c_int, _p, _p, _i64, _i64, _u64]
             getattr(L, name).restype = _i64
@@ -232,3 +240,45 @@ def ll_unpack_reduce(fifos, n: int, step_lines: int, first_step: int = 0):
 
 def ll128_unpack_reduce(fifos, n: int, step_lines: int, first_step: int = 0):
     return _unpack(lib().orc_ll128_unpack_reduce, fifos, n, step_lines, first_step)
+
+
+# --------------------------------------------------------------------------
+# Lamport data-as-flag wire for the fused one-shot
+# --------------------------------------------------------------------------
+LAMPORT_SENTINEL = 0x80008000
+
+
+def lamport_comm(W: int, M: int, N: int) -> np.ndarray:
+    """A comm buffer of one rank, filled with the sentinel: u32 words
+    [3 regions][W slots][M][N / 2]."""
+    return np.full(3 * W * M * N // 2, LAMPORT_SENTINEL, np.uint32)
+
+
+def lamport_pack(lo: int, hi: int) -> int:
+    return int(lib().orc_lamport_pack(lo, hi))
+
+
+def lamport_push(x, rank: int, comms, flag: int) -> None:
+    """Rank `rank` pushes bf16 [M, N] x into the comm buffers of all W ranks
+    (in place); `comms` lists those W buffers, so W = len(comms)."""
+    x = _u16(x)
+    M, N = x.shape
+    for c in comms:
+        assert c.dtype == np.uint32 and c.flags.c_contiguous
+    lib().orc_lamport_push(_ptr(x), len(comms), rank, _ptr_table(comms), M, N, flag)
+
+
+def lamport_fused_residual_rmsnorm(comm, W: int, residual, weight, eps: float, flag: int):
+    """Reader side for one rank; returns (residual_out, norm_out, norm_exact,
+    bad_chunks).  Resets region (flag + 2) % 3 of `comm` in place."""
+    residual = _u16(residual)
+    M, N = residual.shape
+    weight = _u16(weight).reshape(N)
+    assert comm.dtype == np.uint32 and comm.flags.c_contiguous
+    res_out = np.empty((M, N), np.uint16)
+    norm_out = np.empty((M, N), np.uint16)
+    norm_exact = np.empty((M, N), np.float64)
+    bad = lib().orc_lamport_fused_residual_rmsnorm(
+        _ptr(comm), W, _ptr(residual), _ptr(weight), _ptr(res_out), _ptr(norm_out),
+        _ptr(norm_exact), M, N, float(eps), flag)
+    return res_out, norm_out, norm_exact, int(bad)

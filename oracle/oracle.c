@@ -434,3 +434,83 @@ void orc_bf16_from_f64_array(const double *x, uint16_t *out, int64_t n)
     for (int64_t i = 0; i < n; ++i)
         out[i] = orc_bf16_from_f64(x[i]);
 }
+
+/* ---------------------------------------------------------------------------
+ * Lamport data-as-flag wire for the fused one-shot.
+ * [TRIAR] "Option 2: Lamport": each rank pushes its bf16 row to every peer
+ * as u32 words holding two bf16 (element 2j in the low half).  Before
+ * packing, a bf16 -0.0 (0x8000) is scrubbed to +0.0, so no word can equal
+ * the sentinel 0x80008000 (two -0.0) that fills an empty comm buffer; a
+ * reader polls until no word is the sentinel.  The buffer is used in three
+ * regions selected by flag mod 3.
+ * Layout read here: comm[region][slot r][row m][word j], region = flag % 3,
+ * slot = the pushing rank.  After reading region flag % 3 the reader resets
+ * region (flag + 2) % 3 (the region of the previous call) to the sentinel:
+ * every peer finished writing it before the previous call could complete,
+ * and peers write it again only two calls later.
+ * ------------------------------------------------------------------------- */
+#define ORC_LAMPORT_SENTINEL 0x80008000u
+
+uint32_t orc_lamport_pack(uint16_t lo, uint16_t hi)
+{
+    if (lo == 0x8000u)
+        lo = 0;
+    if (hi == 0x8000u)
+        hi = 0;
+    return (uint32_t)lo | ((uint32_t)hi << 16);
+}
+
+/* Rank `rank` pushes its [M, N] row block into every rank's comm buffer. */
+void orc_lamport_push(const uint16_t *x, int W, int rank, uint32_t *const *comms,
+                      int64_t M, int64_t N, uint32_t flag)
+{
+    const int64_t words = M * N / 2;
+    const int64_t region = (int64_t)(flag % 3u);
+    for (int p = 0; p < W; ++p) {
+        uint32_t *slot = comms[p] + (region * W + rank) * words;
+        for (int64_t q = 0; q < words; ++q)
+            slot[q] = orc_lamport_pack(x[2 * q], x[2 * q + 1]);
+    }
+}
+
+/* Reader side for one rank: returns the number of (slot, 16-byte chunk)
+ * units that still hold a sentinel word (their outputs are unspecified).
+ * The reduction and the norm are the fused operator above, applied to the
+ * unpacked slots in slot order 0..W-1. */
+int64_t orc_lamport_fused_residual_rmsnorm(uint32_t *comm, int W,
+                                           const uint16_t *residual,
+                                           const uint16_t *weight,
+                                           uint16_t *residual_out,
+                                           uint16_t *norm_out, double *norm_exact,
+                                           int64_t M, int64_t N, double eps,
+                                           uint32_t flag)
+{
+    const int64_t words = M * N / 2;
+    const int64_t region = (int64_t)(flag % 3u);
+    int64_t bad = 0;
+    uint16_t *xs[8] = {0};
+    for (int r = 0; r < W; ++r) {
+        const uint32_t *slot = comm + (region * W + r) * words;
+        xs[r] = (uint16_t *)malloc((size_t)(M * N) * sizeof(uint16_t));
+        for (int64_t q = 0; q < words; ++q) {
+            xs[r][2 * q] = (uint16_t)(slot[q] & 0xFFFFu);
+            xs[r][2 * q + 1] = (uint16_t)(slot[q] >> 16);
+        }
+        for (int64_t c = 0; c < words / 4; ++c) {
+            int any = 0;
+            for (int k = 0; k < 4; ++k)
+                any |= slot[4 * c + k] == ORC_LAMPORT_SENTINEL;
+            bad += any;
+        }
+    }
+    float *h = (float *)malloc((size_t)N * sizeof(float));
+    orc_fused_residual_rmsnorm((const uint16_t *const *)xs, W, residual, weight,
+                               residual_out, norm_out, norm_exact, M, N, eps, h);
+    free(h);
+    for (int r = 0; r < W; ++r)
+        free(xs[r]);
+    const int64_t stale = (int64_t)((flag + 2u) % 3u);
+    for (int64_t q = 0; q < (int64_t)W * words; ++q)
+        comm[stale * W * words + q] = ORC_LAMPORT_SENTINEL;
+    return bad;
+}

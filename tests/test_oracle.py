@@ -21,6 +21,7 @@ import pytest
 import torch
 
 import oracle as orc
+from ar_rmsnorm_amd import synth
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -508,3 +509,123 @@ def test_pack_from_unaligned_source_gives_same_wire(fmt, offset):
     pack(x, a, sl)
     pack(view, b, sl)
     assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# Lamport data-as-flag wire ([TRIAR] "Option 2: Lamport")
+# ---------------------------------------------------------------------------
+SENT = orc.LAMPORT_SENTINEL
+
+
+@pytest.mark.parametrize("lo,hi,want", [
+    (0x3F80, 0x4000, 0x40003F80),   # element 2j in the low half
+    (0x8000, 0x3F80, 0x3F800000),   # -0.0 scrubbed to +0.0 (low)
+    (0x3F80, 0x8000, 0x00003F80),   # -0.0 scrubbed to +0.0 (high)
+    (0x8000, 0x8000, 0x00000000),   # two -0.0: not the sentinel
+    (0x8001, 0xFF80, 0xFF808001),   # other negatives untouched
+    (0x0000, 0x7FC0, 0x7FC00000),
+])
+def test_lamport_pack_hand_cases(lo, hi, want):
+    assert orc.lamport_pack(lo, hi) == want
+
+
+def test_lamport_pack_never_produces_the_sentinel():
+    """Exhaustive over every bf16 paired with -0.0 on either side: only a
+    -0.0/-0.0 pair could form 0x80008000, and scrubbing removes it."""
+    v = np.arange(65536, dtype=np.uint16)
+    for pair in (np.stack([v, np.full_like(v, 0x8000)], 1),
+                 np.stack([np.full_like(v, 0x8000), v], 1)):
+        x = pair.reshape(1, -1)
+        comm = orc.lamport_comm(1, 1, x.shape[1])
+        orc.lamport_push(x, 0, [comm], 0)
+        words = comm[: x.shape[1] // 2]
+        assert not np.any(words == SENT)
+        lo, hi = (words & 0xFFFF).astype(np.uint16), (words >> 16).astype(np.uint16)
+        want = np.where(pair == 0x8000, 0, pair).astype(np.uint16)
+        assert np.array_equal(lo, want[:, 0]) and np.array_equal(hi, want[:, 1])
+
+
+def test_lamport_regions_hand_example():
+    """W=2, M=1, N=8: a slot is 4 words, a region 2 slots (8 words).  Flag 4
+    uses region 4 % 3 = 1 (words 8..15: slot 0 at 8, slot 1 at 12) and the
+    reader then resets region (4 + 2) % 3 = 0 (words 0..7)."""
+    x0 = np.array([[0x3F80, 0x4000, 0x4040, 0x4080, 0x40A0, 0x40C0, 0x40E0, 0x4100]],
+                  np.uint16)                                  # 1..8
+    x1 = np.array([[0x3F80] * 8], np.uint16)                  # 1.0
+    comms = [np.full(3 * 2 * 4, 0x11111111, np.uint32) for _ in range(2)]
+    orc.lamport_push(x0, 0, comms, 4)
+    orc.lamport_push(x1, 1, comms, 4)
+    for c in comms:
+        assert list(c[8:12]) == [0x40003F80, 0x40804040, 0x40C040A0, 0x410040E0]
+        assert list(c[12:16]) == [0x3F803F80] * 4
+        assert np.all(c[0:8] == 0x11111111) and np.all(c[16:24] == 0x11111111)
+    res = np.zeros((1, 8), np.uint16)
+    w = np.full(8, 0x3F80, np.uint16)
+    ro, no, ne, bad = orc.lamport_fused_residual_rmsnorm(comms[0], 2, res, w, 1e-6, 4)
+    assert bad == 0
+    assert list(orc.bf16_to_f32(ro[0])) == [2, 3, 4, 5, 6, 7, 8, 9]
+    assert np.all(comms[0][0:8] == SENT)                      # region 0 reset
+    assert np.all(comms[0][16:24] == 0x11111111)              # region 2 untouched
+    assert list(comms[0][12:16]) == [0x3F803F80] * 4          # region 1 kept
+
+
+def test_lamport_fused_equals_the_fused_operator():
+    """Without -0.0 inputs the Lamport path computes exactly the fused
+    operator (already pinned above) on the pushed rows."""
+    W, M, N, eps = 4, 16, 2048, 1e-6
+    xs, res, w = synth.fused_inputs(W, M, N, [90])
+    for x in xs:
+        assert not np.any(x == 0x8000)
+    comms = [orc.lamport_comm(W, M, N) for _ in range(W)]
+    for r, x in enumerate(xs):
+        orc.lamport_push(x, r, comms, 7)
+    want = orc.fused_residual_rmsnorm(xs, res, w, eps)
+    for p in range(W):
+        ro, no, ne, bad = orc.lamport_fused_residual_rmsnorm(comms[p], W, res, w, eps, 7)
+        assert bad == 0
+        assert np.array_equal(ro, want[0]) and np.array_equal(no, want[1])
+        assert np.array_equal(ne, want[2])
+
+
+def test_lamport_scrub_changes_the_sign_of_an_all_negative_zero_sum():
+    """All inputs and the residual -0.0: the fused operator gives -0.0 for
+    residual_out, the Lamport path +0.0 (its inputs were scrubbed)."""
+    W, M, N = 2, 1, 16
+    xs = [np.full((M, N), 0x8000, np.uint16) for _ in range(W)]
+    res = np.full((M, N), 0x8000, np.uint16)
+    w = np.full(N, 0x3F80, np.uint16)
+    assert np.all(orc.fused_residual_rmsnorm(xs, res, w, 1e-6)[0] == 0x8000)
+    comms = [orc.lamport_comm(W, M, N) for _ in range(W)]
+    for r, x in enumerate(xs):
+        orc.lamport_push(x, r, comms, 0)
+    ro, _, _, bad = orc.lamport_fused_residual_rmsnorm(comms[0], W, res, w, 1e-6, 0)
+    assert bad == 0 and np.all(ro == 0x0000)
+
+
+def test_lamport_counts_missing_pushes():
+    W, M, N = 3, 2, 64
+    xs, res, w = synth.fused_inputs(W, M, N, [91])
+    comms = [orc.lamport_comm(W, M, N) for _ in range(W)]
+    orc.lamport_push(xs[0], 0, comms, 2)        # rank 1 never pushes
+    orc.lamport_push(xs[2], 2, comms, 2)
+    *_, bad = orc.lamport_fused_residual_rmsnorm(comms[0], W, res, w, 1e-6, 2)
+    assert bad == M * N // 8                    # every chunk of slot 1
+
+
+def test_lamport_triple_buffer_invariant_over_calls():
+    """Before the pushes of call f, region f % 3 of every buffer is all
+    sentinel: it was reset by call f - 2 and untouched by call f - 1."""
+    W, M, N = 3, 2, 32
+    comms = [orc.lamport_comm(W, M, N) for _ in range(W)]
+    words = M * N // 2
+    for f in range(7):
+        xs, res, w = synth.fused_inputs(W, M, N, [92, f])
+        for c in comms:
+            reg = c.reshape(3, W * words)[f % 3]
+            assert np.all(reg == SENT), f
+        for r, x in enumerate(xs):
+            orc.lamport_push(x, r, comms, f)
+        want = orc.fused_residual_rmsnorm(xs, res, w, 1e-6)
+        for p in range(W):
+            ro, no, _, bad = orc.lamport_fused_residual_rmsnorm(comms[p], W, res, w, 1e-6, f)
+            assert bad == 0 and np.array_equal(ro, want[0]) and np.array_equal(no, want[1])
