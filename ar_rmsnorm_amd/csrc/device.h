@@ -54,6 +54,27 @@ __device__ __forceinline__ void st2_stream_a4(uint32_t *p, u32x2 v)
     __builtin_nontemporal_store(u32x2_a4(v), reinterpret_cast<u32x2_a4 *>(p));
 }
 
+// Lamport push: clear every bf16 half equal to -0.0 (0x8000), so that no
+// u32 word of two bf16 can equal the sentinel 0x80008000.
+__device__ __forceinline__ u32x4 scrub_negative_zero(u32x4 v)
+{
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t w = v[k];
+        const uint32_t lo = (w & 0xFFFFu) == 0x8000u ? 0xFFFFu : 0u;
+        const uint32_t hi = (w & 0xFFFF0000u) == 0x80000000u ? 0xFFFF0000u : 0u;
+        v[k] = w & ~(lo | hi);
+    }
+    return v;
+}
+
+// Re-read one 16-byte chunk past the caches (a real load on every spin of a
+// bounded flag wait).
+__device__ __forceinline__ u32x4 reload16(const u32x4 *p)
+{
+    return *reinterpret_cast<const volatile u32x4 *>(p);
+}
+
 // Kernel-argument pointer tables, passed by value so no device-side
 // indirection is needed (the W pointers land in SGPRs).
 template <int W>

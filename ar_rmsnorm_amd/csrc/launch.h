@@ -21,6 +21,17 @@ hipError_t launch_fused_rmsnorm(const void *const *inputs, int W,
                                 void *residual_out, void *norm_out, int64_t M,
                                 int64_t N, float eps, hipStream_t s);
 
+hipError_t launch_lamport_fill(void *comm, int64_t chunks, hipStream_t s);
+hipError_t launch_lamport_push(const void *x, int W, int rank, void *const *comms,
+                               int64_t M, int64_t N, uint32_t flag, hipStream_t s);
+// x_self == NULL: reader only; otherwise also push x_self as rank `rank`
+// into every buffer of `comms` in the same launch (comm == comms[rank]).
+hipError_t launch_lamport_fused(void *comm, int W, const void *residual,
+                                const void *weight, void *residual_out, void *norm_out,
+                                int64_t M, int64_t N, float eps, uint32_t flag,
+                                uint32_t max_spins, uint32_t *bad, const void *x_self,
+                                int rank, void *const *comms, hipStream_t s);
+
 hipError_t launch_ll_pack(const float *src, int64_t n, void *fifo,
                           int64_t step_lines, uint64_t first_step, hipStream_t s);
 hipError_t launch_ll_unpack_reduce(const void *const *fifos, int W, float *out,

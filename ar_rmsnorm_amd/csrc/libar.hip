@@ -176,6 +176,160 @@ LIBAR_EXPORT ar_status_t ar_fused_residual_rmsnorm(const void *const *inputs, in
 }
 
 // ---------------------------------------------------------------------------
+// Lamport data-as-flag fused one-shot
+// ---------------------------------------------------------------------------
+namespace {
+
+bool fused_shape_ok(int64_t M, int64_t N)
+{
+    return M >= 0 && M <= 0x7FFFFFFF && N >= 8 && N <= AR_FUSED_MAX_N && N % 8 == 0;
+}
+
+}  // namespace
+
+LIBAR_EXPORT int64_t ar_lamport_comm_bytes(int W, int64_t M, int64_t N)
+{
+    if (W < 2 || W > AR_MAX_WORLD || !fused_shape_ok(M, N))
+        return 0;
+    return 3 * (int64_t)W * M * N * 2;
+}
+
+LIBAR_EXPORT ar_status_t ar_lamport_fill(void *comm, int W, int64_t M, int64_t N,
+                                         ar_stream_t stream)
+{
+    if (!comm)
+        return AR_ERR_NULL;
+    if (W < 2 || W > AR_MAX_WORLD)
+        return AR_ERR_WORLD;
+    if (!fused_shape_ok(M, N))
+        return AR_ERR_ARG;
+    if (!aligned(comm, 16))
+        return AR_ERR_ALIGN;
+    if (M == 0)
+        return AR_OK;
+    return from_hip(ar::launch_lamport_fill(comm, ar_lamport_comm_bytes(W, M, N) / 16,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+LIBAR_EXPORT ar_status_t ar_lamport_push(const void *x, int W, int rank, void *const *comms,
+                                         int64_t M, int64_t N, uint32_t flag,
+                                         ar_stream_t stream)
+{
+    if (!x || !comms)
+        return AR_ERR_NULL;
+    if (W < 2 || W > AR_MAX_WORLD)
+        return AR_ERR_WORLD;
+    for (int p = 0; p < W; ++p)
+        if (!comms[p])
+            return AR_ERR_NULL;
+    if (rank < 0 || rank >= W || !fused_shape_ok(M, N))
+        return AR_ERR_ARG;
+    if (!aligned(x, 16))
+        return AR_ERR_ALIGN;
+    for (int p = 0; p < W; ++p)
+        if (!aligned(comms[p], 16))
+            return AR_ERR_ALIGN;
+    const int64_t cb = ar_lamport_comm_bytes(W, M, N);
+    for (int p = 0; p < W; ++p) {
+        if (overlaps(x, 2 * M * N, comms[p], cb))
+            return AR_ERR_ARG;
+        for (int q = 0; q < p; ++q)
+            if (overlaps(comms[p], cb, comms[q], cb))
+                return AR_ERR_ARG;
+    }
+    if (M == 0)
+        return AR_OK;
+    return from_hip(ar::launch_lamport_push(x, W, rank, comms, M, N, flag,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+LIBAR_EXPORT ar_status_t ar_lamport_fused_residual_rmsnorm(
+    void *comm, int W, const void *residual, const void *weight, void *residual_out,
+    void *norm_out, int64_t M, int64_t N, float eps, uint32_t flag, uint32_t max_spins,
+    uint32_t *bad_chunks, ar_stream_t stream)
+{
+    if (!comm || !residual || !weight || !residual_out || !norm_out)
+        return AR_ERR_NULL;
+    if (W < 2 || W > AR_MAX_WORLD)
+        return AR_ERR_WORLD;
+    if (!fused_shape_ok(M, N) || max_spins > AR_MAX_SPINS)
+        return AR_ERR_ARG;
+    if (!(eps >= 0.0f) || eps > 3.0e38f)
+        return AR_ERR_ARG;
+    if (!aligned(comm, 16) || !aligned(residual, 16) || !aligned(weight, 16) ||
+        !aligned(residual_out, 16) || !aligned(norm_out, 16) ||
+        (bad_chunks && !aligned(bad_chunks, 4)))
+        return AR_ERR_ALIGN;
+    const int64_t mat = 2 * M * N, vec = 2 * N, cb = ar_lamport_comm_bytes(W, M, N);
+    if (overlaps_partially(residual_out, residual, mat) ||
+        overlaps(residual_out, mat, weight, vec) || overlaps(residual_out, mat, comm, cb) ||
+        overlaps(norm_out, mat, residual, mat) || overlaps(norm_out, mat, weight, vec) ||
+        overlaps(norm_out, mat, residual_out, mat) || overlaps(norm_out, mat, comm, cb) ||
+        overlaps(residual, mat, comm, cb) || overlaps(weight, vec, comm, cb))
+        return AR_ERR_ARG;
+    if (bad_chunks && (overlaps(bad_chunks, 4, comm, cb) || overlaps(bad_chunks, 4, norm_out, mat) ||
+                       overlaps(bad_chunks, 4, residual_out, mat)))
+        return AR_ERR_ARG;
+    if (M == 0)
+        return AR_OK;
+    return from_hip(ar::launch_lamport_fused(comm, W, residual, weight, residual_out, norm_out,
+                                             M, N, eps, flag, max_spins, bad_chunks, nullptr, 0,
+                                             nullptr, static_cast<hipStream_t>(stream)));
+}
+
+LIBAR_EXPORT ar_status_t ar_lamport_oneshot_residual_rmsnorm(
+    const void *x, int rank, void *const *comms, int W, const void *residual,
+    const void *weight, void *residual_out, void *norm_out, int64_t M, int64_t N, float eps,
+    uint32_t flag, uint32_t max_spins, uint32_t *bad_chunks, ar_stream_t stream)
+{
+    if (!x || !comms)
+        return AR_ERR_NULL;
+    if (W < 2 || W > AR_MAX_WORLD)
+        return AR_ERR_WORLD;
+    for (int p = 0; p < W; ++p)
+        if (!comms[p])
+            return AR_ERR_NULL;
+    if (rank < 0 || rank >= W)
+        return AR_ERR_ARG;
+    // the reader's checks, on this rank's own buffer
+    if (!residual || !weight || !residual_out || !norm_out)
+        return AR_ERR_NULL;
+    if (!fused_shape_ok(M, N) || max_spins > AR_MAX_SPINS || !(eps >= 0.0f) || eps > 3.0e38f)
+        return AR_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(weight, 16) ||
+        !aligned(residual_out, 16) || !aligned(norm_out, 16) ||
+        (bad_chunks && !aligned(bad_chunks, 4)))
+        return AR_ERR_ALIGN;
+    for (int p = 0; p < W; ++p)
+        if (!aligned(comms[p], 16))
+            return AR_ERR_ALIGN;
+    const int64_t mat = 2 * M * N, vec = 2 * N, cb = ar_lamport_comm_bytes(W, M, N);
+    if (overlaps_partially(residual_out, residual, mat) ||
+        overlaps(residual_out, mat, weight, vec) || overlaps(norm_out, mat, residual, mat) ||
+        overlaps(norm_out, mat, weight, vec) || overlaps(norm_out, mat, residual_out, mat) ||
+        overlaps(x, mat, residual_out, mat) || overlaps(x, mat, norm_out, mat))
+        return AR_ERR_ARG;
+    for (int p = 0; p < W; ++p) {
+        const void *c = comms[p];
+        if (overlaps(c, cb, x, mat) || overlaps(c, cb, residual, mat) ||
+            overlaps(c, cb, weight, vec) || overlaps(c, cb, residual_out, mat) ||
+            overlaps(c, cb, norm_out, mat) || (bad_chunks && overlaps(c, cb, bad_chunks, 4)))
+            return AR_ERR_ARG;
+        for (int q = 0; q < p; ++q)
+            if (overlaps(c, cb, comms[q], cb))
+                return AR_ERR_ARG;
+    }
+    if (bad_chunks && (overlaps(bad_chunks, 4, norm_out, mat) ||
+                       overlaps(bad_chunks, 4, residual_out, mat)))
+        return AR_ERR_ARG;
+    if (M == 0)
+        return AR_OK;
+    return from_hip(ar::launch_lamport_fused(comms[rank], W, residual, weight, residual_out,
+                                             norm_out, M, N, eps, flag, max_spins, bad_chunks,
+                                             x, rank, comms, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
 // wire formats
 // ---------------------------------------------------------------------------
 LIBAR_EXPORT int64_t ll_lines(int64_t n) { return n > 0 ? (4 * n + 7) / 8 : 0; }

@@ -71,12 +71,6 @@ __global__ __launch_bounds__(kWireThreads) void ll_pack_kernel(
     st_stream(fifo + sp.line, u32x4{lo, flag, hi, flag});
 }
 
-// Re-read one 16-byte chunk past the caches (a real load on every spin).
-__device__ __forceinline__ u32x4 reload16(const u32x4 *p)
-{
-    return *reinterpret_cast<const volatile u32x4 *>(p);
-}
-
 template <int W>
 __global__ __launch_bounds__(kWireThreads) void ll_unpack_reduce_kernel(
     InTable<W> fifos, float *out, int64_t n, uint32_t lines, uint32_t step_lines,

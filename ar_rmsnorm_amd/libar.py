@@ -31,7 +31,9 @@ AR_MAX_WORLD, AR_FUSED_MAX_N, AR_MAX_SPINS, AR_FIFO_STEPS = 8, 16384, 65536, 8
 
 EXPORTS = (
     "ar_status_str", "ar_last_hip_error", "ar_reduce_1stage", "ar_reduce_2stage",
-    "ar_fused_residual_rmsnorm", "ll_pack", "ll_unpack_reduce", "ll128_pack",
+    "ar_fused_residual_rmsnorm", "ar_lamport_comm_bytes", "ar_lamport_fill",
+    "ar_lamport_push", "ar_lamport_fused_residual_rmsnorm",
+    "ar_lamport_oneshot_residual_rmsnorm", "ll_pack", "ll_unpack_reduce", "ll128_pack",
     "ll128_unpack_reduce", "ll_lines", "ll128_lines", "ll_fifo_bytes",
     "ll128_fifo_bytes", "ll_default_step_lines", "ll128_default_step_lines",
 )
@@ -48,11 +50,22 @@ _lib.ar_reduce_1stage.argtypes = [_pp, _int, _vp, _i64, _vp]
 _lib.ar_reduce_2stage.argtypes = [_pp, _pp, _int, _int, _vp, _i64, ctypes.c_uint, _vp]
 _lib.ar_fused_residual_rmsnorm.argtypes = [_pp, _int, _vp, _vp, _vp, _vp, _i64, _i64,
                                            ctypes.c_float, _vp]
+_lib.ar_lamport_comm_bytes.argtypes = [_int, _i64, _i64]
+_lib.ar_lamport_comm_bytes.restype = _i64
+_lib.ar_lamport_fill.argtypes = [_vp, _int, _i64, _i64, _vp]
+_lib.ar_lamport_push.argtypes = [_vp, _int, _int, _pp, _i64, _i64, _u32, _vp]
+_lib.ar_lamport_fused_residual_rmsnorm.argtypes = [_vp, _int, _vp, _vp, _vp, _vp, _i64, _i64,
+                                                   ctypes.c_float, _u32, _u32, _vp, _vp]
+_lib.ar_lamport_oneshot_residual_rmsnorm.argtypes = [_vp, _int, _pp, _int, _vp, _vp, _vp, _vp,
+                                                     _i64, _i64, ctypes.c_float, _u32, _u32,
+                                                     _vp, _vp]
 for _n in ("ll_pack", "ll128_pack"):
     getattr(_lib, _n).argtypes = [_vp, _i64, _vp, _i64, _u64, _vp]
 for _n in ("ll_unpack_reduce", "ll128_unpack_reduce"):
     getattr(_lib, _n).argtypes = [_pp, _int, _vp, _i64, _i64, _u64, _u32, _vp, _vp]
-for _n in ("ar_reduce_1stage", "ar_reduce_2stage", "ar_fused_residual_rmsnorm", "ll_pack",
+for _n in ("ar_reduce_1stage", "ar_reduce_2stage", "ar_fused_residual_rmsnorm",
+           "ar_lamport_fill", "ar_lamport_push", "ar_lamport_fused_residual_rmsnorm",
+           "ar_lamport_oneshot_residual_rmsnorm", "ll_pack",
            "ll128_pack", "ll_unpack_reduce", "ll128_unpack_reduce"):
     getattr(_lib, _n).restype = _int
 for _n in ("ll_lines", "ll128_lines", "ll_fifo_bytes", "ll128_fifo_bytes"):
@@ -130,6 +143,54 @@ def ar_fused_residual_rmsnorm(inputs: Sequence, residual, weight, residual_out, 
                                           _addr(norm_out), M, N, float(eps),
                                           _stream(stream)),
            "ar_fused_residual_rmsnorm")
+
+
+def ar_lamport_comm_bytes(W: int, M: int, N: int) -> int:
+    return _lib.ar_lamport_comm_bytes(W, M, N)
+
+
+def ar_lamport_fill(comm, W: int, M: int, N: int, stream=None) -> None:
+    """Fill a comm buffer with the sentinel (all three regions)."""
+    _check(_lib.ar_lamport_fill(_addr(comm), W, M, N, _stream(stream)), "ar_lamport_fill")
+
+
+def ar_lamport_push(x, rank: int, comms: Sequence, flag: int, M: Optional[int] = None,
+                    N: Optional[int] = None, stream=None) -> None:
+    """Push bf16 [M, N] rows of `rank` into slot `rank` of region flag % 3 of
+    the W comm buffers (W = len(comms))."""
+    if M is None or N is None:
+        M, N = x.shape
+    _check(_lib.ar_lamport_push(_addr(x), len(comms), rank, _table(comms), M, N,
+                                flag & 0xFFFFFFFF, _stream(stream)), "ar_lamport_push")
+
+
+def ar_lamport_fused_residual_rmsnorm(comm, W: int, residual, weight, residual_out,
+                                      norm_out, eps: float, flag: int, max_spins: int = 0,
+                                      bad_chunks=None, M: Optional[int] = None,
+                                      N: Optional[int] = None, stream=None) -> None:
+    """Reduce the W slots of region flag % 3 of `comm`, add the residual,
+    normalise; then reset region (flag + 2) % 3 to the sentinel."""
+    if M is None or N is None:
+        M, N = residual.shape
+    _check(_lib.ar_lamport_fused_residual_rmsnorm(
+        _addr(comm), W, _addr(residual), _addr(weight), _addr(residual_out), _addr(norm_out),
+        M, N, float(eps), flag & 0xFFFFFFFF, max_spins, _addr(bad_chunks), _stream(stream)),
+        "ar_lamport_fused_residual_rmsnorm")
+
+
+def ar_lamport_oneshot_residual_rmsnorm(x, rank: int, comms: Sequence, residual, weight,
+                                        residual_out, norm_out, eps: float, flag: int,
+                                        max_spins: int = 0, bad_chunks=None,
+                                        M: Optional[int] = None, N: Optional[int] = None,
+                                        stream=None) -> None:
+    """One launch: push x as `rank` into the W comm buffers, then reduce
+    comms[rank], add the residual and normalise (W = len(comms))."""
+    if M is None or N is None:
+        M, N = residual.shape
+    _check(_lib.ar_lamport_oneshot_residual_rmsnorm(
+        _addr(x), rank, _table(comms), len(comms), _addr(residual), _addr(weight),
+        _addr(residual_out), _addr(norm_out), M, N, float(eps), flag & 0xFFFFFFFF, max_spins,
+        _addr(bad_chunks), _stream(stream)), "ar_lamport_oneshot_residual_rmsnorm")
 
 
 def ll_pack(src, fifo, step_lines: int, first_step: int = 0, n: Optional[int] = None,

@@ -268,6 +268,51 @@ def main():
                                    orc.fused_residual_rmsnorm(fx, fr, fw, fc["eps"])))
         result["fused_m1_us_per_call"] = rows["fused_W4_M1_N2048"]["us_per_call"]
 
+        # Lamport data-as-flag form of the same operator: rank 0's push into
+        # the W comm buffers, rank 0's reader (the peers' pushes staged once),
+        # and the whole per-rank call (push then read).  A repeated call with
+        # one flag is idempotent: it rewrites and rereads one region and
+        # resets another.
+        for M in fc["Ms"]:
+            fx, fr, fw = synth.fused(M)
+            Wf, N = fc["W"], fc["N"]
+            d = [to_dev(x) for x in fx]
+            dr, dw = to_dev(fr), to_dev(fw)
+            ro, no = torch.empty_like(dr), torch.empty_like(dr)
+            comms = [torch.empty(ar.ar_lamport_comm_bytes(Wf, M, N) // 4, dtype=torch.int32,
+                                 device=dev) for _ in range(Wf)]
+            for c in comms:
+                ar.ar_lamport_fill(c, Wf, M, N)
+            for r in range(Wf):
+                ar.ar_lamport_push(d[r], r, comms, 1)
+            mat = M * N * 2
+            push = (lambda d=d, comms=comms: ar.ar_lamport_push(d[0], 0, comms, 1))
+            read = (lambda comms=comms, dr=dr, dw=dw, ro=ro, no=no:
+                    ar.ar_lamport_fused_residual_rmsnorm(comms[0], Wf, dr, dw, ro, no,
+                                                         fc["eps"], 1))
+            hc = None
+            if orc:
+                hc = [orc.lamport_comm(Wf, M, N) for _ in range(Wf)]
+                for r in range(Wf):
+                    orc.lamport_push(fx[r], r, hc, 1)
+            row(f"lamport_push_W4_M{M}_N2048", mat + Wf * mat, [push], steps=200,
+                oracle_fn=orc and (lambda fx=fx, hc=hc: orc.lamport_push(fx[0], 0, hc, 1)))
+            row(f"lamport_read_W4_M{M}_N2048", Wf * mat + 2 * mat + 2 * N + 2 * mat + Wf * mat,
+                [read], steps=200,
+                oracle_fn=orc and (lambda hc=hc, fr=fr, fw=fw:
+                                   orc.lamport_fused_residual_rmsnorm(hc[0], Wf, fr, fw,
+                                                                      fc["eps"], 1)))
+            # the whole per-rank call in one launch: push to the W buffers,
+            # poll the W - 1 peer slots, reduce, normalise, reset
+            oneshot = (lambda d=d, comms=comms, dr=dr, dw=dw, ro=ro, no=no:
+                       ar.ar_lamport_oneshot_residual_rmsnorm(d[0], 0, comms, dr, dw, ro, no,
+                                                              fc["eps"], 1))
+            row(f"lamport_oneshot_W4_M{M}_N2048",
+                mat + Wf * mat + (Wf - 1) * mat + mat + 2 * N + 2 * mat + Wf * mat,
+                [oneshot], steps=200)
+            del comms
+        result["lamport_m1_us_per_call"] = rows["lamport_oneshot_W4_M1_N2048"]["us_per_call"]
+
         # one-stage reduce: small, decode shape, and the cap message
         for name, maker in (("1stage_W2_n8192", synth.reduce_small),
                             ("1stage_W8_n8192", synth.reduce_decode)):

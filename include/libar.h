@@ -144,6 +144,92 @@ ar_status_t ar_fused_residual_rmsnorm(const void *const *inputs, int W,
                                       ar_stream_t stream);
 
 /*
+ * Lamport data-as-flag form of the fused one-shot ([TRIAR] "Option 2:
+ * Lamport").  Each rank owns a comm buffer of u32 words
+ * [3 regions][W slots][M][N / 2] (ar_lamport_comm_bytes), filled with the
+ * sentinel 0x80008000 (two bf16 -0.0) before first use (ar_lamport_fill).
+ * A call with counter `flag` (incremented by one per call on every rank)
+ * uses region flag mod 3:
+ *   push   rank r writes its bf16 [M, N] rows into slot r of that region of
+ *          every rank's buffer, as u32 words of two bf16 (element 2j in the
+ *          low half) with every -0.0 turned into +0.0, so no word can equal
+ *          the sentinel;
+ *   fused  rank p waits until no word of its region holds the sentinel (at
+ *          most max_spins re-reads per 16-byte chunk, never a hang), sums the
+ *          W slots in slot order 0..W-1 in fp32 and applies the residual add
+ *          and RMSNorm exactly as ar_fused_residual_rmsnorm; it then refills
+ *          region (flag + 2) mod 3, the previous call's region, with the
+ *          sentinel.  Every peer finished writing that region before the
+ *          previous call could complete, and writes it again only two calls
+ *          later, so three regions make the buffer reusable without a barrier.
+ * On one GPU the W comm buffers are ordinary device buffers and the pushes
+ * are separate launches ahead of the fused call.
+ */
+
+/* Bytes of one rank's comm buffer: 3 * W * M * N * 2 (0 for invalid sizes). */
+int64_t ar_lamport_comm_bytes(int W, int64_t M, int64_t N);
+
+/*
+ * Fill a comm buffer (all three regions) with the sentinel.
+ *   comm   ar_lamport_comm_bytes(W, M, N) bytes, 16-byte aligned
+ *   W, M, N as for ar_lamport_push
+ */
+ar_status_t ar_lamport_fill(void *comm, int W, int64_t M, int64_t N,
+                            ar_stream_t stream);
+
+/*
+ * Push this rank's rows into slot `rank` of region flag mod 3 of every comm
+ * buffer.
+ *   x      bf16 [M, N] row-major, 16-byte aligned; must not overlap a buffer
+ *   comms  host table of the W ranks' comm buffers (16-byte aligned)
+ *   W      2 <= W <= 8                                  else AR_ERR_WORLD
+ *   rank   0 <= rank < W; M >= 0; 8 <= N <= 16384, N multiple of 8
+ *                                                       else AR_ERR_ARG
+ */
+ar_status_t ar_lamport_push(const void *x, int W, int rank, void *const *comms,
+                            int64_t M, int64_t N, uint32_t flag,
+                            ar_stream_t stream);
+
+/*
+ * Read this rank's comm buffer (region flag mod 3), reduce, add the residual,
+ * normalise, and reset region (flag + 2) mod 3 to the sentinel.
+ *   comm          this rank's comm buffer (16-byte aligned)
+ *   residual, weight, residual_out, norm_out, M, N, eps
+ *                 as ar_fused_residual_rmsnorm; no output may overlap comm
+ *   max_spins     <= AR_MAX_SPINS                       else AR_ERR_ARG
+ *   bad_chunks    device u32 (4-byte aligned) the caller zeroes; the library
+ *                 adds the number of (slot, 16-byte chunk) units still holding
+ *                 a sentinel after max_spins re-reads (their outputs are
+ *                 unspecified).  NULL: not counted.
+ */
+ar_status_t ar_lamport_fused_residual_rmsnorm(void *comm, int W,
+                                              const void *residual,
+                                              const void *weight,
+                                              void *residual_out, void *norm_out,
+                                              int64_t M, int64_t N, float eps,
+                                              uint32_t flag, uint32_t max_spins,
+                                              uint32_t *bad_chunks,
+                                              ar_stream_t stream);
+
+/*
+ * The whole Lamport call of one rank in one launch, as the page's program
+ * does it: push x as rank `rank` into every buffer of `comms` (as
+ * ar_lamport_push), then read comms[rank] (as
+ * ar_lamport_fused_residual_rmsnorm).  The own slot is taken from registers;
+ * only the W - 1 peer slots are polled.  Arguments and errors are those of
+ * the two calls; x must not overlap an output or a comm buffer.
+ */
+ar_status_t ar_lamport_oneshot_residual_rmsnorm(const void *x, int rank,
+                                                void *const *comms, int W,
+                                                const void *residual,
+                                                const void *weight,
+                                                void *residual_out, void *norm_out,
+                                                int64_t M, int64_t N, float eps,
+                                                uint32_t flag, uint32_t max_spins,
+                                                uint32_t *bad_chunks,
+                                                ar_stream_t stream);
+
+/*
  * LL wire format ([NCCL14] "LL's 16-byte FIFO line", "How LL publishes and
  * waits for flags", "Prerequisite mental model").
  * A FIFO is a ring of 8 steps of step_lines 16-byte lines.  The payload
