@@ -73,6 +73,12 @@ def lib():
             getattr(L, name).restype = _i64
         for name in ("orc_ll_pack", "orc_ll128_pack"):
             getattr(L, name).argtypes = [_p, _i64, _p, _i64, _u64]
+        L.orc_row_shard_range.argtypes = [_i64, ctypes.c_int, ctypes.c_int,
+                                          ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
+        L.orc_fused_2stage_scatter.argtypes = [_p, ctypes.c_int, ctypes.c_int, _p, _p, _p, _p,
+                                               _i64, _i64, ctypes.c_double, ctypes.c_int]
+        L.orc_fused_2stage.argtypes = [_p, ctypes.c_int, _p, _p, _p, _p, _p, _i64, _i64,
+                                       ctypes.c_double, ctypes.c_int]
         L.orc_lamport_pack.argtypes = [ctypes.c_uint16, ctypes.c_uint16]
         L.orc_lamport_pack.restype = ctypes.c_uint32
         L.orc_lamport_push.argtypes = [_p, ctypes.c_int, ctypes.c_int, _p, _i64, _i64,
@@ -185,6 +191,43 @@ def fused_residual_rmsnorm(xs, residual, weight, eps: float):
                                      _ptr(res_out), _ptr(norm_out), _ptr(norm_exact),
                                      M, N, float(eps), _ptr(h))
     return res_out, norm_out, norm_exact
+
+
+def row_shard_range(M: int, W: int, s: int):
+    """Row range [first, last) owned by shard s of the two-shot fused form."""
+    a, b = _i64(), _i64()
+    lib().orc_row_shard_range(M, W, s, ctypes.byref(a), ctypes.byref(b))
+    return a.value, b.value
+
+
+def fused_2stage_scatter(xs, s: int, residual, weight, eps: float, rank_order: bool = False):
+    """Owner s's staged rows: (residual_out rows, norm_out rows, norm_exact)."""
+    residual = _u16(residual)
+    M, N = residual.shape
+    xs = [_u16(x).reshape(M, N) for x in xs]
+    weight = _u16(weight).reshape(N)
+    m0, m1 = row_shard_range(M, len(xs), s)
+    rows = m1 - m0
+    stage = np.empty(2 * rows * N + 1, np.uint16)
+    exact = np.empty(rows * N + 1, np.float64)
+    lib().orc_fused_2stage_scatter(_ptr_table(xs), len(xs), s, _ptr(residual), _ptr(weight),
+                                   _ptr(stage), _ptr(exact), M, N, float(eps), int(rank_order))
+    return (stage[:rows * N].reshape(rows, N), stage[rows * N:2 * rows * N].reshape(rows, N),
+            exact[:rows * N].reshape(rows, N))
+
+
+def fused_2stage(xs, residual, weight, eps: float, rank_order: bool = False):
+    """Two-shot fused result: (residual_out, norm_out, norm_exact)."""
+    residual = _u16(residual)
+    M, N = residual.shape
+    xs = [_u16(x).reshape(M, N) for x in xs]
+    weight = _u16(weight).reshape(N)
+    ro = np.empty((M, N), np.uint16)
+    no = np.empty((M, N), np.uint16)
+    ne = np.empty((M, N), np.float64)
+    lib().orc_fused_2stage(_ptr_table(xs), len(xs), _ptr(residual), _ptr(weight), _ptr(ro),
+                           _ptr(no), _ptr(ne), M, N, float(eps), int(rank_order))
+    return ro, no, ne
 
 
 # --------------------------------------------------------------------------

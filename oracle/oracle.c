@@ -514,3 +514,66 @@ int64_t orc_lamport_fused_residual_rmsnorm(uint32_t *comm, int W,
         comm[stale * W * words + q] = ORC_LAMPORT_SENTINEL;
     return bad;
 }
+
+/* ---------------------------------------------------------------------------
+ * Two-shot fused all-reduce + residual + RMSNorm: the two-stage structure of
+ * [SGLv1] "2stage: sharding, rotation, and why no exit barrier" applied to
+ * rows, so that each row's statistic stays with one owner ([TRIAR] "overall
+ * design" keeps a row whole).  Rows are cut into W shards: part = M / W,
+ * shard s = rows [s*part, (s+1)*part), the last shard also taking the
+ * remainder.  The owner of shard s applies the fused operator to its rows,
+ * summing in the rotated order s, s+1, ..., s-1 (rank_order != 0: 0..W-1),
+ * and stages residual_out and norm_out rows; the gather copies every shard's
+ * rows into place.
+ * ------------------------------------------------------------------------- */
+void orc_row_shard_range(int64_t M, int W, int s, int64_t *first, int64_t *last)
+{
+    int64_t part = M / W;
+    *first = (int64_t)s * part;
+    *last = (s == W - 1) ? M : *first + part;
+}
+
+/* Owner s's reduce-scatter: stage[0 .. rows*N) = residual_out rows,
+ * stage[rows*N .. 2*rows*N) = norm_out rows, norm_exact (optional) likewise
+ * for its rows only. */
+void orc_fused_2stage_scatter(const uint16_t *const *x, int W, int s,
+                              const uint16_t *residual, const uint16_t *weight,
+                              uint16_t *stage, double *norm_exact, int64_t M,
+                              int64_t N, double eps, int rank_order)
+{
+    int64_t m0, m1;
+    orc_row_shard_range(M, W, s, &m0, &m1);
+    const int64_t rows = m1 - m0;
+    if (rows == 0)
+        return;
+    const uint16_t *xs[8];
+    for (int i = 0; i < W; ++i)
+        xs[i] = x[rank_order ? i : (s + i) % W] + m0 * N;
+    float *h = (float *)malloc((size_t)N * sizeof(float));
+    orc_fused_residual_rmsnorm(xs, W, residual + m0 * N, weight, stage, stage + rows * N,
+                               norm_exact, rows, N, eps, h);
+    free(h);
+}
+
+/* The whole two-shot result (every shard staged by its owner, then
+ * gathered); the same for every rank. */
+void orc_fused_2stage(const uint16_t *const *x, int W, const uint16_t *residual,
+                      const uint16_t *weight, uint16_t *residual_out,
+                      uint16_t *norm_out, double *norm_exact, int64_t M, int64_t N,
+                      double eps, int rank_order)
+{
+    for (int s = 0; s < W; ++s) {
+        int64_t m0, m1;
+        orc_row_shard_range(M, W, s, &m0, &m1);
+        const int64_t rows = m1 - m0;
+        uint16_t *stage = (uint16_t *)malloc((size_t)(2 * rows * N + 1) * sizeof(uint16_t));
+        orc_fused_2stage_scatter(x, W, s, residual, weight, stage,
+                                 norm_exact ? norm_exact + m0 * N : NULL, M, N, eps,
+                                 rank_order);
+        for (int64_t q = 0; q < rows * N; ++q) {
+            residual_out[m0 * N + q] = stage[q];
+            norm_out[m0 * N + q] = stage[rows * N + q];
+        }
+        free(stage);
+    }
+}

@@ -629,3 +629,57 @@ def test_lamport_triple_buffer_invariant_over_calls():
         for p in range(W):
             ro, no, _, bad = orc.lamport_fused_residual_rmsnorm(comms[p], W, res, w, 1e-6, f)
             assert bad == 0 and np.array_equal(ro, want[0]) and np.array_equal(no, want[1])
+
+
+# ---------------------------------------------------------------------------
+# two-shot fused (rows sharded as [SGLv1]'s two-stage form, [TRIAR] operator)
+# ---------------------------------------------------------------------------
+def test_fused_2stage_row_partition():
+    assert orc.row_shard_range(128, 4, 0) == (0, 32)
+    assert orc.row_shard_range(128, 4, 3) == (96, 128)
+    assert orc.row_shard_range(4 * 10 + 3, 4, 2) == (20, 30)
+    assert orc.row_shard_range(4 * 10 + 3, 4, 3) == (30, 43)
+    assert orc.row_shard_range(3, 8, 0) == (0, 0)
+    assert orc.row_shard_range(3, 8, 7) == (0, 3)
+
+
+@pytest.mark.parametrize("W,M", [(2, 7), (2, 128), (4, 16), (8, 11), (3, 2)])
+def test_fused_2stage_equals_one_shot_when_order_agrees(W, M):
+    """W=2: the rotated order is x0+x1 or x1+x0, equal by commutativity; with
+    the rank-order flag every W gives the one-shot fused result exactly."""
+    N = 512
+    xs, res, w = synth.fused_inputs(W, M, N, [97, W, M])
+    one = orc.fused_residual_rmsnorm(xs, res, w, 1e-6)
+    two = orc.fused_2stage(xs, res, w, 1e-6, rank_order=True)
+    for a, b in zip(one, two):
+        assert np.array_equal(a, b)
+    if W == 2:
+        rot = orc.fused_2stage(xs, res, w, 1e-6)
+        for a, b in zip(one, rot):
+            assert np.array_equal(a, b)
+
+
+def test_fused_2stage_rotation_hand_case():
+    """x = (1, 2^24, 1, -2^24) at every position, W=4, M=4 (one row per
+    shard), residual 0, weight 1: the owners' sums are 0, 1, 2, 2 (as in the
+    two-stage reduce), and the normalised rows are 0, 1, 1, 1."""
+    M, N = 4, 64
+    vals = [0x3F80, 0x4B80, 0x3F80, 0xCB80]
+    xs = [np.full((M, N), v, np.uint16) for v in vals]
+    res = np.zeros((M, N), np.uint16)
+    w = np.full(N, 0x3F80, np.uint16)
+    ro, no, _ = orc.fused_2stage(xs, res, w, 1e-6)
+    assert list(orc.bf16_to_f32(ro[:, 0])) == [0.0, 1.0, 2.0, 2.0]
+    assert list(orc.bf16_to_f32(no[:, 0])) == [0.0, 1.0, 1.0, 1.0]
+    assert np.all(ro == ro[:, :1]) and np.all(no == no[:, :1])
+
+
+def test_fused_2stage_staged_shards_are_the_gathered_rows():
+    W, M, N = 4, 4 * 5 + 3, 256
+    xs, res, w = synth.fused_inputs(W, M, N, [98])
+    ro, no, ne = orc.fused_2stage(xs, res, w, 1e-6)
+    for s in range(W):
+        m0, m1 = orc.row_shard_range(M, W, s)
+        sro, sno, sne = orc.fused_2stage_scatter(xs, s, res, w, 1e-6)
+        assert np.array_equal(sro, ro[m0:m1]) and np.array_equal(sno, no[m0:m1])
+        assert np.array_equal(sne, ne[m0:m1])
