@@ -1,6 +1,7 @@
 """Build libar.so (HIP, gfx950) in-tree with hipcc."""
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
 import subprocess
@@ -20,18 +21,33 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into ar_rmsnorm_amd/lib/libar.so (always)."""
-    os.makedirs(os.path.dirname(LIB), exist_ok=True)
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-o", tmp, *SOURCES]
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err)
+        raise RuntimeError(f"hipcc failed ({r.returncode}): {' '.join(cmd)}\n{err}")
+    return err
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source (one hipcc per file, in parallel) and link
+    ar_rmsnorm_amd/lib/libar.so.  Always recompiles."""
+    os.makedirs(os.path.dirname(LIB), exist_ok=True)
+    objdir = os.path.join(os.path.dirname(LIB), "obj")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    objs = [os.path.join(objdir, os.path.basename(src) + ".o") for src in SOURCES]
+    jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
+        errs = list(pool.map(lambda so: _run([HIPCC, *compile_flags, "-c", so[0], "-o", so[1]]),
+                             zip(SOURCES, objs)))
+    tmp = LIB + ".tmp"
+    errs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]))
+    if verbose:
+        for e in errs:
+            if e.strip():
+                print(e)
     os.replace(tmp, LIB)
     return LIB
 

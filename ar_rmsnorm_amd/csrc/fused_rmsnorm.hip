@@ -43,6 +43,71 @@ __device__ __forceinline__ bool has_sentinel(u32x4 v)
            v.z == kLamportSentinel || v.w == kLamportSentinel;
 }
 
+// One row's arithmetic, shared by the one-shot and two-shot kernels.
+// a = sum over the W inputs in table order starting from the first one's
+// value, then h = a + residual, all in fp32 ([TRIAR] "what this operator
+// computes"; the all-reduce part is [SGLv1]'s one-stage sum).  Returns the
+// lane's sum of h^2; lanes past the row's end hold no packs and return 0.
+template <int W, int NT, int PPL>
+__device__ __forceinline__ float sum_residual(const u32x4 (&xv)[PPL][W], const u32x4 (&rv)[PPL],
+                                              int t, int packs_per_row, float (&h)[PPL][8])
+{
+    float ss = 0.0f;
+#pragma unroll
+    for (int p = 0; p < PPL; ++p) {
+        const int idx = t + p * NT;
+        if (idx < packs_per_row) {
+            float acc[8], tmp[8];
+            widen8(xv[p][0], acc);
+#pragma unroll
+            for (int r = 1; r < W; ++r) {
+                widen8(xv[p][r], tmp);
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    acc[k] = acc[k] + tmp[k];
+            }
+            widen8(rv[p], tmp);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                h[p][k] = acc[k] + tmp[k];
+                ss += h[p][k] * h[p][k];
+            }
+        }
+    }
+    return ss;
+}
+
+// Sum of the lanes' partials over the workgroup: DPP within each wavefront,
+// then the wavefront sums through LDS.  Every lane gets the result.
+template <int NT>
+__device__ __forceinline__ float row_sum(float ss)
+{
+    constexpr int kWaves = NT / 64;
+    ss = wave_sum(ss);
+    if (kWaves > 1) {
+        __shared__ float part[kWaves];
+        if ((threadIdx.x & 63) == 0)
+            part[threadIdx.x >> 6] = ss;
+        __syncthreads();
+        ss = part[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+            ss += part[w];
+    }
+    return ss;
+}
+
+// (h * rms) * weight, rounded once to bf16.
+__device__ __forceinline__ u32x4 normalize8(const float (&h)[8], float rms, u32x4 w)
+{
+    float wf[8], y[8];
+    widen8(w, wf);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        y[k] = (h[k] * rms) * wf[k];
+    return narrow8(y);
+}
+
 // NT lanes per row, each lane owning PPL packs: packs t, t + NT, ... so a
 // wavefront's loads of one pack index are 1 KiB contiguous.
 template <int W, int NT, int PPL, bool LAMPORT, bool PUSH>
@@ -51,7 +116,6 @@ __global__ __launch_bounds__(NT) void fused_rmsnorm_kernel(
     u32x4 *residual_out, u32x4 *norm_out, int packs_per_row, float n_cols,
     float eps, LamportArgs<W> la)
 {
-    constexpr int kWaves = NT / 64;
     const int t = threadIdx.x;
     const int64_t row0 = (int64_t)blockIdx.x * packs_per_row;
 
@@ -97,58 +161,21 @@ __global__ __launch_bounds__(NT) void fused_rmsnorm_kernel(
             atomicAdd(la.bad, bad);
     }
 
-    // a = sum over ranks in order 0..W-1 starting from rank 0's value, then
-    // h = a + residual, all in fp32 ([TRIAR] "what this operator computes";
-    // the all-reduce part is [SGLv1]'s one-stage sum).
     float h[PPL][8];
-    float ss = 0.0f;
+    const float ss = sum_residual<W, NT, PPL>(xv, rv, t, packs_per_row, h);
 #pragma unroll
     for (int p = 0; p < PPL; ++p) {
         const int idx = t + p * NT;
-        if (idx < packs_per_row) {
-            float acc[8], tmp[8];
-            widen8(xv[p][0], acc);
-#pragma unroll
-            for (int r = 1; r < W; ++r) {
-                widen8(xv[p][r], tmp);
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    acc[k] = acc[k] + tmp[k];
-            }
-            widen8(rv[p], tmp);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                h[p][k] = acc[k] + tmp[k];
-                ss += h[p][k] * h[p][k];
-            }
+        if (idx < packs_per_row)
             residual_out[row0 + idx] = narrow8(h[p]);
-        }
     }
-
-    // Row sum of h^2: wavefront via DPP, then the kWaves partials via LDS.
-    ss = wave_sum(ss);
-    if (kWaves > 1) {
-        __shared__ float part[kWaves];
-        if ((t & 63) == 0)
-            part[t >> 6] = ss;
-        __syncthreads();
-        ss = part[0];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w)
-            ss += part[w];
-    }
-    const float rms = rsqrtf(ss / n_cols + eps);
+    const float rms = rsqrtf(row_sum<NT>(ss) / n_cols + eps);
 
 #pragma unroll
     for (int p = 0; p < PPL; ++p) {
         const int idx = t + p * NT;
         if (idx < packs_per_row) {
-            float wf[8], y[8];
-            widen8(wv[p], wf);
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                y[k] = (h[p][k] * rms) * wf[k];
-            norm_out[row0 + idx] = narrow8(y);
+            norm_out[row0 + idx] = normalize8(h[p], rms, wv[p]);
             if (LAMPORT) {
                 const u32x4 sent = {kLamportSentinel, kLamportSentinel, kLamportSentinel,
                                     kLamportSentinel};
@@ -277,6 +304,177 @@ hipError_t launch_lamport_fused(void *comm, int W, const void *residual,
     AR_LAMPORT_CASE(7)
     AR_LAMPORT_CASE(8)
 #undef AR_LAMPORT_CASE
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// Two-shot fused form, as run by one rank: [SGLv1]'s two-stage structure on
+// rows.  part = M / W rows per shard, the last shard also taking the
+// remainder; tmps[s] stages shard s as residual_out rows followed by norm_out
+// rows ([2][part + rem][N] bf16).  One-dimensional grid:
+//   blocks [0, rs_rows) (RS): one row of this rank's shard each, inputs in
+//       `in` order (the owner's rotation); both outputs go to tmps[rank] and,
+//       with AG, straight to residual_out / norm_out (each workgroup gathers
+//       the rows it computed, so no barrier is needed inside the launch);
+//   the remaining blocks (AG): part + rem per shard, copying row j of shard
+//       g = (rank + i) mod W from tmps[g], for i = 1..W-1 after an RS, or
+//       i = 0..W-1 for a gather alone.
+template <int W, int NT, int PPL, bool RS, bool AG>
+__global__ __launch_bounds__(NT) void fused_2stage_kernel(
+    InTable<W> in, const u32x4 *residual, const u32x4 *weight, u32x4 *residual_out,
+    u32x4 *norm_out, OutTable<W> tmps, int rank, int64_t part, int64_t rem,
+    int packs_per_row, float n_cols, float eps, uint32_t rs_rows)
+{
+    const uint32_t b = blockIdx.x;
+    const int t = threadIdx.x;
+    const int64_t cap = part + rem;
+    const int64_t packs = packs_per_row;
+    if (RS && b < rs_rows) {
+        const int64_t row0 = ((int64_t)rank * part + b) * packs;
+        u32x4 *stage_res = tmps.p[rank] + (int64_t)b * packs;
+        u32x4 *stage_norm = tmps.p[rank] + (cap + b) * packs;
+        u32x4 xv[PPL][W], rv[PPL], wv[PPL];
+#pragma unroll
+        for (int p = 0; p < PPL; ++p) {
+            const int idx = t + p * NT;
+            if (idx < packs_per_row) {
+#pragma unroll
+                for (int r = 0; r < W; ++r)
+                    xv[p][r] = in.p[r][row0 + idx];
+                rv[p] = residual[row0 + idx];
+                wv[p] = weight[idx];
+            }
+        }
+        float h[PPL][8];
+        const float ss = sum_residual<W, NT, PPL>(xv, rv, t, packs_per_row, h);
+#pragma unroll
+        for (int p = 0; p < PPL; ++p) {
+            const int idx = t + p * NT;
+            if (idx < packs_per_row) {
+                const u32x4 ro = narrow8(h[p]);
+                st_stream(stage_res + idx, ro);
+                if (AG)
+                    st_stream(residual_out + row0 + idx, ro);
+            }
+        }
+        const float rms = rsqrtf(row_sum<NT>(ss) / n_cols + eps);
+#pragma unroll
+        for (int p = 0; p < PPL; ++p) {
+            const int idx = t + p * NT;
+            if (idx < packs_per_row) {
+                const u32x4 no = normalize8(h[p], rms, wv[p]);
+                st_stream(stage_norm + idx, no);
+                if (AG)
+                    st_stream(norm_out + row0 + idx, no);
+            }
+        }
+        return;
+    }
+    if (!AG)
+        return;
+    const uint32_t k = RS ? b - rs_rows : b;
+    const int i = (RS ? 1 : 0) + (int)(k / cap);
+    const int64_t j = k % cap;
+    int g = rank + i;
+    if (g >= W)
+        g -= W;
+    const int64_t rows_g = part + (g == W - 1 ? rem : 0);
+    if (j >= rows_g)
+        return;
+    const int64_t row0 = ((int64_t)g * part + j) * packs;
+    const u32x4 *src_res = tmps.p[g] + j * packs;
+    const u32x4 *src_norm = tmps.p[g] + (cap + j) * packs;
+#pragma unroll
+    for (int p = 0; p < PPL; ++p) {
+        const int idx = t + p * NT;
+        if (idx < packs_per_row) {
+            st_stream(residual_out + row0 + idx, src_res[idx]);
+            st_stream(norm_out + row0 + idx, src_norm[idx]);
+        }
+    }
+}
+
+template <int W, int NT, int PPL, bool RS, bool AG>
+static hipError_t launch_2stage_shape(const InTable<W> &in, const OutTable<W> &tmps,
+                                      int rank, const void *residual, const void *weight,
+                                      void *residual_out, void *norm_out, int64_t M,
+                                      int64_t N, float eps, hipStream_t s)
+{
+    const int64_t part = M / W, rem = M % W, cap = part + rem;
+    const int64_t rs_rows = RS ? part + (rank == W - 1 ? rem : 0) : 0;
+    const int64_t blocks = rs_rows + (AG ? (RS ? W - 1 : W) * cap : 0);
+    if (blocks == 0)
+        return hipSuccess;
+    fused_2stage_kernel<W, NT, PPL, RS, AG><<<dim3((unsigned)blocks), dim3(NT), 0, s>>>(
+        in, static_cast<const u32x4 *>(residual), static_cast<const u32x4 *>(weight),
+        static_cast<u32x4 *>(residual_out), static_cast<u32x4 *>(norm_out), tmps, rank, part,
+        rem, (int)(N / 8), (float)N, eps, (uint32_t)rs_rows);
+    return hipGetLastError();
+}
+
+template <int W, bool RS, bool AG>
+static hipError_t launch_2stage_mode(const InTable<W> &in, const OutTable<W> &tmps, int rank,
+                                     const void *residual, const void *weight,
+                                     void *residual_out, void *norm_out, int64_t M, int64_t N,
+                                     float eps, hipStream_t s)
+{
+    const int64_t packs = N / 8;
+#define AR_2SHOT(NT, PPL)                                                                   \
+    return launch_2stage_shape<W, NT, PPL, RS, AG>(in, tmps, rank, residual, weight,        \
+                                                   residual_out, norm_out, M, N, eps, s)
+    if (packs <= 64)
+        AR_2SHOT(64, 1);
+    if (packs <= 256)
+        AR_2SHOT(256, 1);
+    if (packs <= 512)
+        AR_2SHOT(256, 2);
+    if (packs <= 1024)
+        AR_2SHOT(256, 4);
+    AR_2SHOT(512, 4);
+#undef AR_2SHOT
+}
+
+template <int W>
+static hipError_t launch_2stage_w(const void *const *inputs, const int *order,
+                                  void *const *tmps, int rank, const void *residual,
+                                  const void *weight, void *residual_out, void *norm_out,
+                                  int64_t M, int64_t N, float eps, bool rs, bool ag,
+                                  hipStream_t s)
+{
+    InTable<W> in;
+    OutTable<W> tp;
+    for (int r = 0; r < W; ++r) {
+        in.p[r] = static_cast<const u32x4 *>(inputs[order[r]]);
+        tp.p[r] = static_cast<u32x4 *>(tmps[r]);
+    }
+    if (rs && ag)
+        return launch_2stage_mode<W, true, true>(in, tp, rank, residual, weight, residual_out,
+                                                 norm_out, M, N, eps, s);
+    if (rs)
+        return launch_2stage_mode<W, true, false>(in, tp, rank, residual, weight, residual_out,
+                                                  norm_out, M, N, eps, s);
+    return launch_2stage_mode<W, false, true>(in, tp, rank, residual, weight, residual_out,
+                                              norm_out, M, N, eps, s);
+}
+
+hipError_t launch_fused_2stage(const void *const *inputs, const int *order,
+                               void *const *tmps, int W, int rank, const void *residual,
+                               const void *weight, void *residual_out, void *norm_out,
+                               int64_t M, int64_t N, float eps, bool rs, bool ag, hipStream_t s)
+{
+    switch (W) {
+#define AR_2SHOT_CASE(w)                                                                  \
+    case w:                                                                               \
+        return launch_2stage_w<w>(inputs, order, tmps, rank, residual, weight, residual_out, \
+                                  norm_out, M, N, eps, rs, ag, s);
+    AR_2SHOT_CASE(2)
+    AR_2SHOT_CASE(3)
+    AR_2SHOT_CASE(4)
+    AR_2SHOT_CASE(5)
+    AR_2SHOT_CASE(6)
+    AR_2SHOT_CASE(7)
+    AR_2SHOT_CASE(8)
+#undef AR_2SHOT_CASE
     default: return hipErrorInvalidValue;
     }
 }

@@ -21,6 +21,13 @@ hipError_t launch_fused_rmsnorm(const void *const *inputs, int W,
                                 void *residual_out, void *norm_out, int64_t M,
                                 int64_t N, float eps, hipStream_t s);
 
+// order[i] = index of the input summed i-th; tmps absolute per shard owner.
+hipError_t launch_fused_2stage(const void *const *inputs, const int *order,
+                               void *const *tmps, int W, int rank, const void *residual,
+                               const void *weight, void *residual_out, void *norm_out,
+                               int64_t M, int64_t N, float eps, bool rs, bool ag,
+                               hipStream_t s);
+
 hipError_t launch_lamport_fill(void *comm, int64_t chunks, hipStream_t s);
 hipError_t launch_lamport_push(const void *x, int W, int rank, void *const *comms,
                                int64_t M, int64_t N, uint32_t flag, hipStream_t s);

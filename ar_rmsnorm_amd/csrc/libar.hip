@@ -176,6 +176,64 @@ LIBAR_EXPORT ar_status_t ar_fused_residual_rmsnorm(const void *const *inputs, in
 }
 
 // ---------------------------------------------------------------------------
+LIBAR_EXPORT ar_status_t ar_fused_residual_rmsnorm_2stage(
+    const void *const *inputs, void *const *tmps, int W, int rank, const void *residual,
+    const void *weight, void *residual_out, void *norm_out, int64_t M, int64_t N, float eps,
+    unsigned flags, ar_stream_t stream)
+{
+    if (!inputs || !tmps || !residual || !weight)
+        return AR_ERR_NULL;
+    if (W < 2 || W > AR_MAX_WORLD)
+        return AR_ERR_WORLD;
+    if (flags & ~(AR_STAGE_RS | AR_STAGE_AG | AR_ORDER_RANK))
+        return AR_ERR_ARG;
+    if ((flags & (AR_STAGE_RS | AR_STAGE_AG)) == 0)
+        flags |= AR_STAGE_RS | AR_STAGE_AG;
+    const bool rs = flags & AR_STAGE_RS, ag = flags & AR_STAGE_AG;
+    for (int r = 0; r < W; ++r)
+        if (!inputs[r] || !tmps[r])
+            return AR_ERR_NULL;
+    if (ag && (!residual_out || !norm_out))
+        return AR_ERR_NULL;
+    if (rank < 0 || rank >= W || M < 0 || M > 0x7FFFFFFF || N < 8 || N > AR_FUSED_MAX_N ||
+        N % 8 != 0 || !(eps >= 0.0f) || eps > 3.0e38f)
+        return AR_ERR_ARG;
+    if (!aligned(residual, 16) || !aligned(weight, 16) ||
+        (ag && (!aligned(residual_out, 16) || !aligned(norm_out, 16))))
+        return AR_ERR_ALIGN;
+    for (int r = 0; r < W; ++r)
+        if (!aligned(inputs[r], 16) || !aligned(tmps[r], 16))
+            return AR_ERR_ALIGN;
+    const int64_t mat = 2 * M * N, vec = 2 * N;
+    const int64_t tmp_bytes = 2 * (M / W + M % W) * N * 2;
+    for (int r = 0; r < W; ++r) {
+        if (rs && (overlaps(tmps[rank], tmp_bytes, inputs[r], mat) ||
+                   (r != rank && overlaps(tmps[rank], tmp_bytes, tmps[r], tmp_bytes))))
+            return AR_ERR_ARG;
+        if (ag && (overlaps(residual_out, mat, inputs[r], mat) ||
+                   overlaps(residual_out, mat, tmps[r], tmp_bytes) ||
+                   overlaps(norm_out, mat, inputs[r], mat) ||
+                   overlaps(norm_out, mat, tmps[r], tmp_bytes)))
+            return AR_ERR_ARG;
+    }
+    if (rs && (overlaps(tmps[rank], tmp_bytes, residual, mat) ||
+               overlaps(tmps[rank], tmp_bytes, weight, vec)))
+        return AR_ERR_ARG;
+    if (ag && (overlaps_partially(residual_out, residual, mat) ||
+               overlaps(residual_out, mat, weight, vec) || overlaps(norm_out, mat, residual, mat) ||
+               overlaps(norm_out, mat, weight, vec) || overlaps(norm_out, mat, residual_out, mat)))
+        return AR_ERR_ARG;
+    if (M == 0)
+        return AR_OK;
+    int order[AR_MAX_WORLD];
+    for (int i = 0; i < W; ++i)
+        order[i] = (flags & AR_ORDER_RANK) ? i : (rank + i) % W;
+    return from_hip(ar::launch_fused_2stage(inputs, order, tmps, W, rank, residual, weight,
+                                            residual_out, norm_out, M, N, eps, rs, ag,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
 // Lamport data-as-flag fused one-shot
 // ---------------------------------------------------------------------------
 namespace {

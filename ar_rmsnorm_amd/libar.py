@@ -31,7 +31,7 @@ AR_MAX_WORLD, AR_FUSED_MAX_N, AR_MAX_SPINS, AR_FIFO_STEPS = 8, 16384, 65536, 8
 
 EXPORTS = (
     "ar_status_str", "ar_last_hip_error", "ar_reduce_1stage", "ar_reduce_2stage",
-    "ar_fused_residual_rmsnorm", "ar_lamport_comm_bytes", "ar_lamport_fill",
+    "ar_fused_residual_rmsnorm", "ar_fused_residual_rmsnorm_2stage", "ar_lamport_comm_bytes", "ar_lamport_fill",
     "ar_lamport_push", "ar_lamport_fused_residual_rmsnorm",
     "ar_lamport_oneshot_residual_rmsnorm", "ll_pack", "ll_unpack_reduce", "ll128_pack",
     "ll128_unpack_reduce", "ll_lines", "ll128_lines", "ll_fifo_bytes",
@@ -50,6 +50,9 @@ _lib.ar_reduce_1stage.argtypes = [_pp, _int, _vp, _i64, _vp]
 _lib.ar_reduce_2stage.argtypes = [_pp, _pp, _int, _int, _vp, _i64, ctypes.c_uint, _vp]
 _lib.ar_fused_residual_rmsnorm.argtypes = [_pp, _int, _vp, _vp, _vp, _vp, _i64, _i64,
                                            ctypes.c_float, _vp]
+_lib.ar_fused_residual_rmsnorm_2stage.argtypes = [_pp, _pp, _int, _int, _vp, _vp, _vp, _vp,
+                                                  _i64, _i64, ctypes.c_float, ctypes.c_uint,
+                                                  _vp]
 _lib.ar_lamport_comm_bytes.argtypes = [_int, _i64, _i64]
 _lib.ar_lamport_comm_bytes.restype = _i64
 _lib.ar_lamport_fill.argtypes = [_vp, _int, _i64, _i64, _vp]
@@ -64,6 +67,7 @@ for _n in ("ll_pack", "ll128_pack"):
 for _n in ("ll_unpack_reduce", "ll128_unpack_reduce"):
     getattr(_lib, _n).argtypes = [_pp, _int, _vp, _i64, _i64, _u64, _u32, _vp, _vp]
 for _n in ("ar_reduce_1stage", "ar_reduce_2stage", "ar_fused_residual_rmsnorm",
+           "ar_fused_residual_rmsnorm_2stage",
            "ar_lamport_fill", "ar_lamport_push", "ar_lamport_fused_residual_rmsnorm",
            "ar_lamport_oneshot_residual_rmsnorm", "ll_pack",
            "ll128_pack", "ll_unpack_reduce", "ll128_unpack_reduce"):
@@ -143,6 +147,20 @@ def ar_fused_residual_rmsnorm(inputs: Sequence, residual, weight, residual_out, 
                                           _addr(norm_out), M, N, float(eps),
                                           _stream(stream)),
            "ar_fused_residual_rmsnorm")
+
+
+def ar_fused_residual_rmsnorm_2stage(inputs: Sequence, tmps: Sequence, rank: int, residual,
+                                     weight, residual_out, norm_out, eps: float,
+                                     flags: int = 0, M: Optional[int] = None,
+                                     N: Optional[int] = None, stream=None) -> None:
+    """Two-shot fused form for one rank: the fused operator on this rank's
+    row shard (staged in tmps[rank]), then the gather of every shard."""
+    if M is None or N is None:
+        M, N = residual.shape
+    _check(_lib.ar_fused_residual_rmsnorm_2stage(
+        _table(inputs), _table(tmps), len(inputs), rank, _addr(residual), _addr(weight),
+        _addr(residual_out), _addr(norm_out), M, N, float(eps), flags, _stream(stream)),
+        "ar_fused_residual_rmsnorm_2stage")
 
 
 def ar_lamport_comm_bytes(W: int, M: int, N: int) -> int:

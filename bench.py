@@ -313,6 +313,53 @@ def main():
             del comms
         result["lamport_m1_us_per_call"] = rows["lamport_oneshot_W4_M1_N2048"]["us_per_call"]
 
+        # one-shot against two-shot fused, one rank's call, at the workload's
+        # M=128 and at a large M (2048 rows of 8192); cold buffer sets
+        for M, N in ((128, 2048), (2048, 8192)):
+            Wf = fc["W"]
+            if (M, N) == (128, 2048):
+                fx, fr, fw = synth.fused(M)
+            else:
+                fx, fr, fw = synth.fused_inputs(Wf, M, N, [1000 + fc["id"], M, N])
+            mat, rowb = M * N * 2, N * 2
+            part, rem = M // Wf, M % Wf
+            own = part                       # rank 0 owns rows [0, part)
+            one_bytes = (Wf + 3) * mat + 2 * N
+            two_bytes = (Wf * own * rowb + own * rowb + 2 * N + 4 * own * rowb
+                         + 4 * (M - own) * rowb)
+            base_x = [to_dev(x) for x in fx]
+            base_r, dw = to_dev(fr), to_dev(fw)
+            s1 = []
+            for k in range(sets_for(one_bytes)):
+                xx = base_x if k == 0 else [b.clone() for b in base_x]
+                rr = base_r if k == 0 else base_r.clone()
+                s1.append((xx, rr, torch.empty_like(rr), torch.empty_like(rr)))
+            if M != 128:
+                row(f"fused_W4_M{M}_N{N}", one_bytes,
+                    [lambda q=q: ar.ar_fused_residual_rmsnorm(q[0], q[1], dw, q[2], q[3],
+                                                              fc["eps"]) for q in s1],
+                    steps=8 * len(s1))
+            del s1
+            s2 = []
+            for k in range(sets_for(two_bytes)):
+                xx = base_x if k == 0 else [b.clone() for b in base_x]
+                rr = base_r if k == 0 else base_r.clone()
+                tmps = [torch.empty(2 * (part + rem) * N, dtype=torch.int16, device=dev)
+                        for _ in range(Wf)]
+                for r in range(1, Wf):
+                    ar.ar_fused_residual_rmsnorm_2stage(xx, tmps, r, rr, dw, None, None,
+                                                        fc["eps"], flags=ar.AR_STAGE_RS)
+                s2.append((xx, rr, tmps, torch.empty_like(rr), torch.empty_like(rr)))
+            row(f"fused2_W4_M{M}_N{N}_per_rank", two_bytes,
+                [lambda q=q: ar.ar_fused_residual_rmsnorm_2stage(q[0], q[2], 0, q[1], dw, q[3],
+                                                                 q[4], fc["eps"])
+                 for q in s2],
+                steps=8 * len(s2),
+                oracle_fn=orc and (lambda fx=fx, fr=fr, fw=fw:
+                                   orc.fused_2stage_scatter(fx, 0, fr, fw, fc["eps"])))
+            del s2, base_x
+            torch.cuda.empty_cache()
+
         # one-stage reduce: small, decode shape, and the cap message
         for name, maker in (("1stage_W2_n8192", synth.reduce_small),
                             ("1stage_W8_n8192", synth.reduce_decode)):

@@ -57,7 +57,7 @@ typedef int ar_status_t;
 #define AR_MAX_SPINS 65536u     /* bound on flag re-reads per line */
 #define AR_FIFO_STEPS 8         /* slots in a wire FIFO ring */
 
-/* Flags of ar_reduce_2stage. */
+/* Flags of ar_reduce_2stage and ar_fused_residual_rmsnorm_2stage. */
 #define AR_STAGE_RS 1u     /* run the reduce-scatter of this rank's shard */
 #define AR_STAGE_AG 2u     /* run the all-gather into out */
 #define AR_ORDER_RANK 4u   /* sum 0..W-1 instead of the owner's rotation */
@@ -142,6 +142,41 @@ ar_status_t ar_fused_residual_rmsnorm(const void *const *inputs, int W,
                                       void *residual_out, void *norm_out,
                                       int64_t M, int64_t N, float eps,
                                       ar_stream_t stream);
+
+/*
+ * Two-shot fused all-reduce + residual + RMSNorm, as run by one rank: the
+ * two-stage structure of [SGLv1] "2stage: sharding, rotation, and why no
+ * exit barrier" applied to rows, so that each row is normalised by one owner
+ * ([TRIAR] "overall design" keeps a row whole).  part = M / W rows per
+ * shard; shard s is rows [s*part, (s+1)*part), the last shard also taking the
+ * M mod W remainder.
+ *   RS: the rows of shard `rank` get the fused operator (as
+ *       ar_fused_residual_rmsnorm), the W inputs summed in the owner's
+ *       rotated order rank, rank+1, ..., rank-1 (AR_ORDER_RANK: 0..W-1, which
+ *       gives exactly the one-shot result); tmps[rank] receives the shard's
+ *       residual_out rows followed by its norm_out rows.
+ *   AG: residual_out and norm_out receive every shard's rows from tmps[s].
+ * On one GPU the peers' shards are whatever tmps[s != rank] hold: run the
+ * RS stage for every other rank first (flags = AR_STAGE_RS).  With both
+ * stages this rank's rows go from registers to both tmps[rank] and the
+ * outputs, so no barrier is needed inside the launch.
+ *   inputs, W, residual, weight, M, N, eps  as ar_fused_residual_rmsnorm
+ *   tmps     host table of W device pointers, each to at least
+ *            2 * (part + M mod W) * N bf16, 16-byte aligned
+ *   rank     0 <= rank < W                               else AR_ERR_ARG
+ *   residual_out, norm_out  bf16 [M, N] (may be NULL when AG is not run);
+ *            residual_out may equal residual; no other overlap with an
+ *            input, a tmp buffer or each other             else AR_ERR_ARG
+ *   flags    AR_STAGE_RS | AR_STAGE_AG | AR_ORDER_RANK; no stage bit means
+ *            both stages                                  else AR_ERR_ARG
+ */
+ar_status_t ar_fused_residual_rmsnorm_2stage(const void *const *inputs,
+                                             void *const *tmps, int W, int rank,
+                                             const void *residual,
+                                             const void *weight,
+                                             void *residual_out, void *norm_out,
+                                             int64_t M, int64_t N, float eps,
+                                             unsigned flags, ar_stream_t stream);
 
 /*
  * Lamport data-as-flag form of the fused one-shot ([TRIAR] "Option 2:
