@@ -79,6 +79,12 @@ def lib():
                                                _i64, _i64, ctypes.c_double, ctypes.c_int]
         L.orc_fused_2stage.argtypes = [_p, ctypes.c_int, _p, _p, _p, _p, _p, _i64, _i64,
                                        ctypes.c_double, ctypes.c_int]
+        L.orc_fifo_step_wire_bytes.argtypes = [ctypes.c_int, _i64]
+        L.orc_fifo_step_wire_bytes.restype = _i64
+        L.orc_fifo_total_steps.argtypes = [_i64, _i64]
+        L.orc_fifo_total_steps.restype = _i64
+        L.orc_fifo_stream.argtypes = [ctypes.c_int, _p, _p, _p, _i64, _p, ctypes.c_int, _i64,
+                                      _u64]
         L.orc_lamport_pack.argtypes = [ctypes.c_uint16, ctypes.c_uint16]
         L.orc_lamport_pack.restype = ctypes.c_uint32
         L.orc_lamport_push.argtypes = [_p, ctypes.c_int, ctypes.c_int, _p, _i64, _i64,
@@ -325,3 +331,34 @@ def lamport_fused_residual_rmsnorm(comm, W: int, residual, weight, eps: float, f
         _ptr(comm), W, _ptr(residual), _ptr(weight), _ptr(res_out), _ptr(norm_out),
         _ptr(norm_exact), M, N, float(eps), flag)
     return res_out, norm_out, norm_exact, int(bad)
+
+
+# --------------------------------------------------------------------------
+# streaming through an 8-step FIFO (LL = 0, LL128 = 1, Simple = 2)
+# --------------------------------------------------------------------------
+PROTO_LL, PROTO_LL128, PROTO_SIMPLE = 0, 1, 2
+
+
+def fifo_step_wire_bytes(proto: int, step_bytes: int) -> int:
+    return lib().orc_fifo_step_wire_bytes(proto, step_bytes)
+
+
+def fifo_total_steps(n: int, step_bytes: int) -> int:
+    return lib().orc_fifo_total_steps(n, step_bytes)
+
+
+def fifo_stream(proto: int, src, channels: int, step_bytes: int, first_step: int = 0,
+                local=None, fifo=None):
+    """Returns (out, fifo): the delivered payload and the rings' final bytes
+    (written over `fifo` if given, else over a zeroed buffer)."""
+    src = np.ascontiguousarray(src, dtype=np.float32)
+    n = src.size
+    wire = fifo_step_wire_bytes(proto, step_bytes)
+    if fifo is None:
+        fifo = np.zeros(channels * 8 * wire, np.uint8)
+    assert fifo.dtype == np.uint8 and fifo.size >= channels * 8 * wire
+    out = np.empty(n, np.float32)
+    loc = None if local is None else np.ascontiguousarray(local, dtype=np.float32)
+    lib().orc_fifo_stream(proto, _ptr(src), None if loc is None else _ptr(loc), _ptr(out), n,
+                          _ptr(fifo), channels, step_bytes, first_step)
+    return out, fifo

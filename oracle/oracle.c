@@ -577,3 +577,82 @@ void orc_fused_2stage(const uint16_t *const *x, int W, const uint16_t *residual,
         free(stage);
     }
 }
+
+/* ---------------------------------------------------------------------------
+ * Streaming through an 8-step FIFO ([NCCL14] "prerequisite mental model":
+ * a ring of NCCL_STEPS = 8 steps, the sender never overwriting a step the
+ * receiver has not consumed; "how LL publishes and waits for flags", "LL128's
+ * 128-byte line", "how Simple synchronizes").  The payload (4n bytes) is cut
+ * into steps of step_bytes payload bytes; the T steps are dealt to
+ * `channels` channels in contiguous runs (channel c takes steps
+ * [c*T/G, (c+1)*T/G)), each channel owning its own 8-slot ring.  Local step
+ * j of a channel is ring step k = first_step + j, stored in slot k mod 8 of
+ * that channel's ring:
+ *   LL     step_bytes/8 lines of 16 bytes (as orc_ll_pack, flag = k + 1)
+ *   LL128  step_bytes/120 lines of 128 bytes (as orc_ll128_pack)
+ *   Simple step_bytes raw payload bytes (readiness is a separate counter)
+ * A step writes only the lines (LL, LL128) or bytes (Simple) that carry
+ * payload, so the last step of a message may be partial; padding bytes of a
+ * partial line are zero.  The receiver delivers out[e] = src[e], or
+ * local[e] + src[e] (fp32) when a local buffer is given.  Every step is written into its slot in order, so
+ * the ring ends holding the last lap of each channel: that final state is
+ * what this function leaves in `fifo`.
+ * proto: 0 = LL, 1 = LL128, 2 = Simple.
+ * ------------------------------------------------------------------------- */
+int64_t orc_fifo_step_wire_bytes(int proto, int64_t step_bytes)
+{
+    if (proto == 0)
+        return step_bytes / 8 * 16;
+    if (proto == 1)
+        return step_bytes / 120 * 128;
+    return step_bytes;
+}
+
+int64_t orc_fifo_total_steps(int64_t n, int64_t step_bytes)
+{
+    return (4 * n + step_bytes - 1) / step_bytes;
+}
+
+void orc_fifo_stream(int proto, const uint8_t *src, const float *local, float *out,
+                     int64_t n, uint8_t *fifo, int channels, int64_t step_bytes,
+                     uint64_t first_step)
+{
+    const int64_t nbytes = 4 * n;
+    const int64_t T = orc_fifo_total_steps(n, step_bytes);
+    const int64_t wire = orc_fifo_step_wire_bytes(proto, step_bytes);
+    for (int c = 0; c < channels; ++c) {
+        const int64_t s0 = (int64_t)c * T / channels, s1 = (int64_t)(c + 1) * T / channels;
+        uint8_t *ring = fifo + (int64_t)c * 8 * wire;
+        for (int64_t g = s0; g < s1; ++g) {
+            const uint64_t k = first_step + (uint64_t)(g - s0);
+            uint8_t *slot = ring + (int64_t)(k % 8u) * wire;
+            const int64_t b0 = g * step_bytes;
+            const int64_t len = nbytes - b0 < step_bytes ? nbytes - b0 : step_bytes;
+            if (proto == 0) {
+                for (int64_t i = 0; i < (len + 7) / 8; ++i) {
+                    uint8_t d[8];
+                    for (int b = 0; b < 8; ++b)
+                        d[b] = payload_byte(src, nbytes, b0 + 8 * i + b);
+                    put_u32le(slot + 16 * i + 0, get_u32le(d));
+                    put_u32le(slot + 16 * i + 4, (uint32_t)(k + 1));
+                    put_u32le(slot + 16 * i + 8, get_u32le(d + 4));
+                    put_u32le(slot + 16 * i + 12, (uint32_t)(k + 1));
+                }
+            } else if (proto == 1) {
+                for (int64_t l = 0; l < (len + 119) / 120; ++l) {
+                    for (int b = 0; b < 120; ++b)
+                        slot[128 * l + b] = payload_byte(src, nbytes, b0 + 120 * l + b);
+                    put_u64le(slot + 128 * l + 120, k + 1);
+                }
+            } else {
+                for (int64_t b = 0; b < len; ++b)
+                    slot[b] = src[b0 + b];
+            }
+        }
+    }
+    for (int64_t e = 0; e < n; ++e) {
+        float v;
+        memcpy(&v, src + 4 * e, 4);
+        out[e] = local ? local[e] + v : v;
+    }
+}

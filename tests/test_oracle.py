@@ -683,3 +683,73 @@ def test_fused_2stage_staged_shards_are_the_gathered_rows():
         sro, sno, sne = orc.fused_2stage_scatter(xs, s, res, w, 1e-6)
         assert np.array_equal(sro, ro[m0:m1]) and np.array_equal(sno, no[m0:m1])
         assert np.array_equal(sne, ne[m0:m1])
+
+
+# ---------------------------------------------------------------------------
+# streaming through the 8-step FIFO ([NCCL14] "prerequisite mental model")
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("proto,step", [(orc.PROTO_LL, 256), (orc.PROTO_LL128, 240),
+                                        (orc.PROTO_SIMPLE, 256)])
+def test_fifo_stream_delivers_the_payload(proto, step):
+    g = np.random.default_rng(proto)
+    src = g.standard_normal(1000 + proto).astype(np.float32)
+    out, _ = orc.fifo_stream(proto, src, 3, step)
+    assert np.array_equal(out.view(np.uint32), src.view(np.uint32))
+    out, _ = orc.fifo_stream(proto, src, 3, step, local=src)
+    assert np.array_equal(out, 2 * src)                      # doubling is exact
+
+
+@pytest.mark.parametrize("first", [0, 5])
+def test_fifo_stream_within_one_lap_is_the_packers(first):
+    """One channel, at most 8 steps: the ring is exactly what the (pinned)
+    LL / LL128 packers produce with step_lines = step_bytes / 8 or / 120."""
+    g = np.random.default_rng(first)
+    src = g.standard_normal(7 * 60 + 11).astype(np.float32)      # 1724 payload bytes
+    _, ring = orc.fifo_stream(orc.PROTO_LL, src, 1, 256, first)
+    want = np.zeros(8 * 32 * 16, np.uint8)
+    orc.ll_pack(src, want, 32, first)
+    assert np.array_equal(ring, want)
+    _, ring = orc.fifo_stream(orc.PROTO_LL128, src, 1, 240, first)
+    want = np.zeros(8 * 2 * 128, np.uint8)
+    orc.ll128_pack(src, want, 2, first)
+    assert np.array_equal(ring, want)
+
+
+def test_fifo_stream_ring_keeps_the_last_lap():
+    """13 steps of 256 payload bytes through one ring (the last one partial):
+    the ring is the first lap (steps 0..7) overwritten by steps 8..12, each
+    slot holding the latest step with its index mod 8, and slot 4 keeping
+    step 4's lines past the end of the partial step 12."""
+    g = np.random.default_rng(3)
+    src = g.standard_normal(13 * 64 - 7).astype(np.float32)
+    _, ring = orc.fifo_stream(orc.PROTO_LL, src, 1, 256)
+    want = np.zeros(8 * 32 * 16, np.uint8)
+    orc.ll_pack(src[:8 * 64], want, 32, 0)
+    orc.ll_pack(src[8 * 64:], want, 32, 8)
+    assert np.array_equal(ring, want)
+    _, ring = orc.fifo_stream(orc.PROTO_SIMPLE, src, 1, 256)
+    raw = src.view(np.uint8)
+    for k in range(5, 13):
+        part = raw[k * 256:(k + 1) * 256]            # the last step is partial
+        assert np.array_equal(ring[(k % 8) * 256:(k % 8) * 256 + part.size], part)
+    # past the partial step 12, slot 4 still holds step 4's bytes
+    cut = raw.size - 12 * 256
+    assert np.array_equal(ring[4 * 256 + cut:5 * 256], raw[4 * 256 + cut:5 * 256])
+
+
+def test_fifo_stream_channel_split():
+    """T = 10 steps over 4 channels: channel c takes steps [c*10/4, (c+1)*10/4)
+    = [0,2), [2,5), [5,7), [7,10), each numbered from first_step in its ring."""
+    step = 256
+    src = np.arange(10 * 64, dtype=np.float32)
+    _, ring = orc.fifo_stream(orc.PROTO_SIMPLE, src, 4, step, first_step=3)
+    raw = src.view(np.uint8)
+    for c, (s0, s1) in enumerate([(0, 2), (2, 5), (5, 7), (7, 10)]):
+        base = c * 8 * step
+        for j, gstep in enumerate(range(s0, s1)):
+            slot = (3 + j) % 8
+            assert np.array_equal(ring[base + slot * step: base + (slot + 1) * step],
+                                  raw[gstep * step:(gstep + 1) * step]), (c, j)
+    assert orc.fifo_total_steps(10 * 64, step) == 10
+    assert orc.fifo_step_wire_bytes(orc.PROTO_LL, 32768) == 65536
+    assert orc.fifo_step_wire_bytes(orc.PROTO_LL128, 576000) == 614400
