@@ -39,6 +39,12 @@ hipError_t launch_lamport_fused(void *comm, int W, const void *residual,
                                 uint32_t max_spins, uint32_t *bad, const void *x_self,
                                 int rank, void *const *comms, hipStream_t s);
 
+// One cooperative launch of 2 * channels workgroups (producers, consumers).
+hipError_t launch_fifo_stream(int proto, const float *src, const float *local, float *out,
+                              int64_t n, void *fifo, uint64_t *counters, int channels,
+                              int64_t step_bytes, int64_t wire_bytes, uint64_t first_step,
+                              uint32_t max_spins, uint32_t *errors, hipStream_t s);
+
 hipError_t launch_ll_pack(const float *src, int64_t n, void *fifo,
                           int64_t step_lines, uint64_t first_step, hipStream_t s);
 hipError_t launch_ll_unpack_reduce(const void *const *fifos, int W, float *out,

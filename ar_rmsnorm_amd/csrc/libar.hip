@@ -504,3 +504,59 @@ LIBAR_EXPORT ar_status_t ll128_unpack_reduce(const void *const *fifos, int W, fl
                                                    first_step, max_spins, bad_lines,
                                                    static_cast<hipStream_t>(stream)));
 }
+
+// ---------------------------------------------------------------------------
+// streaming through 8-step FIFOs
+// ---------------------------------------------------------------------------
+LIBAR_EXPORT int64_t ar_fifo_step_wire_bytes(int proto, int64_t step_bytes)
+{
+    const int64_t unit = proto == AR_PROTO_LL ? 8 : proto == AR_PROTO_LL128 ? 120 : 16;
+    if (proto < AR_PROTO_LL || proto > AR_PROTO_SIMPLE || step_bytes < unit ||
+        step_bytes > ((int64_t)1 << 30) || step_bytes % unit != 0)
+        return 0;
+    if (proto == AR_PROTO_LL)
+        return step_bytes / 8 * 16;
+    if (proto == AR_PROTO_LL128)
+        return step_bytes / 120 * 128;
+    return step_bytes;
+}
+
+LIBAR_EXPORT int64_t ar_fifo_steps_per_channel(int64_t n, int64_t step_bytes, int channels)
+{
+    if (n <= 0 || step_bytes <= 0 || channels < 1)
+        return 0;
+    const int64_t total = (4 * n + step_bytes - 1) / step_bytes;
+    return (total + channels - 1) / channels;
+}
+
+LIBAR_EXPORT ar_status_t ar_fifo_stream(int proto, const float *src, const float *local,
+                                        float *out, int64_t n, void *fifo, uint64_t *counters,
+                                        int channels, int64_t step_bytes, uint64_t first_step,
+                                        uint32_t max_spins, uint32_t *errors,
+                                        ar_stream_t stream)
+{
+    if (!src || !out || !fifo || !counters || !errors)
+        return AR_ERR_NULL;
+    const int64_t wire = ar_fifo_step_wire_bytes(proto, step_bytes);
+    if (wire == 0 || n < 0 || n > kMaxElems || channels < 1 || channels > AR_FIFO_MAX_CHANNELS ||
+        max_spins > AR_MAX_SPINS)
+        return AR_ERR_ARG;
+    if (!aligned(src, 4) || !aligned(out, 4) || (local && !aligned(local, 4)) ||
+        !aligned(fifo, proto == AR_PROTO_LL128 ? 128 : 16) || !aligned(counters, 8) ||
+        !aligned(errors, 4))
+        return AR_ERR_ALIGN;
+    const int64_t fifo_bytes = (int64_t)channels * AR_FIFO_STEPS * wire;
+    const int64_t cnt_bytes = 2 * (int64_t)channels * 8;
+    if (overlaps(out, 4 * n, src, 4 * n) || (local && overlaps_partially(out, local, 4 * n)) ||
+        overlaps(out, 4 * n, fifo, fifo_bytes) || overlaps(out, 4 * n, counters, cnt_bytes) ||
+        overlaps(out, 4 * n, errors, 4) || overlaps(fifo, fifo_bytes, src, 4 * n) ||
+        (local && overlaps(fifo, fifo_bytes, local, 4 * n)) ||
+        overlaps(fifo, fifo_bytes, counters, cnt_bytes) || overlaps(fifo, fifo_bytes, errors, 4) ||
+        overlaps(counters, cnt_bytes, errors, 4) || overlaps(counters, cnt_bytes, src, 4 * n))
+        return AR_ERR_ARG;
+    if (n == 0)
+        return AR_OK;
+    return from_hip(ar::launch_fifo_stream(proto, src, local, out, n, fifo, counters, channels,
+                                           step_bytes, wire, first_step, max_spins, errors,
+                                           static_cast<hipStream_t>(stream)));
+}

@@ -36,7 +36,10 @@ EXPORTS = (
     "ar_lamport_oneshot_residual_rmsnorm", "ll_pack", "ll_unpack_reduce", "ll128_pack",
     "ll128_unpack_reduce", "ll_lines", "ll128_lines", "ll_fifo_bytes",
     "ll128_fifo_bytes", "ll_default_step_lines", "ll128_default_step_lines",
+    "ar_fifo_stream", "ar_fifo_step_wire_bytes", "ar_fifo_steps_per_channel",
 )
+AR_PROTO_LL, AR_PROTO_LL128, AR_PROTO_SIMPLE = 0, 1, 2
+AR_FIFO_MAX_CHANNELS = 128
 
 _vp, _i64, _u64, _u32, _int = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
                                ctypes.c_uint32, ctypes.c_int)
@@ -78,6 +81,15 @@ for _n in ("ll_lines", "ll128_lines", "ll_fifo_bytes", "ll128_fifo_bytes"):
 for _n in ("ll_default_step_lines", "ll128_default_step_lines"):
     getattr(_lib, _n).argtypes = []
     getattr(_lib, _n).restype = _i64
+
+
+_lib.ar_fifo_stream.argtypes = [_int, _vp, _vp, _vp, _i64, _vp, _vp, _int, _i64, _u64, _u32,
+                                _vp, _vp]
+_lib.ar_fifo_stream.restype = _int
+_lib.ar_fifo_step_wire_bytes.argtypes = [_int, _i64]
+_lib.ar_fifo_step_wire_bytes.restype = _i64
+_lib.ar_fifo_steps_per_channel.argtypes = [_i64, _i64, _int]
+_lib.ar_fifo_steps_per_channel.restype = _i64
 
 
 class ArError(RuntimeError):
@@ -261,6 +273,24 @@ def ll_default_step_lines() -> int:
 
 def ll128_default_step_lines() -> int:
     return _lib.ll128_default_step_lines()
+
+
+def ar_fifo_step_wire_bytes(proto: int, step_bytes: int) -> int:
+    return _lib.ar_fifo_step_wire_bytes(proto, step_bytes)
+
+
+def ar_fifo_steps_per_channel(n: int, step_bytes: int, channels: int) -> int:
+    return _lib.ar_fifo_steps_per_channel(n, step_bytes, channels)
+
+
+def ar_fifo_stream(proto: int, src, out, fifo, counters, channels: int, step_bytes: int,
+                   first_step: int = 0, max_spins: int = AR_MAX_SPINS, errors=None,
+                   local=None, n: Optional[int] = None, stream=None) -> None:
+    """Stream src through `channels` 8-slot rings (one cooperative launch of
+    producers and consumers) into out (= src, or local + src)."""
+    _check(_lib.ar_fifo_stream(proto, _addr(src), _addr(local), _addr(out), _numel(src, n),
+                               _addr(fifo), _addr(counters), channels, step_bytes, first_step,
+                               max_spins, _addr(errors), _stream(stream)), "ar_fifo_stream")
 
 
 def status_str(status: int) -> str:

@@ -324,6 +324,68 @@ ar_status_t ll128_unpack_reduce(const void *const *fifos, int W, float *out,
                                 uint64_t first_step, uint32_t max_spins,
                                 uint32_t *bad_lines, ar_stream_t stream);
 
+/*
+ * Streaming through 8-step FIFOs on one device ([NCCL14] "prerequisite
+ * mental model": a ring of 8 steps; the sender never overwrites a step the
+ * receiver has not consumed and the receiver never consumes a step before it
+ * is ready; "how LL publishes and waits for flags", "LL128's warp-level
+ * ready check", "how Simple synchronizes").  The 4n payload bytes are cut
+ * into steps of step_bytes payload bytes; the T = ceil(4n / step_bytes)
+ * steps are dealt to `channels` channels in contiguous runs (channel c takes
+ * steps [c*T/channels, (c+1)*T/channels)).  Each channel has an 8-slot ring
+ * and a producer and a consumer workgroup that run concurrently in one
+ * cooperative launch.  Local step j of a channel is ring step
+ * k = first_step + j, in slot k mod 8:
+ *   AR_PROTO_LL      16-byte lines of 8 payload bytes + two 32-bit flags
+ *                    (k + 1), ready when both flags match
+ *   AR_PROTO_LL128   128-byte lines of 120 payload bytes + a 64-bit flag;
+ *                    the producer writes a step's data, fences, then its
+ *                    flags; the consumer re-reads a line after validating it
+ *   AR_PROTO_SIMPLE  raw payload; ready when the channel's tail counter
+ *                    reaches k + 1
+ * After each step the consumer sets the channel's head counter to k + 1; the
+ * producer reuses slot k mod 8 only once head >= k - 7.  A step writes only
+ * the lines (or bytes) that carry payload.  The consumer delivers
+ * out[e] = src[e], or local[e] + src[e] in fp32 when local is given.
+ *   proto       AR_PROTO_LL / AR_PROTO_LL128 / AR_PROTO_SIMPLE
+ *   step_bytes  payload bytes per step: a multiple of 8 / 120 / 16, at most
+ *               2^30 (NCCL's defaults: 32768 / 576000 / 524288)
+ *   fifo        channels * 8 * ar_fifo_step_wire_bytes(proto, step_bytes)
+ *               bytes, 16-byte aligned (128 for LL128)
+ *   counters    2 * channels u64 (heads, then tails), 8-byte aligned
+ *   channels    1..AR_FIFO_MAX_CHANNELS
+ *   first_step  0 with fifo and counters zeroed; a later call on the same
+ *               fifo and counters continues with first_step advanced by
+ *               ar_fifo_steps_per_channel(n, step_bytes, channels) of the
+ *               previous call (flags and counters only ever grow)
+ *   max_spins   bound on every wait (<= AR_MAX_SPINS); a wait that runs out
+ *               adds 1 to errors[0] and makes every other wait of the launch
+ *               give up, so the launch always ends
+ *   errors      device u32 the caller zeroes; non-zero afterwards means out
+ *               is unspecified and fifo/counters must be zeroed before reuse
+ *   src, local, out  n fp32, 4-byte aligned; out may equal local, no other
+ *               overlap among the buffers                 else AR_ERR_ARG
+ * AR_ERR_HIP if the runtime cannot make all 2 * channels workgroups
+ * resident at once.
+ */
+#define AR_PROTO_LL 0
+#define AR_PROTO_LL128 1
+#define AR_PROTO_SIMPLE 2
+#define AR_FIFO_MAX_CHANNELS 128
+
+ar_status_t ar_fifo_stream(int proto, const float *src, const float *local,
+                           float *out, int64_t n, void *fifo, uint64_t *counters,
+                           int channels, int64_t step_bytes, uint64_t first_step,
+                           uint32_t max_spins, uint32_t *errors,
+                           ar_stream_t stream);
+
+/* Ring bytes per step for a protocol (0 if step_bytes is not valid). */
+int64_t ar_fifo_step_wire_bytes(int proto, int64_t step_bytes);
+
+/* Ring steps a call advances every channel's numbering by:
+ * ceil(ceil(4n / step_bytes) / channels) (0 for invalid arguments). */
+int64_t ar_fifo_steps_per_channel(int64_t n, int64_t step_bytes, int channels);
+
 /* Geometry helpers ([NCCL14] "Default buffers and effective data per
  * step": the default buffers give 4096 LL lines and 4800 LL128 lines per
  * step).  Negative arguments give 0. */

@@ -1,0 +1,113 @@
+"""GPU parity of streaming through 8-step FIFOs (producer and consumer
+workgroups concurrent in one cooperative launch) against the oracle: the
+delivered payload and the rings' final bytes are bit-exact, and no wait
+times out.  Every wait in the kernel is bounded; the abort test forces the
+give-up path from the host (the error count set before the launch)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from ar_rmsnorm_amd import libar as ar
+from ar_rmsnorm_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+PROTOS = {"ll": ar.AR_PROTO_LL, "ll128": ar.AR_PROTO_LL128, "simple": ar.AR_PROTO_SIMPLE}
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+class Fifo:
+    def __init__(self, proto, step, channels, device):
+        self.proto, self.step, self.channels = proto, step, channels
+        wire = ar.ar_fifo_step_wire_bytes(proto, step)
+        assert wire > 0
+        self.fifo = torch.zeros(channels * 8 * wire, dtype=torch.uint8, device=device)
+        self.counters = torch.zeros(2 * channels, dtype=torch.int64, device=device)
+        self.errors = torch.zeros(1, dtype=torch.int32, device=device)
+        self.host = np.zeros(channels * 8 * wire, np.uint8)
+        self.first = 0
+
+    def run(self, src, local=None, max_spins=ar.AR_MAX_SPINS):
+        n = src.size
+        d = torch.from_numpy(src).to(self.fifo.device)
+        dl = None if local is None else torch.from_numpy(local).to(self.fifo.device)
+        out = torch.full((n + 16,), 777.0, dtype=torch.float32, device=self.fifo.device)
+        ar.ar_fifo_stream(self.proto, d, out, self.fifo, self.counters, self.channels, self.step,
+                          self.first, max_spins, self.errors, local=dl, n=n)
+        sync()
+        got = out.cpu().numpy()
+        assert np.all(got[n:] == 777.0), "wrote past n"
+        want, self.host = orc.fifo_stream(self.proto, src, self.channels, self.step, self.first,
+                                          local=local, fifo=self.host)
+        assert int(self.errors.item()) == 0, "a wait timed out"
+        assert np.array_equal(got[:n].view(np.uint32), want.view(np.uint32)), "payload"
+        assert np.array_equal(self.fifo.cpu().numpy(), self.host), "ring bytes"
+        self.first += ar.ar_fifo_steps_per_channel(n, self.step, self.channels)
+
+
+@pytest.mark.parametrize("name,step", [("ll", 1024), ("ll128", 1200), ("simple", 1024)])
+@pytest.mark.parametrize("channels", [1, 4, 16])
+def test_stream_many_laps(gpu, name, step, channels):
+    """About 20 steps per channel (2.5 laps of the ring) and a ragged tail."""
+    n = channels * 20 * step // 4 + 13
+    src = synth.wire_payloads(1, n, [102, channels, step])[0]
+    Fifo(PROTOS[name], step, channels, gpu).run(src)
+
+
+@pytest.mark.parametrize("name,step,channels", [("ll", 32768, 16), ("ll128", 576000, 4),
+                                                ("simple", 524288, 4)])
+def test_stream_nccl_default_steps_wire_workload(gpu, name, step, channels):
+    """The wire workload (16 Mi + 13 fp32) at NCCL's default step sizes."""
+    n = synth.WIRE["n"] + synth.WIRE["tail"]
+    src = synth.wire(n)[0]
+    Fifo(PROTOS[name], step, channels, gpu).run(src)
+
+
+@pytest.mark.parametrize("name,step", [("ll", 2048), ("ll128", 2400), ("simple", 2048)])
+def test_stream_reduce_with_local_and_consecutive_calls(gpu, name, step):
+    f = Fifo(PROTOS[name], step, 8, gpu)
+    for call in range(3):
+        n = 8 * 13 * step // 4 + 7 * call + 1
+        src, local = synth.wire_payloads(2, n, [103, call])
+        f.run(src, local=local if call != 1 else None)
+
+
+def test_stream_aborted_launch_ends(gpu):
+    """The error count is set before the launch, so every wait gives up at
+    once: the launch must end (outputs unspecified)."""
+    proto, step, channels = ar.AR_PROTO_LL, 1024, 8
+    n = channels * 40 * step // 4
+    f = Fifo(proto, step, channels, gpu)
+    f.errors.fill_(1)
+    src = torch.zeros(n, dtype=torch.float32, device=gpu)
+    out = torch.empty_like(src)
+    ar.ar_fifo_stream(proto, src, out, f.fifo, f.counters, channels, step, 0, 64, f.errors)
+    sync()
+    assert int(f.errors.item()) >= 1
+
+
+def test_stream_argument_errors(gpu):
+    f = Fifo(ar.AR_PROTO_LL128, 1200, 2, gpu)
+    src = torch.zeros(1000, dtype=torch.float32, device=gpu)
+    out = torch.zeros(1000, dtype=torch.float32, device=gpu)
+    for bad_step in (1000, 0, 119):
+        with pytest.raises(ar.ArError) as e:
+            ar.ar_fifo_stream(ar.AR_PROTO_LL128, src, out, f.fifo, f.counters, 2, bad_step, 0,
+                              100, f.errors)
+        assert e.value.status == ar.AR_ERR_ARG
+    with pytest.raises(ar.ArError) as e:
+        ar.ar_fifo_stream(ar.AR_PROTO_LL128, src, out, f.fifo, f.counters, 0, 1200, 0, 100,
+                          f.errors)
+    assert e.value.status == ar.AR_ERR_ARG
+    with pytest.raises(ar.ArError) as e:
+        ar.ar_fifo_stream(3, src, out, f.fifo, f.counters, 2, 1200, 0, 100, f.errors)
+    assert e.value.status == ar.AR_ERR_ARG
+    with pytest.raises(ar.ArError) as e:
+        ar.ar_fifo_stream(ar.AR_PROTO_LL128, src, src, f.fifo, f.counters, 2, 1200, 0, 100,
+                          f.errors)
+    assert e.value.status == ar.AR_ERR_ARG      # out overlaps src
+    sync()
