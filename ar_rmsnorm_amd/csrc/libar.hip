@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "launch.h"
 
 #define LIBAR_EXPORT extern "C" __attribute__((visibility("default")))
@@ -529,6 +531,38 @@ LIBAR_EXPORT int64_t ar_fifo_steps_per_channel(int64_t n, int64_t step_bytes, in
     return (total + channels - 1) / channels;
 }
 
+LIBAR_EXPORT int64_t ar_fifo_counter_words(int channels)
+{
+    return channels < 1 || channels > AR_FIFO_MAX_CHANNELS ? 0 : 2 * (int64_t)channels + 2;
+}
+
+namespace {
+
+// Workgroups of the streaming kernel the device can hold at once, per
+// (device, protocol), looked up once.
+int resident_workgroups(int proto, bool local, int *workgroups)
+{
+    constexpr int kDevices = 64;
+    static std::atomic<int> cache[kDevices][3][2];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return (int)e;
+    if (dev >= 0 && dev < kDevices) {
+        const int c = cache[dev][proto][local].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *workgroups = c;
+            return 0;
+        }
+    }
+    e = ar::fifo_stream_resident_workgroups(proto, local, workgroups);
+    if (e == hipSuccess && dev >= 0 && dev < kDevices)
+        cache[dev][proto][local].store(*workgroups, std::memory_order_relaxed);
+    return (int)e;
+}
+
+}  // namespace
+
 LIBAR_EXPORT ar_status_t ar_fifo_stream(int proto, const float *src, const float *local,
                                         float *out, int64_t n, void *fifo, uint64_t *counters,
                                         int channels, int64_t step_bytes, uint64_t first_step,
@@ -546,17 +580,31 @@ LIBAR_EXPORT ar_status_t ar_fifo_stream(int proto, const float *src, const float
         !aligned(errors, 4))
         return AR_ERR_ALIGN;
     const int64_t fifo_bytes = (int64_t)channels * AR_FIFO_STEPS * wire;
-    const int64_t cnt_bytes = 2 * (int64_t)channels * 8;
-    if (overlaps(out, 4 * n, src, 4 * n) || (local && overlaps_partially(out, local, 4 * n)) ||
-        overlaps(out, 4 * n, fifo, fifo_bytes) || overlaps(out, 4 * n, counters, cnt_bytes) ||
-        overlaps(out, 4 * n, errors, 4) || overlaps(fifo, fifo_bytes, src, 4 * n) ||
-        (local && overlaps(fifo, fifo_bytes, local, 4 * n)) ||
-        overlaps(fifo, fifo_bytes, counters, cnt_bytes) || overlaps(fifo, fifo_bytes, errors, 4) ||
-        overlaps(counters, cnt_bytes, errors, 4) || overlaps(counters, cnt_bytes, src, 4 * n))
+    const int64_t cnt_bytes = ar_fifo_counter_words(channels) * 8;
+    const int64_t nb = 4 * n;
+    const void *ro[2] = {src, local};   // read-only inputs
+    for (const void *r : ro) {
+        if (!r)
+            continue;
+        if (overlaps(fifo, fifo_bytes, r, nb) || overlaps(counters, cnt_bytes, r, nb) ||
+            overlaps(errors, 4, r, nb))
+            return AR_ERR_ARG;
+    }
+    if (overlaps(out, nb, src, nb) || (local && overlaps_partially(out, local, nb)) ||
+        overlaps(out, nb, fifo, fifo_bytes) || overlaps(out, nb, counters, cnt_bytes) ||
+        overlaps(out, nb, errors, 4) || overlaps(fifo, fifo_bytes, counters, cnt_bytes) ||
+        overlaps(fifo, fifo_bytes, errors, 4) || overlaps(counters, cnt_bytes, errors, 4))
         return AR_ERR_ARG;
     if (n == 0)
         return AR_OK;
+    int resident = 0;
+    const int he = resident_workgroups(proto, local != nullptr, &resident);
+    if (he != 0)
+        return from_hip((hipError_t)he);
+    if (resident < 2 * channels)
+        return AR_ERR_CAPACITY;
     return from_hip(ar::launch_fifo_stream(proto, src, local, out, n, fifo, counters, channels,
-                                           step_bytes, wire, first_step, max_spins, errors,
+                                           step_bytes, wire, first_step,
+                                           first_step == AR_FIFO_CONTINUE, max_spins, errors,
                                            static_cast<hipStream_t>(stream)));
 }

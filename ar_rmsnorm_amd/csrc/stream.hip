@@ -1,6 +1,6 @@
 // Streaming a payload through 8-step FIFOs on one device: producer and
-// consumer workgroups run concurrently in one cooperative launch, one pair
-// per channel, each channel with its own 8-slot ring.
+// consumer workgroups run concurrently in one launch, one pair per channel,
+// each channel with its own 8-slot ring.
 //
 // Source (web page; cited by tag and section):
 //   [NCCL14] "NCCL 专家课程 14：Simple、LL、LL128 的线格式、同步与真实性能边界"
@@ -12,32 +12,55 @@
 //            synchronizes".
 //
 // Protocols (payload per step = step_bytes):
-//   LL      16-byte lines {lo, flag, hi, flag}; each 8-byte half is written
-//           in one access, so a line is ready once both flags are k + 1.
+//   LL      16-byte lines {lo, flag, hi, flag}; each line is written in one
+//           16-byte access, so a line is ready once both flags are k + 1.
 //   LL128   128-byte lines, 120 payload bytes + a 64-bit flag.  gfx950 does
 //           not promise that a line written by eight lanes becomes visible
 //           as a whole, so the producer makes the order explicit: all data
-//           chunks of the step, then a release fence, then the flag words;
-//           the consumer validates the flags with a wavefront vote and
-//           re-reads the line after validation, as the page's receiver does.
-//   Simple  raw payload; the producer publishes a tail step after a release
-//           fence and the consumer waits for it.
+//           of the step, then a release fence, then the flag words.  The
+//           consumer waits for one flag of the step (after which every data
+//           byte of the step is visible), then reads every line and checks
+//           every line's flag, re-reading the flag chunk of lines whose flag
+//           has not arrived yet.
+//   Simple  raw payload; the producer publishes a tail step once the step's
+//           data is acknowledged, and the consumer waits for it.
 // For every protocol the consumer publishes a head step (the next step it
 // will consume) after each step, and the producer reuses slot k mod 8 only
 // once head >= k - 7.
 //
-// Ring accesses use system-coherent loads and stores (sc0 sc1): producer and
-// consumer may sit on different XCDs, whose L2 caches are not coherent with
-// each other for these buffers.  Counters use agent-scope acquire/release
-// atomics.  Every wait is bounded by max_spins and also ends as soon as any
-// wait of the launch has failed (errors[0] != 0), so the launch always
-// drains; its outputs are then unspecified.
+// Memory-level parallelism: every lane issues kBatch loads (source words,
+// ring chunks, local addends) before it checks or stores any of them, items
+// not yet ready are re-polled together, and the consumer releases a slot
+// before it stores the step's last batch, so a step costs a few memory round
+// trips rather than one per line.
+//
+// Step numbering persists in device memory between calls, as NCCL keeps a
+// connection's step across launches: the counters end with {next first step,
+// finished consumers}, and the last consumer of a launch to finish advances
+// the stored first step by the call's steps per channel.  A call that asks
+// for the stored step starts from it, which keeps a captured graph
+// replayable.
+//
+// Ordering without cache maintenance.  Producer and consumer may sit on
+// different XCDs, whose L2 caches are not coherent with each other, so every
+// ring and counter access is system-coherent (sc0 sc1): a load reads the
+// coherent copy and a store is acknowledged only once it is visible there.
+// With that, "data before flag" needs no L2 write-back: a wavefront waits
+// for its own stores (vmcnt(0)), the workgroup meets at a barrier, and only
+// then is the flag, tail or head written.  A reader orders its later loads
+// after a flag simply by issuing them after the flag's value came back.
+// Counters are relaxed atomics, and each side caches the last value it saw
+// of the other's counter, as NCCL caches a peer's step.  Every wait is
+// bounded by max_spins and also ends as soon as any wait of the launch has
+// failed (errors[0] != 0), so the launch always drains; its outputs are then
+// unspecified.
 #include "device.h"
 #include "launch.h"
 
 namespace ar {
 
-constexpr int kStreamThreads = 256;
+constexpr int kStreamThreads = 512;
+constexpr int kBatch = 8;              // loads in flight per lane
 constexpr uint32_t kAbortCheck = 16;   // spins between looks at the error count
 
 struct StreamArgs {
@@ -48,11 +71,14 @@ struct StreamArgs {
     uint8_t *fifo;          // channels x 8 slots x wire bytes
     uint64_t *head;         // per channel: next ring step the consumer needs
     uint64_t *tail;         // per channel (Simple): ring steps published
+    uint64_t *state;        // {next first step, finished consumers}
     uint32_t *errors;       // [0]: failed waits
     int64_t step_bytes;     // payload bytes per step
     int64_t wire_bytes;     // ring bytes per step
     int64_t total_steps;    // T = ceil(4n / step_bytes)
+    int64_t steps_per_channel;
     int channels;
+    int from_state;         // the first step comes from state[0]
     uint64_t first_step;
     uint32_t max_spins;
 };
@@ -65,235 +91,664 @@ __device__ __forceinline__ void store8_sys(uint8_t *p, u32x2 v)
 {
     *reinterpret_cast<volatile u32x2 *>(p) = v;
 }
+__device__ __forceinline__ void store4_sys(uint8_t *p, uint32_t v)
+{
+    *reinterpret_cast<volatile uint32_t *>(p) = v;
+}
 __device__ __forceinline__ u32x4 load16_sys(const uint8_t *p)
 {
     return *reinterpret_cast<const volatile u32x4 *>(p);
 }
-__device__ __forceinline__ uint64_t load_acquire(const uint64_t *p)
+__device__ __forceinline__ u32x2 load8_sys(const uint8_t *p)
 {
-    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+    return *reinterpret_cast<const volatile u32x2 *>(p);
 }
-__device__ __forceinline__ void store_release(uint64_t *p, uint64_t v)
+__device__ __forceinline__ uint64_t load_counter(const uint64_t *p)
 {
-    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ void store_counter(uint64_t *p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 __device__ __forceinline__ bool aborted(const uint32_t *errors)
 {
     return __hip_atomic_load(errors, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
 }
+// The wavefront's loads have returned and its stores are acknowledged (on
+// gfx950 a workgroup-scope release fence is s_waitcnt vmcnt(0) lgkmcnt(0)).
+__device__ __forceinline__ void drain_memory()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+}
 
-// Lane 0 waits until *counter >= target (bounded); the verdict reaches the
-// whole workgroup through LDS.  Returns false if the launch must stop.
-__device__ bool wait_counter(const uint64_t *counter, uint64_t target, const StreamArgs &a,
-                             int *verdict)
+// Per-workgroup LDS slots for broadcasting lane 0's results.
+struct Shared {
+    int verdict;
+    uint64_t value;
+};
+
+// Lane 0 waits (bounded) until poll() returns a value v with ready(v); the
+// verdict and v reach the whole workgroup through LDS.  Returns false if the
+// launch must stop.  Callers call it uniformly.
+template <typename Poll, typename Ready>
+__device__ bool wait_lane0(const StreamArgs &a, Shared *sh, uint64_t *seen, Poll poll,
+                           Ready ready)
 {
     if (threadIdx.x == 0) {
-        bool ok = load_acquire(counter) >= target;
+        uint64_t v = poll();
+        bool ok = ready(v);
         for (uint32_t s = 0; !ok && s < a.max_spins; ++s) {
             if (s % kAbortCheck == 0 && aborted(a.errors))
                 break;
-            ok = load_acquire(counter) >= target;
+            v = poll();
+            ok = ready(v);
         }
         if (!ok)
             atomicAdd(a.errors, 1u);
-        *verdict = ok ? 1 : 0;
+        sh->verdict = ok ? 1 : 0;
+        sh->value = v;
     }
     __syncthreads();
-    const bool go = *verdict != 0;
-    __syncthreads();   // the verdict slot is reused by the next wait
+    const bool go = sh->verdict != 0;
+    if (seen)
+        *seen = sh->value;
+    __syncthreads();   // the slots are reused by the next wait
     return go;
 }
 
-// Payload word w (zero past the end).
+// Wait until *counter >= need, skipping the poll when the last value seen
+// already satisfies it.
+__device__ bool wait_counter(const StreamArgs &a, Shared *sh, const uint64_t *counter,
+                             uint64_t need, uint64_t *seen)
+{
+    if (*seen >= need)
+        return true;
+    return wait_lane0(
+        a, sh, seen, [&] { return load_counter(counter); }, [&](uint64_t v) { return v >= need; });
+}
+
+// ---------------------------------------------------------------------------
+// Payload access: source words past n read as zero; only out[0, n) is
+// written and only local[0, n) is read.
 __device__ __forceinline__ uint32_t word_at(const StreamArgs &a, int64_t w)
 {
     return w < a.n ? a.src[w] : 0u;
 }
-
-__device__ __forceinline__ void deliver(const StreamArgs &a, int64_t w, uint32_t bits)
+__device__ __forceinline__ u32x2 pair_at(const StreamArgs &a, int64_t w)
 {
-    if (w < a.n) {
-        const float v = __uint_as_float(bits);
-        a.out[w] = a.local ? a.local[w] + v : v;
+    if (w + 2 <= a.n)
+        return ld2_stream_a4(a.src + w);
+    return u32x2{word_at(a, w), word_at(a, w + 1)};
+}
+__device__ __forceinline__ u32x4 quad_at(const StreamArgs &a, int64_t w)
+{
+    if (w + 4 <= a.n)
+        return ld4_stream_a4(a.src + w);
+    return u32x4{word_at(a, w), word_at(a, w + 1), word_at(a, w + 2), word_at(a, w + 3)};
+}
+
+// The local addend of words [w, w + cnt) (cnt is 2 or 4), zero past n.
+__device__ __forceinline__ u32x4 local_at(const StreamArgs &a, int64_t w, int cnt)
+{
+    const uint32_t *l = reinterpret_cast<const uint32_t *>(a.local);
+    if (cnt == 4 && w + 4 <= a.n)
+        return ld4_stream_a4(l + w);
+    if (cnt == 2 && w + 2 <= a.n) {
+        const u32x2 v = ld2_stream_a4(l + w);
+        return u32x4{v.x, v.y, 0u, 0u};
+    }
+    u32x4 r = {0u, 0u, 0u, 0u};
+    for (int e = 0; e < cnt; ++e)
+        if (w + e < a.n)
+            r[e] = l[w + e];
+    return r;
+}
+
+// out[w + e] = v[e], or local[w + e] + v[e] in fp32, for e < cnt, w + e < n.
+template <bool LOCAL>
+__device__ __forceinline__ void deliver(const StreamArgs &a, int64_t w, int cnt, u32x4 v,
+                                        u32x4 lv)
+{
+    if (LOCAL) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            v[e] = __float_as_uint(__uint_as_float(lv[e]) + __uint_as_float(v[e]));
+    }
+    uint32_t *o = reinterpret_cast<uint32_t *>(a.out);
+    if (cnt == 4 && w + 4 <= a.n) {
+        st4_stream_a4(o + w, v);
+    } else if (cnt == 2 && w + 2 <= a.n) {
+        st2_stream_a4(o + w, u32x2{v.x, v.y});
+    } else {
+        for (int e = 0; e < cnt; ++e)
+            if (w + e < a.n)
+                o[w + e] = v[e];
     }
 }
 
 // ---------------------------------------------------------------------------
+// Steps and batches.  Items are LL lines, LL128 line chunks (line q / 8,
+// chunk q % 8: chunks 0..6 carry 16 payload bytes, chunk 7 carries 8 payload
+// bytes and then the flag) or Simple 16-byte chunks.  A batch is kBatch items
+// per lane: items base + u * kStreamThreads + threadIdx.x, u < kBatch.
+struct Step {
+    uint8_t *slot;
+    int64_t w0;       // first payload word
+    int64_t words;    // payload words
+    int64_t items;
+    uint64_t k;       // ring step
+};
+
+constexpr int64_t kPerBatch = (int64_t)kStreamThreads * kBatch;
+
 template <int PROTO>
-__device__ void produce(const StreamArgs &a, int c, int64_t s0, int64_t steps, int *verdict)
+__device__ __forceinline__ Step step_at(const StreamArgs &a, uint8_t *ring, int64_t s0,
+                                        uint64_t first, int64_t j)
 {
-    uint8_t *ring = a.fifo + (int64_t)c * 8 * a.wire_bytes;
-    const int t = threadIdx.x;
-    const int64_t nbytes = 4 * a.n;
-    for (int64_t j = 0; j < steps; ++j) {
-        const uint64_t k = a.first_step + (uint64_t)j;
-        if (j >= 8 && !wait_counter(a.head + c, k - 7, a, verdict))
-            return;
-        uint8_t *slot = ring + (int64_t)(k % 8u) * a.wire_bytes;
-        const int64_t b0 = (s0 + j) * a.step_bytes;
-        const int64_t len = nbytes - b0 < a.step_bytes ? nbytes - b0 : a.step_bytes;
-        const int64_t w0 = b0 / 4;
-        if (PROTO == 0) {
-            const uint32_t flag = (uint32_t)(k + 1);
-            for (int64_t i = t; i < (len + 7) / 8; i += kStreamThreads)
-                store16_sys(slot + 16 * i, u32x4{word_at(a, w0 + 2 * i), flag,
-                                                 word_at(a, w0 + 2 * i + 1), flag});
-        } else if (PROTO == 1) {
-            const int64_t lines = (len + 119) / 120;
-            for (int64_t q = t; q < lines * 8; q += kStreamThreads) {
-                const int64_t l = q >> 3;
-                const int ch = (int)(q & 7);
-                const int64_t w = w0 + 30 * l + 4 * ch;
-                if (ch < 7)
-                    store16_sys(slot + 128 * l + 16 * ch,
-                                u32x4{word_at(a, w), word_at(a, w + 1), word_at(a, w + 2),
-                                      word_at(a, w + 3)});
-                else
-                    store8_sys(slot + 128 * l + 112, u32x2{word_at(a, w), word_at(a, w + 1)});
+    Step g;
+    g.k = first + (uint64_t)j;
+    g.slot = ring + (int64_t)(g.k % 8u) * a.wire_bytes;
+    const int64_t b0 = (s0 + j) * a.step_bytes;
+    const int64_t left = 4 * a.n - b0;
+    const int64_t len = left < a.step_bytes ? left : a.step_bytes;
+    g.w0 = b0 / 4;
+    g.words = len / 4;
+    g.items = PROTO == 0 ? (len + 7) / 8 : PROTO == 1 ? (len + 119) / 120 * 8 : (g.words + 3) / 4;
+    return g;
+}
+
+// The next batch after (j, base); more is false past the channel's last step.
+template <int PROTO>
+struct Cursor {
+    int64_t j, base;
+    Step g;
+};
+
+template <int PROTO>
+__device__ __forceinline__ bool advance(const StreamArgs &a, uint8_t *ring, int64_t s0,
+                                        uint64_t first, int64_t steps, const Cursor<PROTO> &cur,
+                                        Cursor<PROTO> *nxt)
+{
+    nxt->j = cur.j;
+    nxt->base = cur.base + kPerBatch;
+    nxt->g = cur.g;
+    if (nxt->base >= cur.g.items) {
+        nxt->j = cur.j + 1;
+        nxt->base = 0;
+        if (nxt->j < steps)
+            nxt->g = step_at<PROTO>(a, ring, s0, first, nxt->j);
+    }
+    return nxt->j < steps;
+}
+
+// Payload words of item i of a step and how many of them there are.
+template <int PROTO>
+__device__ __forceinline__ int64_t item_word(const Step &g, int64_t i)
+{
+    return PROTO == 0 ? g.w0 + 2 * i : PROTO == 1 ? g.w0 + 30 * (i >> 3) + 4 * (i & 7)
+                                                  : g.w0 + 4 * i;
+}
+template <int PROTO>
+__device__ __forceinline__ int item_count(const Step &g, int64_t i)
+{
+    if (PROTO == 0)
+        return 2;
+    if (PROTO == 1)
+        return (i & 7) < 7 ? 4 : 2;
+    const int64_t rem = g.words - 4 * i;
+    return rem < 4 ? (int)rem : 4;
+}
+template <int PROTO>
+__device__ __forceinline__ int64_t ring_offset(int64_t i)
+{
+    return PROTO == 1 ? 128 * (i >> 3) + 16 * (i & 7) : 16 * i;
+}
+
+// Source words of a batch (zero for items past the step).
+template <int PROTO>
+__device__ __forceinline__ void load_src(const StreamArgs &a, const Step &g, int64_t base,
+                                         u32x4 d[kBatch])
+{
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        const int64_t i = base + (int64_t)u * kStreamThreads + threadIdx.x;
+        d[u] = u32x4{0u, 0u, 0u, 0u};
+        if (i < g.items) {
+            const int64_t w = item_word<PROTO>(g, i);
+            if (item_count<PROTO>(g, i) == 2) {
+                const u32x2 p = pair_at(a, w);
+                d[u] = u32x4{p.x, p.y, 0u, 0u};
+            } else {
+                d[u] = quad_at(a, w);
             }
-            __threadfence();     // this lane's data is visible before ...
-            __syncthreads();     // ... any lane of the workgroup writes a flag
-            const uint64_t flag = k + 1;
-            for (int64_t l = t; l < lines; l += kStreamThreads)
-                store8_sys(slot + 128 * l + 120, u32x2{(uint32_t)flag, (uint32_t)(flag >> 32)});
-        } else {
-            const int64_t words = len / 4;
-            for (int64_t q = t; q < (words + 3) / 4; q += kStreamThreads) {
-                const int64_t w = w0 + 4 * q;
-                if (4 * q + 3 < words)
-                    store16_sys(slot + 16 * q, u32x4{word_at(a, w), word_at(a, w + 1),
-                                                     word_at(a, w + 2), word_at(a, w + 3)});
-                else
-                    for (int64_t e = 4 * q; e < words; ++e)
-                        *reinterpret_cast<volatile uint32_t *>(slot + 4 * e) = word_at(a, w0 + e);
-            }
-            __threadfence();
-            __syncthreads();
-            if (t == 0)
-                store_release(a.tail + c, k + 1);
         }
     }
 }
 
 template <int PROTO>
-__device__ void consume(const StreamArgs &a, int c, int64_t s0, int64_t steps, int *verdict)
+__device__ __forceinline__ void store_ring(const Step &g, int64_t base, const u32x4 d[kBatch])
 {
-    const uint8_t *ring = a.fifo + (int64_t)c * 8 * a.wire_bytes;
-    const int t = threadIdx.x;
-    const int lane = t & 63;
-    const int64_t nbytes = 4 * a.n;
-    for (int64_t j = 0; j < steps; ++j) {
-        const uint64_t k = a.first_step + (uint64_t)j;
-        const uint8_t *slot = ring + (int64_t)(k % 8u) * a.wire_bytes;
-        const int64_t b0 = (s0 + j) * a.step_bytes;
-        const int64_t len = nbytes - b0 < a.step_bytes ? nbytes - b0 : a.step_bytes;
-        const int64_t w0 = b0 / 4;
-        bool failed = false;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        const int64_t i = base + (int64_t)u * kStreamThreads + threadIdx.x;
+        if (i >= g.items)
+            continue;
+        uint8_t *p = g.slot + ring_offset<PROTO>(i);
         if (PROTO == 0) {
-            const uint32_t flag = (uint32_t)(k + 1);
-            for (int64_t i = t; i < (len + 7) / 8; i += kStreamThreads) {
-                u32x4 v = load16_sys(slot + 16 * i);
-                bool ok = v.y == flag && v.w == flag;
-                for (uint32_t s = 0; !ok && s < a.max_spins; ++s) {
-                    if (s % kAbortCheck == 0 && aborted(a.errors))
-                        break;
-                    v = load16_sys(slot + 16 * i);
-                    ok = v.y == flag && v.w == flag;
-                }
-                if (!ok) {
-                    failed = true;
-                    break;
-                }
-                deliver(a, w0 + 2 * i, v.x);
-                deliver(a, w0 + 2 * i + 1, v.z);
-            }
+            const uint32_t f = (uint32_t)(g.k + 1);
+            store16_sys(p, u32x4{d[u].x, f, d[u].y, f});
         } else if (PROTO == 1) {
-            const int64_t lines = (len + 119) / 120;
-            const uint64_t flag = k + 1;
-            const uint32_t flo = (uint32_t)flag, fhi = (uint32_t)(flag >> 32);
-            // every lane runs every round (the vote is wavefront-wide)
-            for (int64_t base = 0; base < lines * 8; base += kStreamThreads) {
-                const int64_t q = base + t;
-                const int64_t l = q >> 3;
-                const int ch = (int)(q & 7);
-                const bool live = l < lines;
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (live)
-                    v = load16_sys(slot + 128 * l + 16 * ch);
-                bool ok = !live || ch != 7 || (v.z == flo && v.w == fhi);
-                uint64_t mask = __ballot(!ok);
-                for (uint32_t s = 0; mask != 0 && s < a.max_spins; ++s) {
-                    if (s % kAbortCheck == 0 && aborted(a.errors))
-                        break;
-                    if (live && ((mask >> (lane | 7)) & 1u))
-                        v = load16_sys(slot + 128 * l + 16 * ch);
-                    ok = !live || ch != 7 || (v.z == flo && v.w == fhi);
-                    mask = __ballot(!ok);
-                }
-                if (mask != 0) {
-                    failed = true;
-                    break;       // wavefront-uniform: mask is the same in every lane
-                }
-                // the flag is seen: re-read the chunk, now ordered after it
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                if (live) {
-                    v = load16_sys(slot + 128 * l + 16 * ch);
-                    const int64_t w = w0 + 30 * l + 4 * ch;
-                    deliver(a, w, v.x);
-                    deliver(a, w + 1, v.y);
-                    if (ch < 7) {
-                        deliver(a, w + 2, v.z);
-                        deliver(a, w + 3, v.w);
-                    }
-                }
-            }
+            if ((i & 7) < 7)
+                store16_sys(p, d[u]);
+            else
+                store8_sys(p, u32x2{d[u].x, d[u].y});
+        } else if (4 * i + 4 <= g.words) {
+            store16_sys(p, d[u]);
         } else {
-            if (!wait_counter(a.tail + c, k + 1, a, verdict))
-                return;
-            const int64_t words = len / 4;
-            for (int64_t q = t; q < (words + 3) / 4; q += kStreamThreads) {
-                const u32x4 v = load16_sys(slot + 16 * q);
-                for (int e = 0; e < 4; ++e)
-                    if (4 * q + e < words)
-                        deliver(a, w0 + 4 * q + e, v[e]);
-            }
+            for (int e = 0; e < 4; ++e)
+                if (4 * i + e < g.words)
+                    store4_sys(p + 4 * e, d[u][e]);
         }
-        if (failed)
-            atomicAdd(a.errors, 1u);
-        // all lanes have their data of step k in registers: release the slot
-        __syncthreads();
-        if (t == 0) {
-            *verdict = aborted(a.errors) ? 0 : 1;
-            if (*verdict)
-                store_release(a.head + c, k + 1);
-        }
-        __syncthreads();
-        const bool go = *verdict != 0;
-        __syncthreads();
-        if (!go)
+    }
+}
+
+template <int PROTO>
+__device__ __forceinline__ void load_ring(const Step &g, int64_t base, u32x4 v[kBatch])
+{
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        const int64_t i = base + (int64_t)u * kStreamThreads + threadIdx.x;
+        v[u] = i < g.items ? load16_sys(g.slot + ring_offset<PROTO>(i)) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+template <int PROTO, bool LOCAL>
+__device__ __forceinline__ void load_local(const StreamArgs &a, const Step &g, int64_t base,
+                                           u32x4 lv[kBatch])
+{
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        const int64_t i = base + (int64_t)u * kStreamThreads + threadIdx.x;
+        lv[u] = u32x4{0u, 0u, 0u, 0u};
+        if (LOCAL && i < g.items)
+            lv[u] = local_at(a, item_word<PROTO>(g, i), item_count<PROTO>(g, i));
+    }
+}
+
+template <int PROTO, bool LOCAL>
+__device__ __forceinline__ void deliver_batch(const StreamArgs &a, const Step &g, int64_t base,
+                                              const u32x4 v[kBatch], const u32x4 lv[kBatch])
+{
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        const int64_t i = base + (int64_t)u * kStreamThreads + threadIdx.x;
+        if (i >= g.items)
+            continue;
+        const u32x4 x = PROTO == 0 ? u32x4{v[u].x, v[u].z, 0u, 0u} : v[u];
+        deliver<LOCAL>(a, item_word<PROTO>(g, i), item_count<PROTO>(g, i), x, lv[u]);
+    }
+}
+
+// The batch's loads have returned (their registers are read by an empty
+// asm statement, so the compiler waits for exactly these loads).
+__device__ __forceinline__ void loads_returned(const u32x4 v[kBatch])
+{
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+        asm volatile("" ::"v"(v[u]));
+}
+
+// ---------------------------------------------------------------------------
+// Producer: the batches of the channel's steps in order, each batch's source
+// loads issued before the previous batch's ring stores.
+template <int PROTO>
+__device__ void produce(const StreamArgs &a, int c, int64_t s0, int64_t steps, uint64_t first,
+                        Shared *sh)
+{
+    if (steps <= 0)
+        return;
+    uint8_t *ring = a.fifo + (int64_t)c * 8 * a.wire_bytes;
+    uint64_t head_seen = first;      // the consumer has taken every step before `first`
+    Cursor<PROTO> cur{0, 0, step_at<PROTO>(a, ring, s0, first, 0)};
+    u32x4 d[kBatch];
+    load_src<PROTO>(a, cur.g, 0, d);
+    for (;;) {
+        Cursor<PROTO> nxt;
+        const bool more = advance<PROTO>(a, ring, s0, first, steps, cur, &nxt);
+        u32x4 nd[kBatch];
+        if (more)
+            load_src<PROTO>(a, nxt.g, nxt.base, nd);
+        if (cur.base == 0 && cur.j >= 8 &&
+            !wait_counter(a, sh, a.head + c, cur.g.k - 7, &head_seen))
             return;
+        store_ring<PROTO>(cur.g, cur.base, d);
+        if (PROTO == 1) {
+            // this batch's data is acknowledged before any of its flags
+            drain_memory();
+            __syncthreads();
+            const int64_t end = cur.base + kPerBatch < cur.g.items ? cur.base + kPerBatch
+                                                                    : cur.g.items;
+            const uint64_t f = cur.g.k + 1;
+            for (int64_t l = cur.base / 8 + threadIdx.x; l < end / 8; l += kStreamThreads)
+                store8_sys(cur.g.slot + 128 * l + 120, u32x2{(uint32_t)f, (uint32_t)(f >> 32)});
+        }
+        if (PROTO == 2 && nxt.j != cur.j) {
+            // the step's data is acknowledged before its tail
+            drain_memory();
+            __syncthreads();
+            if (threadIdx.x == 0)
+                store_counter(a.tail + c, cur.g.k + 1);
+        }
+        if (!more)
+            return;
+        cur = nxt;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            d[u] = nd[u];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Consumer side.  A step is closed once every lane's loads of it have
+// returned: the workgroup agrees on success and lane 0 publishes head = k + 1,
+// before the step's last batch is delivered from registers.  A failed wait
+// is counted where it happens.  Returns false once the launch must stop.
+__device__ bool close_step(const StreamArgs &a, int c, uint64_t k, bool failed)
+{
+    const bool any_failed = __syncthreads_or(failed ? 1 : 0) != 0;
+    if (threadIdx.x == 0 && !any_failed)
+        store_counter(a.head + c, k + 1);
+    return !any_failed;
+}
+
+// Re-read the items whose check failed, all at once, until every check holds
+// (bounded; gives up early once any wait of the launch has failed).
+template <typename Reload, typename Check>
+__device__ bool poll_batch(const StreamArgs &a, bool ok[kBatch], Reload reload, Check check)
+{
+    bool all = true;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+        all = all && ok[u];
+    for (uint32_t s = 0; !all && s < a.max_spins; ++s) {
+        if (s % kAbortCheck == 0 && aborted(a.errors))
+            break;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            if (!ok[u])
+                reload(u);
+        all = true;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            ok[u] = ok[u] || check(u);
+            all = all && ok[u];
+        }
+    }
+    if (!all)
+        atomicAdd(a.errors, 1u);
+    return all;
+}
+
+// LL: every line validates itself, so the next batch (also of the next step)
+// is loaded before this batch is delivered; lines not yet written are
+// re-polled.
+template <bool LOCAL>
+__device__ void consume_ll(const StreamArgs &a, int c, int64_t s0, int64_t steps, uint64_t first)
+{
+    if (steps <= 0)
+        return;
+    const uint8_t *ring = a.fifo + (int64_t)c * 8 * a.wire_bytes;
+    uint8_t *mring = const_cast<uint8_t *>(ring);
+    Cursor<0> cur{0, 0, step_at<0>(a, mring, s0, first, 0)};
+    u32x4 v[kBatch], lv[kBatch];
+    load_ring<0>(cur.g, 0, v);
+    load_local<0, LOCAL>(a, cur.g, 0, lv);
+    bool failed = false;
+    for (;;) {
+        const uint32_t flag = (uint32_t)(cur.g.k + 1);
+        const int64_t i0 = cur.base + threadIdx.x;
+        auto check = [&](int u) { return v[u].y == flag && v[u].w == flag; };
+        bool ok[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            ok[u] = i0 + (int64_t)u * kStreamThreads >= cur.g.items || check(u);
+        if (!failed)
+            failed = !poll_batch(
+                a, ok,
+                [&](int u) {
+                    v[u] = load16_sys(cur.g.slot + 16 * (i0 + (int64_t)u * kStreamThreads));
+                },
+                check);
+        Cursor<0> nxt;
+        const bool more = advance<0>(a, mring, s0, first, steps, cur, &nxt);
+        loads_returned(v);
+        if (nxt.j != cur.j && !close_step(a, c, cur.g.k, failed))
+            return;
+        u32x4 nv[kBatch], nlv[kBatch];
+        if (more) {
+            load_ring<0>(nxt.g, nxt.base, nv);
+            load_local<0, LOCAL>(a, nxt.g, nxt.base, nlv);
+        }
+        if (!failed)
+            deliver_batch<0, LOCAL>(a, cur.g, cur.base, v, lv);
+        if (!more)
+            return;
+        cur = nxt;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            v[u] = nv[u];
+            lv[u] = nlv[u];
+        }
+    }
+}
+
+// Lane 0 waits for a 64-bit flag, starting from a value it read earlier.
+__device__ bool wait_flag64(const StreamArgs &a, Shared *sh, const uint8_t *p, uint64_t want,
+                            uint64_t pre)
+{
+    bool first = true;
+    return wait_lane0(
+        a, sh, nullptr,
+        [&] {
+            if (first) {
+                first = false;
+                return pre;
+            }
+            const u32x2 f = load8_sys(p);
+            return (uint64_t)f.x | ((uint64_t)f.y << 32);
+        },
+        [&](uint64_t f) { return f == want; });
+}
+__device__ __forceinline__ uint64_t read_flag64(const uint8_t *p)
+{
+    const u32x2 f = load8_sys(p);
+    return (uint64_t)f.x | ((uint64_t)f.y << 32);
+}
+
+// LL128: a batch's data was acknowledged before any of its flags, so once
+// the flag of the batch's first line is seen the whole batch is read, each
+// line's flag checked, and chunk 7 of lines whose flag has not arrived yet
+// re-read.  Lane 0 reads the next batch's first flag together with this
+// batch's data, and the next batch is loaded before this one is delivered.
+template <bool LOCAL>
+__device__ void consume_ll128(const StreamArgs &a, int c, int64_t s0, int64_t steps,
+                              uint64_t first, Shared *sh)
+{
+    if (steps <= 0)
+        return;
+    uint8_t *ring = a.fifo + (int64_t)c * 8 * a.wire_bytes;
+    auto flag_at = [](const Step &g, int64_t base) { return g.slot + 128 * (base >> 3) + 120; };
+    Cursor<1> cur{0, 0, step_at<1>(a, ring, s0, first, 0)};
+    uint64_t pre = threadIdx.x == 0 ? read_flag64(flag_at(cur.g, 0)) : 0;
+    if (!wait_flag64(a, sh, flag_at(cur.g, 0), cur.g.k + 1, pre))
+        return;
+    u32x4 v[kBatch], lv[kBatch];
+    load_ring<1>(cur.g, 0, v);
+    load_local<1, LOCAL>(a, cur.g, 0, lv);
+    bool failed = false;
+    for (;;) {
+        Cursor<1> nxt;
+        const bool more = advance<1>(a, ring, s0, first, steps, cur, &nxt);
+        if (threadIdx.x == 0 && more)
+            pre = read_flag64(flag_at(nxt.g, nxt.base));
+        const uint64_t flag = cur.g.k + 1;
+        const uint32_t flo = (uint32_t)flag, fhi = (uint32_t)(flag >> 32);
+        const int64_t q0 = cur.base + threadIdx.x;
+        auto check = [&](int u) { return v[u].z == flo && v[u].w == fhi; };
+        bool ok[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t q = q0 + (int64_t)u * kStreamThreads;
+            ok[u] = q >= cur.g.items || (q & 7) != 7 || check(u);
+        }
+        if (!failed)
+            failed = !poll_batch(
+                a, ok,
+                [&](int u) {
+                    const int64_t q = q0 + (int64_t)u * kStreamThreads;
+                    v[u] = load16_sys(cur.g.slot + 128 * (q >> 3) + 112);
+                },
+                check);
+        loads_returned(v);
+        if (nxt.j != cur.j && !close_step(a, c, cur.g.k, failed))
+            return;
+        if (more && !wait_flag64(a, sh, flag_at(nxt.g, nxt.base), nxt.g.k + 1, pre))
+            return;
+        u32x4 nv[kBatch], nlv[kBatch];
+        if (more) {
+            load_ring<1>(nxt.g, nxt.base, nv);
+            load_local<1, LOCAL>(a, nxt.g, nxt.base, nlv);
+        }
+        if (!failed)
+            deliver_batch<1, LOCAL>(a, cur.g, cur.base, v, lv);
+        if (!more)
+            return;
+        cur = nxt;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            v[u] = nv[u];
+            lv[u] = nlv[u];
+        }
+    }
+}
+
+// Simple: a step is read only after its tail; within a step (and across a
+// step boundary when the tail already covers the next step) the next batch
+// is loaded before this one is delivered.
+template <bool LOCAL>
+__device__ void consume_simple(const StreamArgs &a, int c, int64_t s0, int64_t steps,
+                               uint64_t first, Shared *sh)
+{
+    if (steps <= 0)
+        return;
+    uint8_t *ring = a.fifo + (int64_t)c * 8 * a.wire_bytes;
+    uint64_t tail_seen = first;      // the producer has written every step before `first`
+    Cursor<2> cur{0, 0, step_at<2>(a, ring, s0, first, 0)};
+    if (!wait_counter(a, sh, a.tail + c, cur.g.k + 1, &tail_seen))
+        return;
+    u32x4 v[kBatch], lv[kBatch];
+    load_ring<2>(cur.g, 0, v);
+    load_local<2, LOCAL>(a, cur.g, 0, lv);
+    for (;;) {
+        Cursor<2> nxt;
+        const bool more = advance<2>(a, ring, s0, first, steps, cur, &nxt);
+        loads_returned(v);
+        if (nxt.j != cur.j && !close_step(a, c, cur.g.k, false))
+            return;
+        if (more && nxt.j != cur.j &&
+            !wait_counter(a, sh, a.tail + c, nxt.g.k + 1, &tail_seen))
+            return;
+        u32x4 nv[kBatch], nlv[kBatch];
+        if (more) {
+            load_ring<2>(nxt.g, nxt.base, nv);
+            load_local<2, LOCAL>(a, nxt.g, nxt.base, nlv);
+        }
+        deliver_batch<2, LOCAL>(a, cur.g, cur.base, v, lv);
+        if (!more)
+            return;
+        cur = nxt;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            v[u] = nv[u];
+            lv[u] = nlv[u];
+        }
     }
 }
 
 // Blocks [0, channels) produce, [channels, 2 * channels) consume.
-template <int PROTO>
+template <int PROTO, bool LOCAL>
 __global__ __launch_bounds__(kStreamThreads) void stream_kernel(StreamArgs a)
 {
-    __shared__ int verdict;
+    __shared__ Shared sh;
     const int b = blockIdx.x;
-    const int c = b < a.channels ? b : b - a.channels;
+    const bool producer = b < a.channels;
+    const int c = producer ? b : b - a.channels;
+    // Every block reads the stored first step before its channel moves, and
+    // the last consumer advances it only after every step of every channel
+    // has been written and read; a channel with no steps may read either
+    // value and uses neither.
+    if (threadIdx.x == 0)
+        sh.value = a.from_state ? __hip_atomic_load(a.state, __ATOMIC_ACQUIRE,
+                                                    __HIP_MEMORY_SCOPE_AGENT)
+                                : a.first_step;
+    __syncthreads();
+    const uint64_t first = sh.value;
+    __syncthreads();
     const int64_t s0 = (int64_t)c * a.total_steps / a.channels;
     const int64_t s1 = (int64_t)(c + 1) * a.total_steps / a.channels;
-    if (b < a.channels)
-        produce<PROTO>(a, c, s0, s1 - s0, &verdict);
+    if (producer) {
+        produce<PROTO>(a, c, s0, s1 - s0, first, &sh);
+        return;
+    }
+    if (PROTO == 0)
+        consume_ll<LOCAL>(a, c, s0, s1 - s0, first);
+    else if (PROTO == 1)
+        consume_ll128<LOCAL>(a, c, s0, s1 - s0, first, &sh);
     else
-        consume<PROTO>(a, c, s0, s1 - s0, &verdict);
+        consume_simple<LOCAL>(a, c, s0, s1 - s0, first, &sh);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint64_t done = __hip_atomic_fetch_add(a.state + 1, (uint64_t)1, __ATOMIC_ACQ_REL,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        if (done == (uint64_t)a.channels - 1) {
+            __hip_atomic_store(a.state + 1, (uint64_t)0, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.state, first + (uint64_t)a.steps_per_channel, __ATOMIC_RELEASE,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+static const void *stream_fn(int proto, bool local)
+{
+    if (local)
+        return proto == 0   ? reinterpret_cast<const void *>(&stream_kernel<0, true>)
+               : proto == 1 ? reinterpret_cast<const void *>(&stream_kernel<1, true>)
+                            : reinterpret_cast<const void *>(&stream_kernel<2, true>);
+    return proto == 0   ? reinterpret_cast<const void *>(&stream_kernel<0, false>)
+           : proto == 1 ? reinterpret_cast<const void *>(&stream_kernel<1, false>)
+                        : reinterpret_cast<const void *>(&stream_kernel<2, false>);
+}
+
+hipError_t fifo_stream_resident_workgroups(int proto, bool local, int *workgroups)
+{
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stream_fn(proto, local),
+                                                         kStreamThreads, 0);
+    *workgroups = e == hipSuccess ? cus * per_cu : 0;
+    return e;
 }
 
 hipError_t launch_fifo_stream(int proto, const float *src, const float *local, float *out,
                               int64_t n, void *fifo, uint64_t *counters, int channels,
                               int64_t step_bytes, int64_t wire_bytes, uint64_t first_step,
-                              uint32_t max_spins, uint32_t *errors, hipStream_t s)
+                              bool from_state, uint32_t max_spins, uint32_t *errors,
+                              hipStream_t s)
 {
     StreamArgs a;
     a.src = reinterpret_cast<const uint32_t *>(src);
@@ -303,18 +758,19 @@ hipError_t launch_fifo_stream(int proto, const float *src, const float *local, f
     a.fifo = static_cast<uint8_t *>(fifo);
     a.head = counters;
     a.tail = counters + channels;
+    a.state = counters + 2 * channels;
     a.errors = errors;
     a.step_bytes = step_bytes;
     a.wire_bytes = wire_bytes;
     a.total_steps = (4 * n + step_bytes - 1) / step_bytes;
+    a.steps_per_channel = (a.total_steps + channels - 1) / channels;
     a.channels = channels;
+    a.from_state = from_state ? 1 : 0;
     a.first_step = first_step;
     a.max_spins = max_spins;
     void *args[] = {&a};
-    const void *fn = proto == 0   ? reinterpret_cast<const void *>(&stream_kernel<0>)
-                     : proto == 1 ? reinterpret_cast<const void *>(&stream_kernel<1>)
-                                  : reinterpret_cast<const void *>(&stream_kernel<2>);
-    return hipLaunchCooperativeKernel(fn, dim3(2 * channels), dim3(kStreamThreads), args, 0, s);
+    return hipLaunchKernel(stream_fn(proto, local != nullptr), dim3(2 * channels),
+                           dim3(kStreamThreads), args, 0, s);
 }
 
 }  // namespace ar

@@ -37,9 +37,11 @@ EXPORTS = (
     "ll128_unpack_reduce", "ll_lines", "ll128_lines", "ll_fifo_bytes",
     "ll128_fifo_bytes", "ll_default_step_lines", "ll128_default_step_lines",
     "ar_fifo_stream", "ar_fifo_step_wire_bytes", "ar_fifo_steps_per_channel",
+    "ar_fifo_counter_words",
 )
 AR_PROTO_LL, AR_PROTO_LL128, AR_PROTO_SIMPLE = 0, 1, 2
 AR_FIFO_MAX_CHANNELS = 128
+AR_FIFO_CONTINUE = (1 << 64) - 1
 
 _vp, _i64, _u64, _u32, _int = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
                                ctypes.c_uint32, ctypes.c_int)
@@ -90,6 +92,8 @@ _lib.ar_fifo_step_wire_bytes.argtypes = [_int, _i64]
 _lib.ar_fifo_step_wire_bytes.restype = _i64
 _lib.ar_fifo_steps_per_channel.argtypes = [_i64, _i64, _int]
 _lib.ar_fifo_steps_per_channel.restype = _i64
+_lib.ar_fifo_counter_words.argtypes = [_int]
+_lib.ar_fifo_counter_words.restype = _i64
 
 
 class ArError(RuntimeError):
@@ -283,11 +287,16 @@ def ar_fifo_steps_per_channel(n: int, step_bytes: int, channels: int) -> int:
     return _lib.ar_fifo_steps_per_channel(n, step_bytes, channels)
 
 
+def ar_fifo_counter_words(channels: int) -> int:
+    return _lib.ar_fifo_counter_words(channels)
+
+
 def ar_fifo_stream(proto: int, src, out, fifo, counters, channels: int, step_bytes: int,
                    first_step: int = 0, max_spins: int = AR_MAX_SPINS, errors=None,
                    local=None, n: Optional[int] = None, stream=None) -> None:
-    """Stream src through `channels` 8-slot rings (one cooperative launch of
-    producers and consumers) into out (= src, or local + src)."""
+    """Stream src through `channels` 8-slot rings (one launch of producer and
+    consumer workgroups) into out (= src, or local + src).  first_step may be
+    AR_FIFO_CONTINUE: start from the step stored in counters by the last call."""
     _check(_lib.ar_fifo_stream(proto, _addr(src), _addr(local), _addr(out), _numel(src, n),
                                _addr(fifo), _addr(counters), channels, step_bytes, first_step,
                                max_spins, _addr(errors), _stream(stream)), "ar_fifo_stream")

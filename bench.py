@@ -458,6 +458,60 @@ def main():
                 del hfifos
             del payloads
             torch.cuda.empty_cache()
+
+        # streaming through 8-step FIFOs (one launch of producer and consumer
+        # workgroups per call): the 16 Mi fp32 wire payload at NCCL's default
+        # step sizes, and a one-step 8 KiB message.  Each call starts from the
+        # step the previous call stored in the counters, so graph replays run
+        # fresh ring steps; the cold src/out sets rotate while the rings stay.
+        def ring_written(proto, n_msg, step):
+            """Ring bytes the producers write for one call: whole steps, then
+            the last step's payload-carrying lines (LL 8 -> 16 bytes, LL128
+            120 -> 128 bytes, Simple raw)."""
+            def wire_of(nb):
+                if proto == ar.AR_PROTO_LL:
+                    return -(-nb // 8) * 16
+                if proto == ar.AR_PROTO_LL128:
+                    return -(-nb // 120) * 128
+                return nb
+            T = -(-4 * n_msg // step)
+            return (T - 1) * wire_of(step) + wire_of(4 * n_msg - (T - 1) * step)
+
+        nn = wc["n"]
+        host_src = synth.wire(nn)[0]
+        dsrc = torch.from_numpy(host_src).to(dev)
+        ss = []
+        for k in range(sets_for(8 * nn)):
+            ss.append((dsrc if k == 0 else dsrc.clone(),
+                       torch.empty(nn, dtype=torch.float32, device=dev)))
+        for fmt, proto, step in (("ll", ar.AR_PROTO_LL, 32768),
+                                 ("ll128", ar.AR_PROTO_LL128, 576000),
+                                 ("simple", ar.AR_PROTO_SIMPLE, 524288)):
+            for ch, n_msg in ((32, nn), (128, nn), (1, 2048)):
+                wire = ar.ar_fifo_step_wire_bytes(proto, step)
+                fifo = torch.zeros(ch * 8 * wire, dtype=torch.uint8, device=dev)
+                cnt = torch.zeros(ar.ar_fifo_counter_words(ch), dtype=torch.int64, device=dev)
+                errs = torch.zeros(1, dtype=torch.int32, device=dev)
+                ring_bytes = ring_written(proto, n_msg, step)
+                calls = [(lambda q=q, proto=proto, step=step, ch=ch, fifo=fifo, cnt=cnt,
+                          errs=errs, n_msg=n_msg:
+                          ar.ar_fifo_stream(proto, q[0], q[1], fifo, cnt, ch, step,
+                                            ar.AR_FIFO_CONTINUE, errors=errs, n=n_msg))
+                         for q in ss]
+                r = row(f"stream_{fmt}_n{n_msg}_step{step}_c{ch}", 8 * n_msg, calls,
+                        steps=8 * len(ss) if n_msg == nn else 200,
+                        oracle_fn=orc and n_msg == nn and ch == 32 and
+                        (lambda proto=proto, step=step: orc.fifo_stream(proto, host_src, 32, step))
+                        or None)
+                t_s = r["us_per_call"] * 1e-6
+                torch.cuda.synchronize()
+                r.update({"channels": ch,
+                          "step_bytes": step, "payload_GBps": round(4 * n_msg / t_s / 1e9, 1),
+                          "ring_bytes": 2 * ring_bytes,
+                          "failed_waits": int(errs.item())})
+                del fifo, cnt, calls
+        del ss, dsrc
+        torch.cuda.empty_cache()
         result["rows"] = rows
 
     if args.calib_copy:

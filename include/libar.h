@@ -334,13 +334,14 @@ ar_status_t ll128_unpack_reduce(const void *const *fifos, int W, float *out,
  * steps are dealt to `channels` channels in contiguous runs (channel c takes
  * steps [c*T/channels, (c+1)*T/channels)).  Each channel has an 8-slot ring
  * and a producer and a consumer workgroup that run concurrently in one
- * cooperative launch.  Local step j of a channel is ring step
- * k = first_step + j, in slot k mod 8:
+ * launch.  Local step j of a channel is ring step k = first + j, in slot
+ * k mod 8:
  *   AR_PROTO_LL      16-byte lines of 8 payload bytes + two 32-bit flags
  *                    (k + 1), ready when both flags match
- *   AR_PROTO_LL128   128-byte lines of 120 payload bytes + a 64-bit flag;
- *                    the producer writes a step's data, fences, then its
- *                    flags; the consumer re-reads a line after validating it
+ *   AR_PROTO_LL128   128-byte lines of 120 payload bytes + a 64-bit flag
+ *                    (k + 1); the producer writes a step's data, fences,
+ *                    then its flags; the consumer acquires one flag of the
+ *                    step, then reads every line and checks its flag
  *   AR_PROTO_SIMPLE  raw payload; ready when the channel's tail counter
  *                    reaches k + 1
  * After each step the consumer sets the channel's head counter to k + 1; the
@@ -352,12 +353,17 @@ ar_status_t ll128_unpack_reduce(const void *const *fifos, int W, float *out,
  *               2^30 (NCCL's defaults: 32768 / 576000 / 524288)
  *   fifo        channels * 8 * ar_fifo_step_wire_bytes(proto, step_bytes)
  *               bytes, 16-byte aligned (128 for LL128)
- *   counters    2 * channels u64 (heads, then tails), 8-byte aligned
+ *   counters    ar_fifo_counter_words(channels) u64, 8-byte aligned: the
+ *               heads, the tails, then {stored first step, finished
+ *               consumers}.  Zero fifo and counters together before the
+ *               first call on them.
  *   channels    1..AR_FIFO_MAX_CHANNELS
- *   first_step  0 with fifo and counters zeroed; a later call on the same
- *               fifo and counters continues with first_step advanced by
- *               ar_fifo_steps_per_channel(n, step_bytes, channels) of the
- *               previous call (flags and counters only ever grow)
+ *   first_step  the first ring step of every channel, or AR_FIFO_CONTINUE
+ *               for the stored first step.  Each call ends by storing
+ *               first + ar_fifo_steps_per_channel(n, step_bytes, channels),
+ *               so calls with AR_FIFO_CONTINUE (also from a replayed graph)
+ *               keep flags and counters growing.  Explicit values must not
+ *               go below the stored step on fifo/counters in use.
  *   max_spins   bound on every wait (<= AR_MAX_SPINS); a wait that runs out
  *               adds 1 to errors[0] and makes every other wait of the launch
  *               give up, so the launch always ends
@@ -365,19 +371,26 @@ ar_status_t ll128_unpack_reduce(const void *const *fifos, int W, float *out,
  *               is unspecified and fifo/counters must be zeroed before reuse
  *   src, local, out  n fp32, 4-byte aligned; out may equal local, no other
  *               overlap among the buffers                 else AR_ERR_ARG
- * AR_ERR_HIP if the runtime cannot make all 2 * channels workgroups
- * resident at once.
+ * The 2 * channels workgroups must be resident together: AR_ERR_CAPACITY if
+ * the device cannot hold them at once.  Work from other streams that holds
+ * compute units while a call runs can delay a consumer or producer; the
+ * bounded waits then end the launch with errors[0] != 0.
  */
 #define AR_PROTO_LL 0
 #define AR_PROTO_LL128 1
 #define AR_PROTO_SIMPLE 2
 #define AR_FIFO_MAX_CHANNELS 128
+#define AR_FIFO_CONTINUE UINT64_MAX
 
 ar_status_t ar_fifo_stream(int proto, const float *src, const float *local,
                            float *out, int64_t n, void *fifo, uint64_t *counters,
                            int channels, int64_t step_bytes, uint64_t first_step,
                            uint32_t max_spins, uint32_t *errors,
                            ar_stream_t stream);
+
+/* u64 words of the counters of `channels` channels: 2 * channels + 2
+ * (0 if channels is out of range). */
+int64_t ar_fifo_counter_words(int channels);
 
 /* Ring bytes per step for a protocol (0 if step_bytes is not valid). */
 int64_t ar_fifo_step_wire_bytes(int proto, int64_t step_bytes);

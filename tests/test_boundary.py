@@ -157,3 +157,44 @@ def test_wire_argument_errors():
     assert st(u, [A], C, 1, 0, 0, C + 4, 8, 0) == ar.AR_ERR_ARG         # counter in out
     assert st(ar.ll128_unpack_reduce, [A + 16], C, 1, 0, 0, None, 8, 0) == ar.AR_ERR_ALIGN
     assert st(u, [A], C, 1, 0, 0, None, 0, 0) == ar.AR_OK
+
+
+def test_stream_geometry_helpers():
+    # NCCL's default steps: LL 32768 payload bytes in 4096 16-byte lines, LL128
+    # 576000 in 4800 128-byte lines, Simple 524288 raw
+    assert ar.ar_fifo_step_wire_bytes(ar.AR_PROTO_LL, 32768) == 65536
+    assert ar.ar_fifo_step_wire_bytes(ar.AR_PROTO_LL128, 576000) == 4800 * 128
+    assert ar.ar_fifo_step_wire_bytes(ar.AR_PROTO_SIMPLE, 524288) == 524288
+    for proto, bad in ((ar.AR_PROTO_LL, 12), (ar.AR_PROTO_LL128, 1000),
+                       (ar.AR_PROTO_SIMPLE, 24), (3, 1024), (ar.AR_PROTO_LL, 0),
+                       (ar.AR_PROTO_LL, (1 << 30) + 8)):
+        assert ar.ar_fifo_step_wire_bytes(proto, bad) == 0
+    # 16 Mi fp32 at 32 KiB steps: 2048 steps; 13 more values need one more
+    assert ar.ar_fifo_steps_per_channel(16_777_216, 32768, 32) == 64
+    assert ar.ar_fifo_steps_per_channel(16_777_229, 32768, 32) == 65
+    assert ar.ar_fifo_steps_per_channel(2048, 32768, 32) == 1
+    assert ar.ar_fifo_steps_per_channel(0, 32768, 4) == 0
+    assert [ar.ar_fifo_counter_words(c) for c in (0, 1, 128, 129)] == [0, 4, 258, 0]
+    assert ar.AR_FIFO_CONTINUE == (1 << 64) - 1
+
+
+@cpu_only
+def test_stream_argument_errors():
+    f = ar.ar_fifo_stream
+    LL, LL128 = ar.AR_PROTO_LL, ar.AR_PROTO_LL128
+    assert st(f, LL, None, B, C, D, 2, 1024, 0, 8, E, None, 8, 0) == ar.AR_ERR_NULL
+    assert st(f, LL, A, B, C, D, 2, 1024, 0, 8, None, None, 8, 0) == ar.AR_ERR_NULL
+    assert st(f, LL, A, B, C, D, 0, 1024, 0, 8, E, None, 8, 0) == ar.AR_ERR_ARG
+    assert st(f, LL, A, B, C, D, 129, 1024, 0, 8, E, None, 8, 0) == ar.AR_ERR_ARG
+    assert st(f, LL, A, B, C, D, 2, 1020, 0, 8, E, None, 8, 0) == ar.AR_ERR_ARG
+    assert st(f, LL, A, B, C, D, 2, 1024, 0, ar.AR_MAX_SPINS + 1, E, None, 8, 0) == ar.AR_ERR_ARG
+    assert st(f, LL, A + 2, B, C, D, 2, 1024, 0, 8, E, None, 8, 0) == ar.AR_ERR_ALIGN
+    assert st(f, LL128, A, B, C + 64, D, 2, 1200, 0, 8, E, None, 8, 0) == ar.AR_ERR_ALIGN
+    assert st(f, LL, A, B, C, D + 4, 2, 1024, 0, 8, E, None, 8, 0) == ar.AR_ERR_ALIGN
+    assert st(f, LL, A, A + 16, C, D, 2, 1024, 0, 8, E, None, 8, 0) == ar.AR_ERR_ARG
+    assert st(f, LL, A, B, C, D, 2, 1024, 0, 8, E, B + 4, 8, 0) == ar.AR_ERR_ARG   # local partial
+    assert st(f, LL, A, B, C, C + 64, 2, 1024, 0, 8, E, None, 8, 0) == ar.AR_ERR_ARG  # counters
+    # the two state words follow the 2 * channels heads and tails
+    assert st(f, LL, A, B, C, D, 2, 1024, 0, 8, D + 40, None, 8, 0) == ar.AR_ERR_ARG
+    assert st(f, LL, A, B, C, D, 2, 1024, 0, 8, D + 48, None, 0, 0) == ar.AR_OK
+    assert st(f, LL, A, B, C, D, 2, 1024, 0, 8, E, None, 0, 0) == ar.AR_OK       # n = 0

@@ -21,24 +21,28 @@ def sync():
 
 
 class Fifo:
+    """One set of rings and counters, with the oracle's copy of the rings and
+    the first step the next call starts from."""
+
     def __init__(self, proto, step, channels, device):
-        self.proto, self.step, self.channels = proto, step, channels
+        self.proto, self.step, self.channels, self.device = proto, step, channels, device
         wire = ar.ar_fifo_step_wire_bytes(proto, step)
         assert wire > 0
         self.fifo = torch.zeros(channels * 8 * wire, dtype=torch.uint8, device=device)
-        self.counters = torch.zeros(2 * channels, dtype=torch.int64, device=device)
+        self.counters = torch.zeros(ar.ar_fifo_counter_words(channels), dtype=torch.int64,
+                                    device=device)
         self.errors = torch.zeros(1, dtype=torch.int32, device=device)
         self.host = np.zeros(channels * 8 * wire, np.uint8)
         self.first = 0
 
-    def run(self, src, local=None, max_spins=ar.AR_MAX_SPINS):
-        n = src.size
-        d = torch.from_numpy(src).to(self.fifo.device)
-        dl = None if local is None else torch.from_numpy(local).to(self.fifo.device)
-        out = torch.full((n + 16,), 777.0, dtype=torch.float32, device=self.fifo.device)
+    def launch(self, d, out, n, dl=None, cont=False, max_spins=ar.AR_MAX_SPINS):
         ar.ar_fifo_stream(self.proto, d, out, self.fifo, self.counters, self.channels, self.step,
-                          self.first, max_spins, self.errors, local=dl, n=n)
-        sync()
+                          ar.AR_FIFO_CONTINUE if cont else self.first, max_spins, self.errors,
+                          local=dl, n=n)
+
+    def check(self, src, out, local=None):
+        """Compare a finished call with the oracle and advance the step."""
+        n = src.size
         got = out.cpu().numpy()
         assert np.all(got[n:] == 777.0), "wrote past n"
         want, self.host = orc.fifo_stream(self.proto, src, self.channels, self.step, self.first,
@@ -47,6 +51,17 @@ class Fifo:
         assert np.array_equal(got[:n].view(np.uint32), want.view(np.uint32)), "payload"
         assert np.array_equal(self.fifo.cpu().numpy(), self.host), "ring bytes"
         self.first += ar.ar_fifo_steps_per_channel(n, self.step, self.channels)
+        state = self.counters.cpu().numpy()[2 * self.channels:]
+        assert state[0] == self.first and state[1] == 0, "stored step"
+
+    def run(self, src, local=None, cont=False, max_spins=ar.AR_MAX_SPINS):
+        n = src.size
+        d = torch.from_numpy(src).to(self.device)
+        dl = None if local is None else torch.from_numpy(local).to(self.device)
+        out = torch.full((n + 16,), 777.0, dtype=torch.float32, device=self.device)
+        self.launch(d, out, n, dl, cont, max_spins)
+        sync()
+        self.check(src, out, local)
 
 
 @pytest.mark.parametrize("name,step", [("ll", 1024), ("ll128", 1200), ("simple", 1024)])
@@ -69,11 +84,44 @@ def test_stream_nccl_default_steps_wire_workload(gpu, name, step, channels):
 
 @pytest.mark.parametrize("name,step", [("ll", 2048), ("ll128", 2400), ("simple", 2048)])
 def test_stream_reduce_with_local_and_consecutive_calls(gpu, name, step):
+    """Calls on one set of rings: explicit first steps, then the stored one."""
     f = Fifo(PROTOS[name], step, 8, gpu)
-    for call in range(3):
+    for call in range(4):
         n = 8 * 13 * step // 4 + 7 * call + 1
         src, local = synth.wire_payloads(2, n, [103, call])
-        f.run(src, local=local if call != 1 else None)
+        f.run(src, local=local if call != 1 else None, cont=call >= 2)
+
+
+@pytest.mark.parametrize("name,step,channels", [("ll", 1024, 3), ("ll128", 1200, 4),
+                                                ("simple", 2048, 5)])
+def test_stream_graph_replays_continue(gpu, name, step, channels):
+    """A captured call with the stored first step, replayed: every replay
+    runs a fresh range of ring steps (flags never repeat) and matches the
+    oracle, with eager calls between replays."""
+    f = Fifo(PROTOS[name], step, channels, gpu)
+    n = channels * 11 * step // 4 + 5
+    src = synth.wire_payloads(1, n, [104, channels])[0]
+    d = torch.from_numpy(src).to(gpu)
+    out = torch.full((n + 16,), 777.0, dtype=torch.float32, device=gpu)
+    f.launch(d, out, n, cont=True)
+    sync()
+    f.check(src, out)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        f.launch(d, out, n, cont=True)
+    torch.cuda.current_stream().wait_stream(s)
+    sync()
+    for r in range(3):
+        out[:n].zero_()
+        sync()
+        g.replay()
+        sync()
+        f.check(src, out)
+        other = synth.wire_payloads(1, n - r, [105, r])[0]      # eager call between replays
+        f.run(other, cont=True)
+    del g
 
 
 def test_stream_aborted_launch_ends(gpu):
@@ -86,6 +134,11 @@ def test_stream_aborted_launch_ends(gpu):
     src = torch.zeros(n, dtype=torch.float32, device=gpu)
     out = torch.empty_like(src)
     ar.ar_fifo_stream(proto, src, out, f.fifo, f.counters, channels, step, 0, 64, f.errors)
+    sync()
+    for p in (ar.AR_PROTO_LL128, ar.AR_PROTO_SIMPLE):
+        g = Fifo(p, 1200 if p == ar.AR_PROTO_LL128 else 1024, channels, gpu)
+        g.errors.fill_(1)
+        ar.ar_fifo_stream(p, src, out, g.fifo, g.counters, channels, g.step, 0, 64, g.errors)
     sync()
     assert int(f.errors.item()) >= 1
 
@@ -110,4 +163,8 @@ def test_stream_argument_errors(gpu):
         ar.ar_fifo_stream(ar.AR_PROTO_LL128, src, src, f.fifo, f.counters, 2, 1200, 0, 100,
                           f.errors)
     assert e.value.status == ar.AR_ERR_ARG      # out overlaps src
+    with pytest.raises(ar.ArError) as e:
+        ar.ar_fifo_stream(ar.AR_PROTO_LL128, src, out, f.fifo, f.counters, 2, 1200, 0, 100,
+                          out[:1].view(torch.int32))
+    assert e.value.status == ar.AR_ERR_ARG      # errors inside out
     sync()
