@@ -228,10 +228,17 @@ __device__ __forceinline__ void deliver(const StreamArgs &a, int64_t w, int cnt,
 }
 
 // ---------------------------------------------------------------------------
-// Steps and batches.  Items are LL lines, LL128 line chunks (line q / 8,
-// chunk q % 8: chunks 0..6 carry 16 payload bytes, chunk 7 carries 8 payload
-// bytes and then the flag) or Simple 16-byte chunks.  A batch is kBatch items
-// per lane: items base + u * kStreamThreads + threadIdx.x, u < kBatch.
+// Steps and batches.  Items are LL lines, LL128 line chunks or Simple
+// 16-byte chunks.  A batch is kBatch items per lane: items
+// base + u * kStreamThreads + threadIdx.x, u < kBatch.
+//
+// LL128 item q is chunk q % 8 of line q / 8 (chunks 0..6 carry 16 payload
+// bytes, chunk 7 carries 8 payload bytes and then the flag).  Sixteen
+// consecutive items, one DPP row, cover a pair of lines, whose 240 payload
+// bytes are 15 aligned 16-byte payload chunks: lane c < 15 of the row moves
+// payload chunk c with one whole dwordx4 load or store, and the 8-byte shift
+// between the second line's chunks and the payload chunks is done across
+// lanes with DPP row shifts.
 struct Step {
     uint8_t *slot;
     int64_t w0;       // first payload word
@@ -306,6 +313,13 @@ __device__ __forceinline__ int64_t ring_offset(int64_t i)
 }
 
 // Source words of a batch (zero for items past the step).
+// Payload word of lane c's 16-byte payload chunk in the LL128 line pair
+// holding item q.
+__device__ __forceinline__ int64_t pair_chunk_word(const Step &g, int64_t q)
+{
+    return g.w0 + 60 * (q >> 4) + 4 * (q & 15);
+}
+
 template <int PROTO>
 __device__ __forceinline__ void load_src(const StreamArgs &a, const Step &g, int64_t base,
                                          u32x4 d[kBatch])
@@ -314,7 +328,12 @@ __device__ __forceinline__ void load_src(const StreamArgs &a, const Step &g, int
     for (int u = 0; u < kBatch; ++u) {
         const int64_t i = base + (int64_t)u * kStreamThreads + threadIdx.x;
         d[u] = u32x4{0u, 0u, 0u, 0u};
-        if (i < g.items) {
+        if (PROTO == 1) {
+            // payload chunk i % 16 of the pair (lane 15 has none); words past
+            // the step belong to lines this step does not write
+            if (i < g.items && (i & 15) < 15)
+                d[u] = quad_at(a, pair_chunk_word(g, i));
+        } else if (i < g.items) {
             const int64_t w = item_word<PROTO>(g, i);
             if (item_count<PROTO>(g, i) == 2) {
                 const u32x2 p = pair_at(a, w);
@@ -326,12 +345,29 @@ __device__ __forceinline__ void load_src(const StreamArgs &a, const Step &g, int
     }
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t row_shift(uint32_t v)
+{
+    // lanes whose source lies outside their row of 16 receive 0
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kRowShr1 = 0x111;   // lane c receives lane c - 1
+constexpr int kRowShl1 = 0x101;   // lane c receives lane c + 1
+
 template <int PROTO>
 __device__ __forceinline__ void store_ring(const Step &g, int64_t base, const u32x4 d[kBatch])
 {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
         const int64_t i = base + (int64_t)u * kStreamThreads + threadIdx.x;
+        // LL128: the second line's chunk c - 8 is the high half of payload
+        // chunk c - 1 and the low half of payload chunk c (every lane takes
+        // part in the shift)
+        uint32_t hz = 0u, hw = 0u;
+        if (PROTO == 1) {
+            hz = row_shift<kRowShr1>(d[u].z);
+            hw = row_shift<kRowShr1>(d[u].w);
+        }
         if (i >= g.items)
             continue;
         uint8_t *p = g.slot + ring_offset<PROTO>(i);
@@ -339,10 +375,13 @@ __device__ __forceinline__ void store_ring(const Step &g, int64_t base, const u3
             const uint32_t f = (uint32_t)(g.k + 1);
             store16_sys(p, u32x4{d[u].x, f, d[u].y, f});
         } else if (PROTO == 1) {
-            if ((i & 7) < 7)
-                store16_sys(p, d[u]);
-            else
-                store8_sys(p, u32x2{d[u].x, d[u].y});
+            // chunk 7 goes out whole with a zero flag word (no step's flag is
+            // 0), so each line is written by one full-line store
+            const int c = (int)(i & 15);
+            store16_sys(p, c < 7    ? d[u]
+                           : c == 7 ? u32x4{d[u].x, d[u].y, 0u, 0u}
+                           : c < 15 ? u32x4{hz, hw, d[u].x, d[u].y}
+                                    : u32x4{hz, hw, 0u, 0u});
         } else if (4 * i + 4 <= g.words) {
             store16_sys(p, d[u]);
         } else {
@@ -363,6 +402,14 @@ __device__ __forceinline__ void load_ring(const Step &g, int64_t base, u32x4 v[k
     }
 }
 
+// LL128 delivery: lane c < 15 of a line pair owns payload chunk c; the step's
+// payload words past the last line of the step are not written.
+__device__ __forceinline__ int pair_chunk_count(const Step &g, int64_t q)
+{
+    const int64_t rem = g.words - (60 * (q >> 4) + 4 * (q & 15));
+    return (q & 15) == 15 || rem <= 0 ? 0 : rem < 4 ? (int)rem : 4;
+}
+
 template <int PROTO, bool LOCAL>
 __device__ __forceinline__ void load_local(const StreamArgs &a, const Step &g, int64_t base,
                                            u32x4 lv[kBatch])
@@ -371,8 +418,14 @@ __device__ __forceinline__ void load_local(const StreamArgs &a, const Step &g, i
     for (int u = 0; u < kBatch; ++u) {
         const int64_t i = base + (int64_t)u * kStreamThreads + threadIdx.x;
         lv[u] = u32x4{0u, 0u, 0u, 0u};
-        if (LOCAL && i < g.items)
+        if (!LOCAL || i >= g.items)
+            continue;
+        if (PROTO == 1) {
+            if (pair_chunk_count(g, i) > 0)
+                lv[u] = local_at(a, pair_chunk_word(g, i), 4);
+        } else {
             lv[u] = local_at(a, item_word<PROTO>(g, i), item_count<PROTO>(g, i));
+        }
     }
 }
 
@@ -383,6 +436,23 @@ __device__ __forceinline__ void deliver_batch(const StreamArgs &a, const Step &g
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
         const int64_t i = base + (int64_t)u * kStreamThreads + threadIdx.x;
+        if (PROTO == 1) {
+            // payload chunk c: line A's chunk c (c < 7); line A's chunk 7
+            // data then line B's chunk 0 low half (c == 7); line B's chunk
+            // c - 8 high half then chunk c - 7 low half (8 <= c < 15)
+            const uint32_t nx = row_shift<kRowShl1>(v[u].x);
+            const uint32_t ny = row_shift<kRowShl1>(v[u].y);
+            if (i >= g.items)
+                continue;
+            const int c = (int)(i & 15);
+            const int cnt = pair_chunk_count(g, i);
+            if (cnt == 0)
+                continue;
+            const u32x4 x = c < 7 ? v[u] : c == 7 ? u32x4{v[u].x, v[u].y, nx, ny}
+                                                  : u32x4{v[u].z, v[u].w, nx, ny};
+            deliver<LOCAL>(a, pair_chunk_word(g, i), cnt, x, lv[u]);
+            continue;
+        }
         if (i >= g.items)
             continue;
         const u32x4 x = PROTO == 0 ? u32x4{v[u].x, v[u].z, 0u, 0u} : v[u];

@@ -52,7 +52,8 @@ def parse():
     p.add_argument("--steps", type=int, default=240)
     p.add_argument("--warmup", type=int, default=24)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--rows", choices=["all", "none"], default="all")
+    p.add_argument("--rows", choices=["all", "none", "stream"], default="all",
+                   help="which rows besides the headline: all, none, or only the streaming rows")
     p.add_argument("--eager", action="store_true",
                    help="time eager launches instead of a HIP graph replay")
     p.add_argument("--calib-copy", action="store_true",
@@ -459,6 +460,9 @@ def main():
             del payloads
             torch.cuda.empty_cache()
 
+
+    if args.rows in ("all", "stream"):
+        wc = synth.WIRE
         # streaming through 8-step FIFOs (one launch of producer and consumer
         # workgroups per call): the 16 Mi fp32 wire payload at NCCL's default
         # step sizes, and a one-step 8 KiB message.  Each call starts from the
@@ -498,7 +502,10 @@ def main():
                           ar.ar_fifo_stream(proto, q[0], q[1], fifo, cnt, ch, step,
                                             ar.AR_FIFO_CONTINUE, errors=errs, n=n_msg))
                          for q in ss]
-                r = row(f"stream_{fmt}_n{n_msg}_step{step}_c{ch}", 8 * n_msg, calls,
+                # bytes the launch moves: payload read, ring written and read,
+                # output written
+                r = row(f"stream_{fmt}_n{n_msg}_step{step}_c{ch}", 8 * n_msg + 2 * ring_bytes,
+                        calls,
                         steps=8 * len(ss) if n_msg == nn else 200,
                         oracle_fn=orc and n_msg == nn and ch == 32 and
                         (lambda proto=proto, step=step: orc.fifo_stream(proto, host_src, 32, step))
@@ -507,11 +514,46 @@ def main():
                 torch.cuda.synchronize()
                 r.update({"channels": ch,
                           "step_bytes": step, "payload_GBps": round(4 * n_msg / t_s / 1e9, 1),
-                          "ring_bytes": 2 * ring_bytes,
+                          "ring_bytes_written": ring_bytes,
                           "failed_waits": int(errs.item())})
                 del fifo, cnt, calls
+        # message-size sweep at 32 channels: where LL, LL128 and Simple cross.
+        # The step is NCCL's default, cut down to the message's share per
+        # channel (rounded up to the protocol's unit) so that a mid-size
+        # message spreads over all channels rather than filling one step.
+        xo = {}
+        for size in (1 << 13, 1 << 16, 1 << 19, 1 << 22, 1 << 25):
+            n_msg = size // 4
+            xo[str(size)] = {}
+            for fmt, proto, default_step, unit in (("ll", ar.AR_PROTO_LL, 32768, 8),
+                                                   ("ll128", ar.AR_PROTO_LL128, 576000, 120),
+                                                   ("simple", ar.AR_PROTO_SIMPLE, 524288, 16)):
+                ch = 32
+                share = -(-(-(-size // ch)) // unit) * unit
+                step = min(default_step, share)
+                wire = ar.ar_fifo_step_wire_bytes(proto, step)
+                fifo = torch.zeros(ch * 8 * wire, dtype=torch.uint8, device=dev)
+                cnt = torch.zeros(ar.ar_fifo_counter_words(ch), dtype=torch.int64, device=dev)
+                errs = torch.zeros(1, dtype=torch.int32, device=dev)
+                calls = [(lambda q=q, proto=proto, step=step, fifo=fifo, cnt=cnt, errs=errs,
+                          n_msg=n_msg:
+                          ar.ar_fifo_stream(proto, q[0], q[1], fifo, cnt, 32, step,
+                                            ar.AR_FIFO_CONTINUE, errors=errs, n=n_msg))
+                         for q in ss]
+                k = 8 * len(ss) if size >= (1 << 22) else 40 * len(ss)
+                t = graph_time(calls, k, args.warmup)
+                torch.cuda.synchronize()
+                xo[str(size)][fmt] = round(t * 1e3, 3)
+                xo[str(size)][fmt + "_step"] = step
+                if int(errs.item()) != 0:
+                    xo[str(size)][fmt + "_failed_waits"] = int(errs.item())
+                del fifo, cnt, calls
+            log(f"stream sweep {size} B at 32 channels: {xo[str(size)]} us")
+        rows["stream_sizes_c32_us_per_call"] = xo
         del ss, dsrc
         torch.cuda.empty_cache()
+
+    if args.rows != "none":
         result["rows"] = rows
 
     if args.calib_copy:

@@ -379,7 +379,7 @@ ar_status_t ll128_unpack_reduce(const void *const *fifos, int W, float *out,
 #define AR_PROTO_LL 0
 #define AR_PROTO_LL128 1
 #define AR_PROTO_SIMPLE 2
-#define AR_FIFO_MAX_CHANNELS 128
+#define AR_FIFO_MAX_CHANNELS 256
 #define AR_FIFO_CONTINUE UINT64_MAX
 
 ar_status_t ar_fifo_stream(int proto, const float *src, const float *local,

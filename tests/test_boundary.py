@@ -174,7 +174,7 @@ def test_stream_geometry_helpers():
     assert ar.ar_fifo_steps_per_channel(16_777_229, 32768, 32) == 65
     assert ar.ar_fifo_steps_per_channel(2048, 32768, 32) == 1
     assert ar.ar_fifo_steps_per_channel(0, 32768, 4) == 0
-    assert [ar.ar_fifo_counter_words(c) for c in (0, 1, 128, 129)] == [0, 4, 258, 0]
+    assert [ar.ar_fifo_counter_words(c) for c in (0, 1, 256, 257)] == [0, 4, 514, 0]
     assert ar.AR_FIFO_CONTINUE == (1 << 64) - 1
 
 
@@ -185,7 +185,7 @@ def test_stream_argument_errors():
     assert st(f, LL, None, B, C, D, 2, 1024, 0, 8, E, None, 8, 0) == ar.AR_ERR_NULL
     assert st(f, LL, A, B, C, D, 2, 1024, 0, 8, None, None, 8, 0) == ar.AR_ERR_NULL
     assert st(f, LL, A, B, C, D, 0, 1024, 0, 8, E, None, 8, 0) == ar.AR_ERR_ARG
-    assert st(f, LL, A, B, C, D, 129, 1024, 0, 8, E, None, 8, 0) == ar.AR_ERR_ARG
+    assert st(f, LL, A, B, C, D, 257, 1024, 0, 8, E, None, 8, 0) == ar.AR_ERR_ARG
     assert st(f, LL, A, B, C, D, 2, 1020, 0, 8, E, None, 8, 0) == ar.AR_ERR_ARG
     assert st(f, LL, A, B, C, D, 2, 1024, 0, ar.AR_MAX_SPINS + 1, E, None, 8, 0) == ar.AR_ERR_ARG
     assert st(f, LL, A + 2, B, C, D, 2, 1024, 0, 8, E, None, 8, 0) == ar.AR_ERR_ALIGN

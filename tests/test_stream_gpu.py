@@ -64,7 +64,8 @@ class Fifo:
         self.check(src, out, local)
 
 
-@pytest.mark.parametrize("name,step", [("ll", 1024), ("ll128", 1200), ("simple", 1024)])
+@pytest.mark.parametrize("name,step", [("ll", 1024), ("ll128", 1200), ("ll128", 840),
+                                       ("simple", 1024)])
 @pytest.mark.parametrize("channels", [1, 4, 16])
 def test_stream_many_laps(gpu, name, step, channels):
     """About 20 steps per channel (2.5 laps of the ring) and a ragged tail."""
@@ -82,7 +83,8 @@ def test_stream_nccl_default_steps_wire_workload(gpu, name, step, channels):
     Fifo(PROTOS[name], step, channels, gpu).run(src)
 
 
-@pytest.mark.parametrize("name,step", [("ll", 2048), ("ll128", 2400), ("simple", 2048)])
+@pytest.mark.parametrize("name,step", [("ll", 2048), ("ll128", 2400), ("ll128", 1080),
+                                       ("simple", 2048)])
 def test_stream_reduce_with_local_and_consecutive_calls(gpu, name, step):
     """Calls on one set of rings: explicit first steps, then the stored one."""
     f = Fifo(PROTOS[name], step, 8, gpu)
