@@ -532,10 +532,13 @@ __device__ bool close_step(const StreamArgs &a, int c, uint64_t k, bool failed)
     return !any_failed;
 }
 
-// Re-read the items whose check failed, all at once, until every check holds
-// (bounded; gives up early once any wait of the launch has failed).
-template <typename Reload, typename Check>
-__device__ bool poll_batch(const StreamArgs &a, bool ok[kBatch], Reload reload, Check check)
+// Wait until every item of a batch is valid (bounded; gives up early once
+// any wait of the launch has failed).  While items are missing, only the
+// earliest of them is polled, since the producer stores a lane's items in
+// that order; once it is valid the missing items are all read again.
+template <typename Addr, typename Valid>
+__device__ bool poll_batch(const StreamArgs &a, u32x4 v[kBatch], bool ok[kBatch], Addr addr,
+                           Valid valid)
 {
     bool all = true;
 #pragma unroll
@@ -544,14 +547,21 @@ __device__ bool poll_batch(const StreamArgs &a, bool ok[kBatch], Reload reload, 
     for (uint32_t s = 0; !all && s < a.max_spins; ++s) {
         if (s % kAbortCheck == 0 && aborted(a.errors))
             break;
+        int lead = 0;
+#pragma unroll
+        for (int u = kBatch - 1; u >= 0; --u)
+            if (!ok[u])
+                lead = u;
+        if (!valid(load16_sys(addr(lead))))
+            continue;
 #pragma unroll
         for (int u = 0; u < kBatch; ++u)
             if (!ok[u])
-                reload(u);
+                v[u] = load16_sys(addr(u));
         all = true;
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            ok[u] = ok[u] || check(u);
+            ok[u] = ok[u] || valid(v[u]);
             all = all && ok[u];
         }
     }
@@ -578,18 +588,16 @@ __device__ void consume_ll(const StreamArgs &a, int c, int64_t s0, int64_t steps
     for (;;) {
         const uint32_t flag = (uint32_t)(cur.g.k + 1);
         const int64_t i0 = cur.base + threadIdx.x;
-        auto check = [&](int u) { return v[u].y == flag && v[u].w == flag; };
+        auto valid = [&](u32x4 x) { return x.y == flag && x.w == flag; };
         bool ok[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u)
-            ok[u] = i0 + (int64_t)u * kStreamThreads >= cur.g.items || check(u);
+            ok[u] = i0 + (int64_t)u * kStreamThreads >= cur.g.items || valid(v[u]);
         if (!failed)
             failed = !poll_batch(
-                a, ok,
-                [&](int u) {
-                    v[u] = load16_sys(cur.g.slot + 16 * (i0 + (int64_t)u * kStreamThreads));
-                },
-                check);
+                a, v, ok,
+                [&](int u) { return cur.g.slot + 16 * (i0 + (int64_t)u * kStreamThreads); },
+                valid);
         Cursor<0> nxt;
         const bool more = advance<0>(a, mring, s0, first, steps, cur, &nxt);
         loads_returned(v);
@@ -665,21 +673,22 @@ __device__ void consume_ll128(const StreamArgs &a, int c, int64_t s0, int64_t st
         const uint64_t flag = cur.g.k + 1;
         const uint32_t flo = (uint32_t)flag, fhi = (uint32_t)(flag >> 32);
         const int64_t q0 = cur.base + threadIdx.x;
-        auto check = [&](int u) { return v[u].z == flo && v[u].w == fhi; };
+        auto valid = [&](u32x4 x) { return x.z == flo && x.w == fhi; };
         bool ok[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int64_t q = q0 + (int64_t)u * kStreamThreads;
-            ok[u] = q >= cur.g.items || (q & 7) != 7 || check(u);
+            ok[u] = q >= cur.g.items || (q & 7) != 7 || valid(v[u]);
         }
+        // only flag chunks can be missing; a re-read takes the line's chunk 7
         if (!failed)
             failed = !poll_batch(
-                a, ok,
+                a, v, ok,
                 [&](int u) {
                     const int64_t q = q0 + (int64_t)u * kStreamThreads;
-                    v[u] = load16_sys(cur.g.slot + 128 * (q >> 3) + 112);
+                    return cur.g.slot + 128 * (q >> 3) + 112;
                 },
-                check);
+                valid);
         loads_returned(v);
         if (nxt.j != cur.j && !close_step(a, c, cur.g.k, failed))
             return;

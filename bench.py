@@ -82,6 +82,16 @@ def traffic_from_profile(source_hash: str):
     return float(t.group(1))
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def log(msg: str) -> None:
     print(f"bench: {msg}", file=sys.stderr, flush=True)
 
@@ -141,6 +151,36 @@ def main():
         del g
         return ms
 
+    def graph_time_stats(fns, steps, warmup, extra=10):
+        """graph_time for the timed `steps` launches, then `extra` further
+        replays of the same graph, each timed on its own, for the spread:
+        returns (ms per launch of the timed replay, per-replay ms per launch)."""
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(max(warmup, len(fns))):
+                fns[i % len(fns)]()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                fns[i % len(fns)]()
+        g.replay()                     # warm the graph itself
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(extra + 2)]
+        ev[0].record()
+        g.replay()
+        ev[1].record()
+        for r in range(extra):
+            g.replay()
+            ev[r + 2].record()
+        ev[-1].synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / steps
+        each = [ev[r + 1].elapsed_time(ev[r + 2]) / steps for r in range(extra)]
+        del g
+        return ms, each
+
     def sets_for(touched_bytes):
         """Buffer sets so that one rotation touches > 2x the Infinity Cache."""
         return max(2, -(-2 * MALL_BYTES // max(touched_bytes, 1)) + 1)
@@ -174,9 +214,23 @@ def main():
     steps = max(args.steps, nsets)
     steps -= steps % nsets
     log(f"two-stage W=8 8MiB: {nsets} buffer sets staged, timing {steps} launches")
-    ms = graph_time(calls, steps, args.warmup)
+    if args.eager:
+        ms = graph_time(calls, steps, args.warmup)
+        each = [ms]
+    else:
+        ms, each = graph_time_stats(calls, steps, args.warmup)
     gbps = bytes_2stage / (ms * 1e-3) / 1e9
     log(f"two-stage: {ms * 1e3:.3f} us/launch, {gbps:.1f} GB/s")
+    us = np.sort(np.array(each) * 1e3)
+    stats = {
+        "spread_over": f"{len(us)} further replays of the timed graph of {steps} launches",
+        "median_us": round(float(np.median(us)), 3),
+        "p5_us": round(float(np.percentile(us, 5)), 3),
+        "p95_us": round(float(np.percentile(us, 95)), 3),
+        "min_us": round(float(us[0]), 3), "max_us": round(float(us[-1]), 3),
+        "cv": round(float(np.std(us) / np.mean(us)), 4),
+    }
+    log(f"two-stage per-replay: {stats}")
     src_hash = kernel_source_hash()
     traffic = traffic_from_profile(src_hash)
 
@@ -202,6 +256,7 @@ def main():
             "buffer_sets_rotated": nsets,
         },
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "timing_stats": stats,
         "roofline": {
             "bound": "hbm",
             "achieved": round(gbps, 1),
@@ -585,7 +640,7 @@ def main():
             "sample": f"the full per-rank two-stage work of the headline workload "
                       f"(reduce-scatter of shard 0 + all-gather of the 8 shards, "
                       f"8 x 4,194,304 bf16), {reps} repetitions in {el:.1f} s, "
-                      f"single-threaded C",
+                      f"single-threaded C on {cpu_model()}",
             "ms_per_step": round(el / reps * 1e3, 3),
         }
 
