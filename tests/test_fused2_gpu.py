@@ -115,3 +115,21 @@ def test_fused_2stage_rotation_hand_case(gpu):
     ro, no = outs[1]
     assert list(orc.bf16_to_f32(ro[:, 0])) == [0.0, 1.0, 2.0, 2.0]
     assert list(orc.bf16_to_f32(no[:, 0])) == [0.0, 1.0, 1.0, 1.0]
+
+
+def test_fused_large_m_row_configuration(gpu):
+    """The large-M shape the bench times (W=4, M=2048, N=8192): the two-shot
+    form for every rank, and the one-shot form, against the oracle."""
+    W, M, N = synth.FUSED["W"], 2048, 8192
+    xs, res, w = synth.fused_inputs(W, M, N, [1000 + synth.FUSED["id"], M, N])
+    eps = synth.FUSED["eps"]
+    check(xs, res, w, eps, gpu)
+    d = [dev_u16(x, gpu) for x in xs]
+    dr, dw = dev_u16(res, gpu), dev_u16(w, gpu)
+    ro, no = torch.empty_like(dr), torch.empty_like(dr)
+    ar.ar_fused_residual_rmsnorm(d, dr, dw, ro, no, eps)
+    sync()
+    wro, _, exact = orc.fused_residual_rmsnorm(xs, res, w, eps)
+    assert np.array_equal(host_u16(ro), wro)
+    ok, _ = norm_within_tolerance(host_u16(no), exact)
+    assert ok.all()

@@ -83,6 +83,37 @@ def test_stream_nccl_default_steps_wire_workload(gpu, name, step, channels):
     Fifo(PROTOS[name], step, channels, gpu).run(src)
 
 
+@pytest.mark.parametrize("name,step,channels", [("ll", 32768, 128), ("ll128", 576000, 128),
+                                                ("simple", 524288, 128), ("ll", 32768, 256)])
+def test_stream_bench_configurations(gpu, name, step, channels):
+    """The channel counts the bench times, on the wire workload's payload,
+    twice in a row from the stored step."""
+    n = synth.WIRE["n"]
+    src = synth.wire(n)[0]
+    f = Fifo(PROTOS[name], step, channels, gpu)
+    f.run(src, cont=True)
+    f.run(src, cont=True)
+
+
+def test_stream_workgroups_that_cannot_be_resident_are_refused(gpu):
+    """256 channels need 512 resident workgroups; where a variant cannot
+    have them the call is refused before anything runs, else it is exact."""
+    n, step, ch = 256 * 2 * 1200 // 4, 1200, 256
+    src, local = synth.wire_payloads(2, n, [106])
+    f = Fifo(ar.AR_PROTO_LL128, step, ch, gpu)
+    d, dl = torch.from_numpy(src).to(gpu), torch.from_numpy(local).to(gpu)
+    out = torch.full((n + 16,), 777.0, dtype=torch.float32, device=gpu)
+    try:
+        f.launch(d, out, n, dl)
+    except ar.ArError as e:
+        assert e.status == ar.AR_ERR_CAPACITY
+        sync()
+        assert np.all(f.counters.cpu().numpy() == 0) and np.all(out.cpu().numpy() == 777.0)
+        return
+    sync()
+    f.check(src, out, local)
+
+
 @pytest.mark.parametrize("name,step", [("ll", 2048), ("ll128", 2400), ("ll128", 1080),
                                        ("simple", 2048)])
 def test_stream_reduce_with_local_and_consecutive_calls(gpu, name, step):
