@@ -44,12 +44,15 @@ _u64 = ctypes.c_uint64
 
 
 def lib():
-    """Load the oracle library, building it first if it is not there."""
+    """Load the oracle library, building it first if it is not there.  The
+    environment variable ORACLE_LIB names another build of oracle.c to load
+    instead (the sanitizer test uses it)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB):
+        path = os.environ.get("ORACLE_LIB", LIB)
+        if path == LIB and not os.path.exists(LIB):
             build()
-        L = ctypes.CDLL(LIB)
+        L = ctypes.CDLL(path)
         L.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
         L.orc_bf16_to_f32.restype = ctypes.c_float
         L.orc_bf16_rne.argtypes = [ctypes.c_float]
