@@ -265,17 +265,17 @@ __device__ __forceinline__ Step step_at(const StreamArgs &a, uint8_t *ring, int6
     return g;
 }
 
-// The next batch after (j, base); more is false past the channel's last step.
-template <int PROTO>
+// A batch: local step j, first item base.
 struct Cursor {
     int64_t j, base;
     Step g;
 };
 
+// The batch after cur; false past the channel's last step.
 template <int PROTO>
 __device__ __forceinline__ bool advance(const StreamArgs &a, uint8_t *ring, int64_t s0,
-                                        uint64_t first, int64_t steps, const Cursor<PROTO> &cur,
-                                        Cursor<PROTO> *nxt)
+                                        uint64_t first, int64_t steps, const Cursor &cur,
+                                        Cursor *nxt)
 {
     nxt->j = cur.j;
     nxt->base = cur.base + kPerBatch;
@@ -289,20 +289,18 @@ __device__ __forceinline__ bool advance(const StreamArgs &a, uint8_t *ring, int6
     return nxt->j < steps;
 }
 
-// Payload words of item i of a step and how many of them there are.
+// Payload words of LL or Simple item i of a step and how many of them there
+// are (LL128 items go through the line-pair helpers below).
 template <int PROTO>
 __device__ __forceinline__ int64_t item_word(const Step &g, int64_t i)
 {
-    return PROTO == 0 ? g.w0 + 2 * i : PROTO == 1 ? g.w0 + 30 * (i >> 3) + 4 * (i & 7)
-                                                  : g.w0 + 4 * i;
+    return PROTO == 0 ? g.w0 + 2 * i : g.w0 + 4 * i;
 }
 template <int PROTO>
 __device__ __forceinline__ int item_count(const Step &g, int64_t i)
 {
     if (PROTO == 0)
         return 2;
-    if (PROTO == 1)
-        return (i & 7) < 7 ? 4 : 2;
     const int64_t rem = g.words - 4 * i;
     return rem < 4 ? (int)rem : 4;
 }
@@ -328,7 +326,7 @@ __device__ __forceinline__ void load_src(const StreamArgs &a, const Step &g, int
     for (int u = 0; u < kBatch; ++u) {
         const int64_t i = base + (int64_t)u * kStreamThreads + threadIdx.x;
         d[u] = u32x4{0u, 0u, 0u, 0u};
-        if (PROTO == 1) {
+        if constexpr (PROTO == 1) {
             // payload chunk i % 16 of the pair (lane 15 has none); words past
             // the step belong to lines this step does not write
             if (i < g.items && (i & 15) < 15)
@@ -420,7 +418,7 @@ __device__ __forceinline__ void load_local(const StreamArgs &a, const Step &g, i
         lv[u] = u32x4{0u, 0u, 0u, 0u};
         if (!LOCAL || i >= g.items)
             continue;
-        if (PROTO == 1) {
+        if constexpr (PROTO == 1) {
             if (pair_chunk_count(g, i) > 0)
                 lv[u] = local_at(a, pair_chunk_word(g, i), 4);
         } else {
@@ -436,7 +434,7 @@ __device__ __forceinline__ void deliver_batch(const StreamArgs &a, const Step &g
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
         const int64_t i = base + (int64_t)u * kStreamThreads + threadIdx.x;
-        if (PROTO == 1) {
+        if constexpr (PROTO == 1) {
             // payload chunk c: line A's chunk c (c < 7); line A's chunk 7
             // data then line B's chunk 0 low half (c == 7); line B's chunk
             // c - 8 high half then chunk c - 7 low half (8 <= c < 15)
@@ -451,12 +449,12 @@ __device__ __forceinline__ void deliver_batch(const StreamArgs &a, const Step &g
             const u32x4 x = c < 7 ? v[u] : c == 7 ? u32x4{v[u].x, v[u].y, nx, ny}
                                                   : u32x4{v[u].z, v[u].w, nx, ny};
             deliver<LOCAL>(a, pair_chunk_word(g, i), cnt, x, lv[u]);
-            continue;
+        } else {
+            if (i >= g.items)
+                continue;
+            const u32x4 x = PROTO == 0 ? u32x4{v[u].x, v[u].z, 0u, 0u} : v[u];
+            deliver<LOCAL>(a, item_word<PROTO>(g, i), item_count<PROTO>(g, i), x, lv[u]);
         }
-        if (i >= g.items)
-            continue;
-        const u32x4 x = PROTO == 0 ? u32x4{v[u].x, v[u].z, 0u, 0u} : v[u];
-        deliver<LOCAL>(a, item_word<PROTO>(g, i), item_count<PROTO>(g, i), x, lv[u]);
     }
 }
 
@@ -480,11 +478,11 @@ __device__ void produce(const StreamArgs &a, int c, int64_t s0, int64_t steps, u
         return;
     uint8_t *ring = a.fifo + (int64_t)c * 8 * a.wire_bytes;
     uint64_t head_seen = first;      // the consumer has taken every step before `first`
-    Cursor<PROTO> cur{0, 0, step_at<PROTO>(a, ring, s0, first, 0)};
+    Cursor cur{0, 0, step_at<PROTO>(a, ring, s0, first, 0)};
     u32x4 d[kBatch];
     load_src<PROTO>(a, cur.g, 0, d);
     for (;;) {
-        Cursor<PROTO> nxt;
+        Cursor nxt;
         const bool more = advance<PROTO>(a, ring, s0, first, steps, cur, &nxt);
         u32x4 nd[kBatch];
         if (more)
@@ -578,9 +576,8 @@ __device__ void consume_ll(const StreamArgs &a, int c, int64_t s0, int64_t steps
 {
     if (steps <= 0)
         return;
-    const uint8_t *ring = a.fifo + (int64_t)c * 8 * a.wire_bytes;
-    uint8_t *mring = const_cast<uint8_t *>(ring);
-    Cursor<0> cur{0, 0, step_at<0>(a, mring, s0, first, 0)};
+    uint8_t *ring = a.fifo + (int64_t)c * 8 * a.wire_bytes;
+    Cursor cur{0, 0, step_at<0>(a, ring, s0, first, 0)};
     u32x4 v[kBatch], lv[kBatch];
     load_ring<0>(cur.g, 0, v);
     load_local<0, LOCAL>(a, cur.g, 0, lv);
@@ -598,8 +595,8 @@ __device__ void consume_ll(const StreamArgs &a, int c, int64_t s0, int64_t steps
                 a, v, ok,
                 [&](int u) { return cur.g.slot + 16 * (i0 + (int64_t)u * kStreamThreads); },
                 valid);
-        Cursor<0> nxt;
-        const bool more = advance<0>(a, mring, s0, first, steps, cur, &nxt);
+        Cursor nxt;
+        const bool more = advance<0>(a, ring, s0, first, steps, cur, &nxt);
         loads_returned(v);
         if (nxt.j != cur.j && !close_step(a, c, cur.g.k, failed))
             return;
@@ -657,7 +654,7 @@ __device__ void consume_ll128(const StreamArgs &a, int c, int64_t s0, int64_t st
         return;
     uint8_t *ring = a.fifo + (int64_t)c * 8 * a.wire_bytes;
     auto flag_at = [](const Step &g, int64_t base) { return g.slot + 128 * (base >> 3) + 120; };
-    Cursor<1> cur{0, 0, step_at<1>(a, ring, s0, first, 0)};
+    Cursor cur{0, 0, step_at<1>(a, ring, s0, first, 0)};
     uint64_t pre = threadIdx.x == 0 ? read_flag64(flag_at(cur.g, 0)) : 0;
     if (!wait_flag64(a, sh, flag_at(cur.g, 0), cur.g.k + 1, pre))
         return;
@@ -666,7 +663,7 @@ __device__ void consume_ll128(const StreamArgs &a, int c, int64_t s0, int64_t st
     load_local<1, LOCAL>(a, cur.g, 0, lv);
     bool failed = false;
     for (;;) {
-        Cursor<1> nxt;
+        Cursor nxt;
         const bool more = advance<1>(a, ring, s0, first, steps, cur, &nxt);
         if (threadIdx.x == 0 && more)
             pre = read_flag64(flag_at(nxt.g, nxt.base));
@@ -723,14 +720,14 @@ __device__ void consume_simple(const StreamArgs &a, int c, int64_t s0, int64_t s
         return;
     uint8_t *ring = a.fifo + (int64_t)c * 8 * a.wire_bytes;
     uint64_t tail_seen = first;      // the producer has written every step before `first`
-    Cursor<2> cur{0, 0, step_at<2>(a, ring, s0, first, 0)};
+    Cursor cur{0, 0, step_at<2>(a, ring, s0, first, 0)};
     if (!wait_counter(a, sh, a.tail + c, cur.g.k + 1, &tail_seen))
         return;
     u32x4 v[kBatch], lv[kBatch];
     load_ring<2>(cur.g, 0, v);
     load_local<2, LOCAL>(a, cur.g, 0, lv);
     for (;;) {
-        Cursor<2> nxt;
+        Cursor nxt;
         const bool more = advance<2>(a, ring, s0, first, steps, cur, &nxt);
         loads_returned(v);
         if (nxt.j != cur.j && !close_step(a, c, cur.g.k, false))
