@@ -39,7 +39,8 @@ hipError_t launch_lamport_fused(void *comm, int W, const void *residual,
                                 uint32_t max_spins, uint32_t *bad, const void *x_self,
                                 int rank, void *const *comms, hipStream_t s);
 
-// One cooperative launch of 2 * channels workgroups (producers, consumers).
+// One launch of 2 * channels workgroups (producers, then consumers), all of
+// which the caller has checked can be resident at once.
 hipError_t launch_fifo_stream(int proto, const float *src, const float *local, float *out,
                               int64_t n, void *fifo, uint64_t *counters, int channels,
                               int64_t step_bytes, int64_t wire_bytes, uint64_t first_step,

@@ -1,5 +1,5 @@
 """GPU parity of streaming through 8-step FIFOs (producer and consumer
-workgroups concurrent in one cooperative launch) against the oracle: the
+workgroups concurrent in one launch) against the oracle: the
 delivered payload and the rings' final bytes are bit-exact, and no wait
 times out.  Every wait in the kernel is bounded; the abort test forces the
 give-up path from the host (the error count set before the launch)."""
