@@ -587,9 +587,12 @@ __device__ void consume_ll(const StreamArgs &a, int c, int64_t s0, int64_t steps
         const int64_t i0 = cur.base + threadIdx.x;
         auto valid = [&](u32x4 x) { return x.y == flag && x.w == flag; };
         bool ok[kBatch];
+        bool ahead = true;       // every line was there on the first look
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u)
+        for (int u = 0; u < kBatch; ++u) {
             ok[u] = i0 + (int64_t)u * kStreamThreads >= cur.g.items || valid(v[u]);
+            ahead = ahead && ok[u];
+        }
         if (!failed)
             failed = !poll_batch(
                 a, v, ok,
@@ -600,13 +603,20 @@ __device__ void consume_ll(const StreamArgs &a, int c, int64_t s0, int64_t steps
         loads_returned(v);
         if (nxt.j != cur.j && !close_step(a, c, cur.g.k, failed))
             return;
+        // With the producer ahead, the next batch is loaded before this one
+        // is delivered; a lane that had to wait delivers first, so that its
+        // next look does not find lines not yet written.
         u32x4 nv[kBatch], nlv[kBatch];
-        if (more) {
+        if (more && ahead) {
             load_ring<0>(nxt.g, nxt.base, nv);
             load_local<0, LOCAL>(a, nxt.g, nxt.base, nlv);
         }
         if (!failed)
             deliver_batch<0, LOCAL>(a, cur.g, cur.base, v, lv);
+        if (more && !ahead) {
+            load_ring<0>(nxt.g, nxt.base, nv);
+            load_local<0, LOCAL>(a, nxt.g, nxt.base, nlv);
+        }
         if (!more)
             return;
         cur = nxt;
@@ -752,9 +762,12 @@ __device__ void consume_simple(const StreamArgs &a, int c, int64_t s0, int64_t s
     }
 }
 
-// Blocks [0, channels) produce, [channels, 2 * channels) consume.
+// Blocks [0, channels) produce, [channels, 2 * channels) consume.  Without
+// a local addend the kernel keeps to 128 VGPRs (4 wavefronts per SIMD), so
+// two workgroups fit on a CU and up to 256 channels can run at once; with one
+// it has two wavefronts per SIMD.
 template <int PROTO, bool LOCAL>
-__global__ __launch_bounds__(kStreamThreads) void stream_kernel(StreamArgs a)
+__global__ __launch_bounds__(kStreamThreads, LOCAL ? 2 : 4) void stream_kernel(StreamArgs a)
 {
     __shared__ Shared sh;
     const int b = blockIdx.x;
