@@ -392,15 +392,23 @@ LIBAR_EXPORT ar_status_t ar_lamport_oneshot_residual_rmsnorm(
 // ---------------------------------------------------------------------------
 // wire formats
 // ---------------------------------------------------------------------------
-LIBAR_EXPORT int64_t ll_lines(int64_t n) { return n > 0 ? (4 * n + 7) / 8 : 0; }
-LIBAR_EXPORT int64_t ll128_lines(int64_t n) { return n > 0 ? (4 * n + 119) / 120 : 0; }
+LIBAR_EXPORT int64_t ll_lines(int64_t n)
+{
+    return n > 0 && n <= kMaxElems ? (4 * n + 7) / 8 : 0;
+}
+LIBAR_EXPORT int64_t ll128_lines(int64_t n)
+{
+    return n > 0 && n <= kMaxElems ? (4 * n + 119) / 120 : 0;
+}
 LIBAR_EXPORT int64_t ll_fifo_bytes(int64_t step_lines)
 {
-    return step_lines > 0 ? AR_FIFO_STEPS * step_lines * 16 : 0;
+    return step_lines > 0 && step_lines <= kMaxLines / AR_FIFO_STEPS
+               ? AR_FIFO_STEPS * step_lines * 16 : 0;
 }
 LIBAR_EXPORT int64_t ll128_fifo_bytes(int64_t step_lines)
 {
-    return step_lines > 0 ? AR_FIFO_STEPS * step_lines * 128 : 0;
+    return step_lines > 0 && step_lines <= kMaxLines / AR_FIFO_STEPS
+               ? AR_FIFO_STEPS * step_lines * 128 : 0;
 }
 LIBAR_EXPORT int64_t ll_default_step_lines(void) { return 4096; }
 LIBAR_EXPORT int64_t ll128_default_step_lines(void) { return 4800; }
@@ -413,7 +421,7 @@ ar_status_t check_pack(const float *src, int64_t n, void *fifo, int64_t step_lin
 {
     if (!src || !fifo)
         return AR_ERR_NULL;
-    if (n < 0 || step_lines < 1 || step_lines > kMaxLines / AR_FIFO_STEPS)
+    if (n < 0 || n > kMaxElems || step_lines < 1 || step_lines > kMaxLines / AR_FIFO_STEPS)
         return AR_ERR_ARG;
     if (lines > AR_FIFO_STEPS * step_lines)
         return AR_ERR_CAPACITY;
@@ -435,7 +443,7 @@ ar_status_t check_unpack(const void *const *fifos, int W, float *out, int64_t n,
     for (int r = 0; r < W; ++r)
         if (!fifos[r])
             return AR_ERR_NULL;
-    if (n < 0 || step_lines < 1 || step_lines > kMaxLines / AR_FIFO_STEPS ||
+    if (n < 0 || n > kMaxElems || step_lines < 1 || step_lines > kMaxLines / AR_FIFO_STEPS ||
         max_spins > AR_MAX_SPINS)
         return AR_ERR_ARG;
     if (lines > AR_FIFO_STEPS * step_lines)
@@ -525,7 +533,7 @@ LIBAR_EXPORT int64_t ar_fifo_step_wire_bytes(int proto, int64_t step_bytes)
 
 LIBAR_EXPORT int64_t ar_fifo_steps_per_channel(int64_t n, int64_t step_bytes, int channels)
 {
-    if (n <= 0 || step_bytes <= 0 || channels < 1)
+    if (n <= 0 || n > kMaxElems || step_bytes <= 0 || channels < 1)
         return 0;
     const int64_t total = (4 * n + step_bytes - 1) / step_bytes;
     return (total + channels - 1) / channels;

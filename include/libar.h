@@ -275,9 +275,10 @@ ar_status_t ar_lamport_oneshot_residual_rmsnorm(const void *x, int rank,
  * (k mod 8) * step_lines + (i mod step_lines), with flag = (uint32)(k + 1).
  * FIFO lines not covered by the payload are left untouched.
  *   src         n fp32, 4-byte aligned (any offset)      else AR_ERR_ALIGN
+ *   n           0 <= n <= 2^40                           else AR_ERR_ARG
  *   fifo        ll_fifo_bytes(step_lines) bytes, 16-byte aligned
- *   step_lines  >= 1, and ll_lines(n) <= 8 * step_lines  else AR_ERR_CAPACITY
- *               ll_lines(n) and 8 * step_lines below 2^31 else AR_ERR_ARG
+ *   step_lines  1 <= step_lines <= 2^28                  else AR_ERR_ARG
+ *               ll_lines(n) <= 8 * step_lines            else AR_ERR_CAPACITY
  */
 ar_status_t ll_pack(const float *src, int64_t n, void *fifo, int64_t step_lines,
                     uint64_t first_step, ar_stream_t stream);
@@ -292,6 +293,7 @@ ar_status_t ll_pack(const float *src, int64_t n, void *fifo, int64_t step_lines,
  *   fifos       host table of W device pointers (16-byte aligned)
  *   W           1 <= W <= 8                               else AR_ERR_WORLD
  *   out         n fp32, 4-byte aligned; only out[0..n) is written
+ *   n, step_lines  as ll_pack
  *   max_spins   <= AR_MAX_SPINS                           else AR_ERR_ARG
  *   bad_lines   device u32 (4-byte aligned) the caller zeroes; the library
  *               adds the number of bad (FIFO, line) pairs.  NULL: not counted.
@@ -401,7 +403,8 @@ int64_t ar_fifo_steps_per_channel(int64_t n, int64_t step_bytes, int channels);
 
 /* Geometry helpers ([NCCL14] "Default buffers and effective data per
  * step": the default buffers give 4096 LL lines and 4800 LL128 lines per
- * step).  Negative arguments give 0. */
+ * step).  Arguments outside what the entry points accept (n < 1 or
+ * n > 2^40 values, step_lines < 1 or step_lines > 2^28) give 0. */
 int64_t ll_lines(int64_t n);                  /* ceil(4n / 8)   */
 int64_t ll128_lines(int64_t n);               /* ceil(4n / 120) */
 int64_t ll_fifo_bytes(int64_t step_lines);    /* 8 * step_lines * 16  */

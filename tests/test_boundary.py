@@ -198,3 +198,22 @@ def test_stream_argument_errors():
     assert st(f, LL, A, B, C, D, 2, 1024, 0, 8, D + 40, None, 8, 0) == ar.AR_ERR_ARG
     assert st(f, LL, A, B, C, D, 2, 1024, 0, 8, D + 48, None, 0, 0) == ar.AR_OK
     assert st(f, LL, A, B, C, D, 2, 1024, 0, 8, E, None, 0, 0) == ar.AR_OK       # n = 0
+
+
+def test_size_limits_of_the_wire_helpers():
+    big = (1 << 62) + 3                     # 4n would not fit in 64 bits
+    assert ar.ll_lines(1 << 40) == (1 << 39) and ar.ll_lines((1 << 40) + 1) == 0
+    assert ar.ll_lines(big) == 0 and ar.ll128_lines(big) == 0
+    assert ar.ll_fifo_bytes(1 << 28) == (1 << 35) and ar.ll_fifo_bytes((1 << 28) + 1) == 0
+    assert ar.ll128_fifo_bytes(1 << 62) == 0
+    assert ar.ar_fifo_steps_per_channel(big, 32768, 4) == 0
+
+
+@cpu_only
+def test_wire_calls_reject_sizes_past_the_limit():
+    big = (1 << 62) + 3
+    assert st(ar.ll_pack, A, B, 1, 0, big, 0) == ar.AR_ERR_ARG
+    assert st(ar.ll128_pack, A, B, 1, 0, (1 << 40) + 30, 0) == ar.AR_ERR_ARG
+    assert st(ar.ll_unpack_reduce, [A], C, 1, 0, 0, None, big, 0) == ar.AR_ERR_ARG
+    assert st(ar.ll128_unpack_reduce, [A], C, 1, 0, 0, None, big, 0) == ar.AR_ERR_ARG
+    assert st(ar.ll_pack, A, B, (1 << 28) + 1, 0, 8, 0) == ar.AR_ERR_ARG
