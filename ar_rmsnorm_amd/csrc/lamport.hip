@@ -32,17 +32,23 @@ __global__ __launch_bounds__(kLamportThreads) void lamport_push_kernel(
         st_stream(slots.p[p] + i, v);
 }
 
+// Grid-stride fill: the whole buffer holds three regions, so the grid is
+// capped and each lane covers every gridDim.x * threads-th chunk.
 __global__ __launch_bounds__(kLamportThreads) void lamport_fill_kernel(u32x4 *comm,
                                                                        int64_t chunks)
 {
-    const int64_t i = (int64_t)blockIdx.x * kLamportThreads + threadIdx.x;
-    if (i < chunks)
+    const int64_t stride = (int64_t)gridDim.x * kLamportThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kLamportThreads + threadIdx.x; i < chunks;
+         i += stride)
         st_stream(comm + i, u32x4{kSentinel, kSentinel, kSentinel, kSentinel});
 }
 
 hipError_t launch_lamport_fill(void *comm, int64_t chunks, hipStream_t s)
 {
-    const int64_t blocks = (chunks + kLamportThreads - 1) / kLamportThreads;
+    constexpr int64_t kMaxBlocks = 1 << 20;
+    int64_t blocks = (chunks + kLamportThreads - 1) / kLamportThreads;
+    if (blocks > kMaxBlocks)
+        blocks = kMaxBlocks;
     lamport_fill_kernel<<<dim3((unsigned)blocks), kLamportThreads, 0, s>>>(
         static_cast<u32x4 *>(comm), chunks);
     return hipGetLastError();

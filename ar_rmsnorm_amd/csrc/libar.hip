@@ -242,7 +242,8 @@ namespace {
 
 bool fused_shape_ok(int64_t M, int64_t N)
 {
-    return M >= 0 && M <= 0x7FFFFFFF && N >= 8 && N <= AR_FUSED_MAX_N && N % 8 == 0;
+    return M >= 0 && M <= 0x7FFFFFFF && N >= 8 && N <= AR_FUSED_MAX_N && N % 8 == 0 &&
+           M * N <= kMaxElems;
 }
 
 }  // namespace

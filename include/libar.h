@@ -218,7 +218,8 @@ ar_status_t ar_lamport_fill(void *comm, int W, int64_t M, int64_t N,
  *   x      bf16 [M, N] row-major, 16-byte aligned; must not overlap a buffer
  *   comms  host table of the W ranks' comm buffers (16-byte aligned)
  *   W      2 <= W <= 8                                  else AR_ERR_WORLD
- *   rank   0 <= rank < W; M >= 0; 8 <= N <= 16384, N multiple of 8
+ *   rank   0 <= rank < W; 0 <= M < 2^31, M * N <= 2^40; 8 <= N <= 16384,
+ *          N multiple of 8
  *                                                       else AR_ERR_ARG
  */
 ar_status_t ar_lamport_push(const void *x, int W, int rank, void *const *comms,

@@ -217,3 +217,9 @@ def test_wire_calls_reject_sizes_past_the_limit():
     assert st(ar.ll_unpack_reduce, [A], C, 1, 0, 0, None, big, 0) == ar.AR_ERR_ARG
     assert st(ar.ll128_unpack_reduce, [A], C, 1, 0, 0, None, big, 0) == ar.AR_ERR_ARG
     assert st(ar.ll_pack, A, B, (1 << 28) + 1, 0, 8, 0) == ar.AR_ERR_ARG
+
+
+def test_lamport_shape_limits():
+    assert ar.ar_lamport_comm_bytes(4, 1 << 26, 16384) == 3 * 4 * (1 << 40) * 2
+    assert ar.ar_lamport_comm_bytes(4, (1 << 26) + 1, 16384) == 0     # M * N > 2^40
+    assert ar.ar_lamport_comm_bytes(4, 1 << 31, 8) == 0               # M >= 2^31
