@@ -436,6 +436,47 @@ def main():
             del s2, base_x
             torch.cuda.empty_cache()
 
+        def fused_crossover(N, Ms):
+            cross = {}
+            Wf = fc["W"]
+            for M in Ms:
+                fx, fr, fw = synth.fused_inputs(Wf, M, N, [1000 + fc["id"], M, N])
+                mat = M * N * 2
+                part, rem = M // Wf, M % Wf
+                base_x = [to_dev(x) for x in fx]
+                base_r, dw = to_dev(fr), to_dev(fw)
+                nsets_f = sets_for((Wf + 3) * mat)
+                s1, s2 = [], []
+                for k in range(nsets_f):
+                    xx = [b.view(M, N) for b in rank_buffers(Wf, mat, torch.int16, base_x)]
+                    rr = base_r if k == 0 else base_r.clone()
+                    tmps = rank_buffers(Wf, 4 * (part + rem) * N, torch.int16)
+                    for r in range(1, Wf):
+                        ar.ar_fused_residual_rmsnorm_2stage(xx, tmps, r, rr, dw, None, None,
+                                                            fc["eps"], flags=ar.AR_STAGE_RS)
+                    s1.append((xx, rr, torch.empty_like(rr), torch.empty_like(rr)))
+                    s2.append((xx, rr, tmps, torch.empty_like(rr), torch.empty_like(rr)))
+                k = 8 * nsets_f
+                t1 = graph_time([lambda q=q: ar.ar_fused_residual_rmsnorm(
+                    q[0], q[1], dw, q[2], q[3], fc["eps"]) for q in s1], k, args.warmup)
+                t2 = graph_time([lambda q=q: ar.ar_fused_residual_rmsnorm_2stage(
+                    q[0], q[2], 0, q[1], dw, q[3], q[4], fc["eps"]) for q in s2], k, args.warmup)
+                cross[str(M)] = {"one_shot_us": round(t1 * 1e3, 3),
+                                 "two_shot_us": round(t2 * 1e3, 3)}
+                del s1, s2, base_x
+                torch.cuda.empty_cache()
+            won = [int(m) for m, v in cross.items() if v["two_shot_us"] < v["one_shot_us"]]
+            rows[f"fused_one_vs_two_shot_W4_N{N}"] = {
+                "us_per_call": cross, "two_shot_faster_from_M": min(won) if won else None}
+            log(f"fused one-shot vs two-shot, N={N}: {cross}")
+
+        # where the two-shot fused form overtakes the one-shot form for one
+        # rank's call on this device: W=4, N = 2048 and 8192, M from 16 to
+        # 8192 rows (cold sets, graph-timed); the crossover M is reported
+        for N, Ms in ((2048, (16, 128, 512, 1024, 2048, 4096, 8192)),
+                      (8192, (32, 64, 128, 256, 512, 1024, 2048))):
+            fused_crossover(N, Ms)
+
         # one-stage reduce: small, decode shape, and the cap message
         for name, maker in (("1stage_W2_n8192", synth.reduce_small),
                             ("1stage_W8_n8192", synth.reduce_decode)):
