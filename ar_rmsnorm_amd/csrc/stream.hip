@@ -83,25 +83,52 @@ struct StreamArgs {
     uint32_t max_spins;
 };
 
-__device__ __forceinline__ void store16_sys(uint8_t *p, u32x4 v)
+// Ring accesses are buffer loads and stores with the system-coherent cache
+// policy (sc0 sc1).  They are deliberately not volatile: on gfx950 every
+// volatile access waits for its own completion before the next one issues,
+// while these let a lane keep a whole batch in flight.  A descriptor covers
+// one ring slot (at most 2^31 bytes), so every offset fits in 32 bits, and
+// the hardware range check drops anything outside the slot.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kSysCoherent = 1 | 16;       // cache-policy bits sc0 | sc1
+constexpr int kRsrcWord3 = 0x00020000;     // descriptor word 3: 32-bit data format
+__device__ __forceinline__ Rsrc slot_rsrc(uint8_t *slot, int64_t bytes)
 {
-    *reinterpret_cast<volatile u32x4 *>(p) = v;
+    return __builtin_amdgcn_make_buffer_rsrc(slot, 0, (int)(uint32_t)bytes, kRsrcWord3);
 }
-__device__ __forceinline__ void store8_sys(uint8_t *p, u32x2 v)
+__device__ __forceinline__ void store16_sys(Rsrc r, uint32_t off, u32x4 v)
 {
-    *reinterpret_cast<volatile u32x2 *>(p) = v;
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kSysCoherent);
 }
-__device__ __forceinline__ void store4_sys(uint8_t *p, uint32_t v)
+__device__ __forceinline__ void store8_sys(Rsrc r, uint32_t off, u32x2 v)
 {
-    *reinterpret_cast<volatile uint32_t *>(p) = v;
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kSysCoherent);
 }
-__device__ __forceinline__ u32x4 load16_sys(const uint8_t *p)
+__device__ __forceinline__ void store4_sys(Rsrc r, uint32_t off, uint32_t v)
 {
-    return *reinterpret_cast<const volatile u32x4 *>(p);
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, kSysCoherent);
 }
-__device__ __forceinline__ u32x2 load8_sys(const uint8_t *p)
+__device__ __forceinline__ u32x4 load16_sys(Rsrc r, uint32_t off)
 {
-    return *reinterpret_cast<const volatile u32x2 *>(p);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kSysCoherent);
+}
+__device__ __forceinline__ u32x2 load8_sys(Rsrc r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kSysCoherent);
+}
+// A compiler-only barrier at the top of every spin, so that a poll loop
+// issues its loads again instead of reusing the values of the last spin.
+__device__ __forceinline__ void respin()
+{
+    asm volatile("" ::: "memory");
+}
+// A value every lane holds alike, made visibly uniform to the compiler (so
+// descriptors and branches built from it stay scalar).
+__device__ __forceinline__ uint64_t uniform64(uint64_t v)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (uint64_t)hi << 32 | lo;
 }
 __device__ __forceinline__ uint64_t load_counter(const uint64_t *p)
 {
@@ -139,6 +166,7 @@ __device__ bool wait_lane0(const StreamArgs &a, Shared *sh, uint64_t *seen, Poll
         uint64_t v = poll();
         bool ok = ready(v);
         for (uint32_t s = 0; !ok && s < a.max_spins; ++s) {
+            respin();
             if (s % kAbortCheck == 0 && aborted(a.errors))
                 break;
             v = poll();
@@ -150,9 +178,9 @@ __device__ bool wait_lane0(const StreamArgs &a, Shared *sh, uint64_t *seen, Poll
         sh->value = v;
     }
     __syncthreads();
-    const bool go = sh->verdict != 0;
+    const bool go = __builtin_amdgcn_readfirstlane(sh->verdict) != 0;
     if (seen)
-        *seen = sh->value;
+        *seen = uniform64(sh->value);
     __syncthreads();   // the slots are reused by the next wait
     return go;
 }
@@ -240,7 +268,7 @@ __device__ __forceinline__ void deliver(const StreamArgs &a, int64_t w, int cnt,
 // between the second line's chunks and the payload chunks is done across
 // lanes with DPP row shifts.
 struct Step {
-    uint8_t *slot;
+    Rsrc slot;        // the step's ring slot
     int64_t w0;       // first payload word
     int64_t words;    // payload words
     int64_t items;
@@ -255,7 +283,7 @@ __device__ __forceinline__ Step step_at(const StreamArgs &a, uint8_t *ring, int6
 {
     Step g;
     g.k = first + (uint64_t)j;
-    g.slot = ring + (int64_t)(g.k % 8u) * a.wire_bytes;
+    g.slot = slot_rsrc(ring + (int64_t)(g.k % 8u) * a.wire_bytes, a.wire_bytes);
     const int64_t b0 = (s0 + j) * a.step_bytes;
     const int64_t left = 4 * a.n - b0;
     const int64_t len = left < a.step_bytes ? left : a.step_bytes;
@@ -305,9 +333,9 @@ __device__ __forceinline__ int item_count(const Step &g, int64_t i)
     return rem < 4 ? (int)rem : 4;
 }
 template <int PROTO>
-__device__ __forceinline__ int64_t ring_offset(int64_t i)
+__device__ __forceinline__ uint32_t ring_offset(int64_t i)
 {
-    return PROTO == 1 ? 128 * (i >> 3) + 16 * (i & 7) : 16 * i;
+    return (uint32_t)(PROTO == 1 ? 128 * (i >> 3) + 16 * (i & 7) : 16 * i);
 }
 
 // Source words of a batch (zero for items past the step).
@@ -368,24 +396,24 @@ __device__ __forceinline__ void store_ring(const Step &g, int64_t base, const u3
         }
         if (i >= g.items)
             continue;
-        uint8_t *p = g.slot + ring_offset<PROTO>(i);
+        const uint32_t p = ring_offset<PROTO>(i);
         if (PROTO == 0) {
             const uint32_t f = (uint32_t)(g.k + 1);
-            store16_sys(p, u32x4{d[u].x, f, d[u].y, f});
+            store16_sys(g.slot, p, u32x4{d[u].x, f, d[u].y, f});
         } else if (PROTO == 1) {
             // chunk 7 goes out whole with a zero flag word (no step's flag is
             // 0), so each line is written by one full-line store
             const int c = (int)(i & 15);
-            store16_sys(p, c < 7    ? d[u]
+            store16_sys(g.slot, p, c < 7    ? d[u]
                            : c == 7 ? u32x4{d[u].x, d[u].y, 0u, 0u}
                            : c < 15 ? u32x4{hz, hw, d[u].x, d[u].y}
                                     : u32x4{hz, hw, 0u, 0u});
         } else if (4 * i + 4 <= g.words) {
-            store16_sys(p, d[u]);
+            store16_sys(g.slot, p, d[u]);
         } else {
             for (int e = 0; e < 4; ++e)
                 if (4 * i + e < g.words)
-                    store4_sys(p + 4 * e, d[u][e]);
+                    store4_sys(g.slot, p + 4 * e, d[u][e]);
         }
     }
 }
@@ -396,7 +424,7 @@ __device__ __forceinline__ void load_ring(const Step &g, int64_t base, u32x4 v[k
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
         const int64_t i = base + (int64_t)u * kStreamThreads + threadIdx.x;
-        v[u] = i < g.items ? load16_sys(g.slot + ring_offset<PROTO>(i)) : u32x4{0u, 0u, 0u, 0u};
+        v[u] = i < g.items ? load16_sys(g.slot, ring_offset<PROTO>(i)) : u32x4{0u, 0u, 0u, 0u};
     }
 }
 
@@ -499,7 +527,8 @@ __device__ void produce(const StreamArgs &a, int c, int64_t s0, int64_t steps, u
                                                                     : cur.g.items;
             const uint64_t f = cur.g.k + 1;
             for (int64_t l = cur.base / 8 + threadIdx.x; l < end / 8; l += kStreamThreads)
-                store8_sys(cur.g.slot + 128 * l + 120, u32x2{(uint32_t)f, (uint32_t)(f >> 32)});
+                store8_sys(cur.g.slot, (uint32_t)(128 * l + 120),
+                           u32x2{(uint32_t)f, (uint32_t)(f >> 32)});
         }
         if (PROTO == 2 && nxt.j != cur.j) {
             // the step's data is acknowledged before its tail
@@ -534,15 +563,16 @@ __device__ bool close_step(const StreamArgs &a, int c, uint64_t k, bool failed)
 // any wait of the launch has failed).  While items are missing, only the
 // earliest of them is polled, since the producer stores a lane's items in
 // that order; once it is valid the missing items are all read again.
-template <typename Addr, typename Valid>
-__device__ bool poll_batch(const StreamArgs &a, u32x4 v[kBatch], bool ok[kBatch], Addr addr,
-                           Valid valid)
+template <typename Offset, typename Valid>
+__device__ bool poll_batch(const StreamArgs &a, u32x4 v[kBatch], bool ok[kBatch], Rsrc slot,
+                           Offset off, Valid valid)
 {
     bool all = true;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)
         all = all && ok[u];
     for (uint32_t s = 0; !all && s < a.max_spins; ++s) {
+        respin();
         if (s % kAbortCheck == 0 && aborted(a.errors))
             break;
         int lead = 0;
@@ -550,12 +580,12 @@ __device__ bool poll_batch(const StreamArgs &a, u32x4 v[kBatch], bool ok[kBatch]
         for (int u = kBatch - 1; u >= 0; --u)
             if (!ok[u])
                 lead = u;
-        if (!valid(load16_sys(addr(lead))))
+        if (!valid(load16_sys(slot, off(lead))))
             continue;
 #pragma unroll
         for (int u = 0; u < kBatch; ++u)
             if (!ok[u])
-                v[u] = load16_sys(addr(u));
+                v[u] = load16_sys(slot, off(u));
         all = true;
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
@@ -595,8 +625,8 @@ __device__ void consume_ll(const StreamArgs &a, int c, int64_t s0, int64_t steps
         }
         if (!failed)
             failed = !poll_batch(
-                a, v, ok,
-                [&](int u) { return cur.g.slot + 16 * (i0 + (int64_t)u * kStreamThreads); },
+                a, v, ok, cur.g.slot,
+                [&](int u) { return (uint32_t)(16 * (i0 + (int64_t)u * kStreamThreads)); },
                 valid);
         Cursor nxt;
         const bool more = advance<0>(a, ring, s0, first, steps, cur, &nxt);
@@ -629,8 +659,8 @@ __device__ void consume_ll(const StreamArgs &a, int c, int64_t s0, int64_t steps
 }
 
 // Lane 0 waits for a 64-bit flag, starting from a value it read earlier.
-__device__ bool wait_flag64(const StreamArgs &a, Shared *sh, const uint8_t *p, uint64_t want,
-                            uint64_t pre)
+__device__ bool wait_flag64(const StreamArgs &a, Shared *sh, Rsrc slot, uint32_t off,
+                            uint64_t want, uint64_t pre)
 {
     bool first = true;
     return wait_lane0(
@@ -640,14 +670,14 @@ __device__ bool wait_flag64(const StreamArgs &a, Shared *sh, const uint8_t *p, u
                 first = false;
                 return pre;
             }
-            const u32x2 f = load8_sys(p);
+            const u32x2 f = load8_sys(slot, off);
             return (uint64_t)f.x | ((uint64_t)f.y << 32);
         },
         [&](uint64_t f) { return f == want; });
 }
-__device__ __forceinline__ uint64_t read_flag64(const uint8_t *p)
+__device__ __forceinline__ uint64_t read_flag64(Rsrc slot, uint32_t off)
 {
-    const u32x2 f = load8_sys(p);
+    const u32x2 f = load8_sys(slot, off);
     return (uint64_t)f.x | ((uint64_t)f.y << 32);
 }
 
@@ -663,10 +693,10 @@ __device__ void consume_ll128(const StreamArgs &a, int c, int64_t s0, int64_t st
     if (steps <= 0)
         return;
     uint8_t *ring = a.fifo + (int64_t)c * 8 * a.wire_bytes;
-    auto flag_at = [](const Step &g, int64_t base) { return g.slot + 128 * (base >> 3) + 120; };
+    auto flag_at = [](int64_t base) { return (uint32_t)(128 * (base >> 3) + 120); };
     Cursor cur{0, 0, step_at<1>(a, ring, s0, first, 0)};
-    uint64_t pre = threadIdx.x == 0 ? read_flag64(flag_at(cur.g, 0)) : 0;
-    if (!wait_flag64(a, sh, flag_at(cur.g, 0), cur.g.k + 1, pre))
+    uint64_t pre = threadIdx.x == 0 ? read_flag64(cur.g.slot, flag_at(0)) : 0;
+    if (!wait_flag64(a, sh, cur.g.slot, flag_at(0), cur.g.k + 1, pre))
         return;
     u32x4 v[kBatch], lv[kBatch];
     load_ring<1>(cur.g, 0, v);
@@ -676,7 +706,7 @@ __device__ void consume_ll128(const StreamArgs &a, int c, int64_t s0, int64_t st
         Cursor nxt;
         const bool more = advance<1>(a, ring, s0, first, steps, cur, &nxt);
         if (threadIdx.x == 0 && more)
-            pre = read_flag64(flag_at(nxt.g, nxt.base));
+            pre = read_flag64(nxt.g.slot, flag_at(nxt.base));
         const uint64_t flag = cur.g.k + 1;
         const uint32_t flo = (uint32_t)flag, fhi = (uint32_t)(flag >> 32);
         const int64_t q0 = cur.base + threadIdx.x;
@@ -690,16 +720,16 @@ __device__ void consume_ll128(const StreamArgs &a, int c, int64_t s0, int64_t st
         // only flag chunks can be missing; a re-read takes the line's chunk 7
         if (!failed)
             failed = !poll_batch(
-                a, v, ok,
+                a, v, ok, cur.g.slot,
                 [&](int u) {
                     const int64_t q = q0 + (int64_t)u * kStreamThreads;
-                    return cur.g.slot + 128 * (q >> 3) + 112;
+                    return (uint32_t)(128 * (q >> 3) + 112);
                 },
                 valid);
         loads_returned(v);
         if (nxt.j != cur.j && !close_step(a, c, cur.g.k, failed))
             return;
-        if (more && !wait_flag64(a, sh, flag_at(nxt.g, nxt.base), nxt.g.k + 1, pre))
+        if (more && !wait_flag64(a, sh, nxt.g.slot, flag_at(nxt.base), nxt.g.k + 1, pre))
             return;
         u32x4 nv[kBatch], nlv[kBatch];
         if (more) {
@@ -782,7 +812,7 @@ __global__ __launch_bounds__(kStreamThreads, LOCAL ? 2 : 4) void stream_kernel(S
                                                     __HIP_MEMORY_SCOPE_AGENT)
                                 : a.first_step;
     __syncthreads();
-    const uint64_t first = sh.value;
+    const uint64_t first = uniform64(sh.value);
     __syncthreads();
     const int64_t s0 = (int64_t)c * a.total_steps / a.channels;
     const int64_t s1 = (int64_t)(c + 1) * a.total_steps / a.channels;
