@@ -40,14 +40,16 @@ hipError_t launch_lamport_fused(void *comm, int W, const void *residual,
                                 int rank, void *const *comms, hipStream_t s);
 
 // One launch of 2 * channels workgroups (producers, then consumers), all of
-// which the caller has checked can be resident at once.
+// which the caller has checked can be resident at once in the chosen
+// geometry (wide: 1,024 lanes per workgroup, else 512).
 hipError_t launch_fifo_stream(int proto, const float *src, const float *local, float *out,
                               int64_t n, void *fifo, uint64_t *counters, int channels,
                               int64_t step_bytes, int64_t wire_bytes, uint64_t first_step,
                               bool from_state, uint32_t max_spins, uint32_t *errors,
-                              hipStream_t s);
-// Workgroups of the streaming kernel the current device holds at once.
-hipError_t fifo_stream_resident_workgroups(int proto, bool local, int *workgroups);
+                              bool wide, hipStream_t s);
+// Workgroups of the streaming kernel, in the given geometry, that the current
+// device holds at once.
+hipError_t fifo_stream_resident_workgroups(int proto, bool local, bool wide, int *workgroups);
 
 hipError_t launch_ll_pack(const float *src, int64_t n, void *fifo,
                           int64_t step_lines, uint64_t first_step, hipStream_t s);

@@ -548,25 +548,25 @@ LIBAR_EXPORT int64_t ar_fifo_counter_words(int channels)
 namespace {
 
 // Workgroups of the streaming kernel the device can hold at once, per
-// (device, protocol), looked up once.
-int resident_workgroups(int proto, bool local, int *workgroups)
+// (device, protocol, local addend, geometry), looked up once.
+int resident_workgroups(int proto, bool local, bool wide, int *workgroups)
 {
     constexpr int kDevices = 64;
-    static std::atomic<int> cache[kDevices][3][2];
+    static std::atomic<int> cache[kDevices][3][2][2];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
         return (int)e;
     if (dev >= 0 && dev < kDevices) {
-        const int c = cache[dev][proto][local].load(std::memory_order_relaxed);
+        const int c = cache[dev][proto][local][wide].load(std::memory_order_relaxed);
         if (c > 0) {
             *workgroups = c;
             return 0;
         }
     }
-    e = ar::fifo_stream_resident_workgroups(proto, local, workgroups);
+    e = ar::fifo_stream_resident_workgroups(proto, local, wide, workgroups);
     if (e == hipSuccess && dev >= 0 && dev < kDevices)
-        cache[dev][proto][local].store(*workgroups, std::memory_order_relaxed);
+        cache[dev][proto][local][wide].store(*workgroups, std::memory_order_relaxed);
     return (int)e;
 }
 
@@ -606,14 +606,21 @@ LIBAR_EXPORT ar_status_t ar_fifo_stream(int proto, const float *src, const float
         return AR_ERR_ARG;
     if (n == 0)
         return AR_OK;
-    int resident = 0;
-    const int he = resident_workgroups(proto, local != nullptr, &resident);
-    if (he != 0)
-        return from_hip((hipError_t)he);
-    if (resident < 2 * channels)
-        return AR_ERR_CAPACITY;
+    // the wide geometry when every workgroup fits at once, else the narrow one
+    bool wide = true;
+    for (;;) {
+        int resident = 0;
+        const int he = resident_workgroups(proto, local != nullptr, wide, &resident);
+        if (he != 0)
+            return from_hip((hipError_t)he);
+        if (resident >= 2 * channels)
+            break;
+        if (!wide)
+            return AR_ERR_CAPACITY;
+        wide = false;
+    }
     return from_hip(ar::launch_fifo_stream(proto, src, local, out, n, fifo, counters, channels,
                                            step_bytes, wire, first_step,
                                            first_step == AR_FIFO_CONTINUE, max_spins, errors,
-                                           static_cast<hipStream_t>(stream)));
+                                           wide, static_cast<hipStream_t>(stream)));
 }

@@ -28,7 +28,7 @@
 // will consume) after each step, and the producer reuses slot k mod 8 only
 // once head >= k - 7.
 //
-// Memory-level parallelism: every lane issues kBatch loads (source words,
+// Memory-level parallelism: every lane issues a batch of loads (source words,
 // ring chunks, local addends) before it checks or stores any of them, items
 // not yet ready are re-polled together, and the consumer releases a slot
 // before it stores the step's last batch, so a step costs a few memory round
@@ -59,8 +59,15 @@
 
 namespace ar {
 
-constexpr int kStreamThreads = 512;
-constexpr int kBatch = 8;              // loads in flight per lane
+// A batch is kPerBatch items of one step.  Two launch geometries cover it:
+// 1,024 lanes with 4 items in flight each when one workgroup per CU is enough
+// for 2 x channels, else 512 lanes with 8 each (two workgroups per CU, up to
+// 256 channels).  The wider one hides more of each batch's round trips.
+constexpr int64_t kPerBatch = 4096;
+constexpr int kWideThreads = 1024;
+constexpr int kNarrowThreads = 512;
+template <int T>
+constexpr int kBatchOf = (int)(kPerBatch / T);   // items in flight per lane
 constexpr uint32_t kAbortCheck = 16;   // spins between looks at the error count
 
 struct StreamArgs {
@@ -257,8 +264,8 @@ __device__ __forceinline__ void deliver(const StreamArgs &a, int64_t w, int cnt,
 
 // ---------------------------------------------------------------------------
 // Steps and batches.  Items are LL lines, LL128 line chunks or Simple
-// 16-byte chunks.  A batch is kBatch items per lane: items
-// base + u * kStreamThreads + threadIdx.x, u < kBatch.
+// 16-byte chunks.  With T lanes a batch is kBatchOf<T> items per lane: items
+// base + u * T + threadIdx.x, u < kBatchOf<T>.
 //
 // LL128 item q is chunk q % 8 of line q / 8 (chunks 0..6 carry 16 payload
 // bytes, chunk 7 carries 8 payload bytes and then the flag).  Sixteen
@@ -274,8 +281,6 @@ struct Step {
     int64_t items;
     uint64_t k;       // ring step
 };
-
-constexpr int64_t kPerBatch = (int64_t)kStreamThreads * kBatch;
 
 template <int PROTO>
 __device__ __forceinline__ Step step_at(const StreamArgs &a, uint8_t *ring, int64_t s0,
@@ -346,13 +351,13 @@ __device__ __forceinline__ int64_t pair_chunk_word(const Step &g, int64_t q)
     return g.w0 + 60 * (q >> 4) + 4 * (q & 15);
 }
 
-template <int PROTO>
+template <int T, int PROTO>
 __device__ __forceinline__ void load_src(const StreamArgs &a, const Step &g, int64_t base,
-                                         u32x4 d[kBatch])
+                                         u32x4 d[kBatchOf<T>])
 {
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-        const int64_t i = base + (int64_t)u * kStreamThreads + threadIdx.x;
+    for (int u = 0; u < kBatchOf<T>; ++u) {
+        const int64_t i = base + (int64_t)u * T + threadIdx.x;
         d[u] = u32x4{0u, 0u, 0u, 0u};
         if constexpr (PROTO == 1) {
             // payload chunk i % 16 of the pair (lane 15 has none); words past
@@ -380,12 +385,12 @@ __device__ __forceinline__ uint32_t row_shift(uint32_t v)
 constexpr int kRowShr1 = 0x111;   // lane c receives lane c - 1
 constexpr int kRowShl1 = 0x101;   // lane c receives lane c + 1
 
-template <int PROTO>
-__device__ __forceinline__ void store_ring(const Step &g, int64_t base, const u32x4 d[kBatch])
+template <int T, int PROTO>
+__device__ __forceinline__ void store_ring(const Step &g, int64_t base, const u32x4 d[kBatchOf<T>])
 {
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-        const int64_t i = base + (int64_t)u * kStreamThreads + threadIdx.x;
+    for (int u = 0; u < kBatchOf<T>; ++u) {
+        const int64_t i = base + (int64_t)u * T + threadIdx.x;
         // LL128: the second line's chunk c - 8 is the high half of payload
         // chunk c - 1 and the low half of payload chunk c (every lane takes
         // part in the shift)
@@ -418,12 +423,12 @@ __device__ __forceinline__ void store_ring(const Step &g, int64_t base, const u3
     }
 }
 
-template <int PROTO>
-__device__ __forceinline__ void load_ring(const Step &g, int64_t base, u32x4 v[kBatch])
+template <int T, int PROTO>
+__device__ __forceinline__ void load_ring(const Step &g, int64_t base, u32x4 v[kBatchOf<T>])
 {
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-        const int64_t i = base + (int64_t)u * kStreamThreads + threadIdx.x;
+    for (int u = 0; u < kBatchOf<T>; ++u) {
+        const int64_t i = base + (int64_t)u * T + threadIdx.x;
         v[u] = i < g.items ? load16_sys(g.slot, ring_offset<PROTO>(i)) : u32x4{0u, 0u, 0u, 0u};
     }
 }
@@ -436,13 +441,13 @@ __device__ __forceinline__ int pair_chunk_count(const Step &g, int64_t q)
     return (q & 15) == 15 || rem <= 0 ? 0 : rem < 4 ? (int)rem : 4;
 }
 
-template <int PROTO, bool LOCAL>
+template <int T, int PROTO, bool LOCAL>
 __device__ __forceinline__ void load_local(const StreamArgs &a, const Step &g, int64_t base,
-                                           u32x4 lv[kBatch])
+                                           u32x4 lv[kBatchOf<T>])
 {
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-        const int64_t i = base + (int64_t)u * kStreamThreads + threadIdx.x;
+    for (int u = 0; u < kBatchOf<T>; ++u) {
+        const int64_t i = base + (int64_t)u * T + threadIdx.x;
         lv[u] = u32x4{0u, 0u, 0u, 0u};
         if (!LOCAL || i >= g.items)
             continue;
@@ -455,13 +460,13 @@ __device__ __forceinline__ void load_local(const StreamArgs &a, const Step &g, i
     }
 }
 
-template <int PROTO, bool LOCAL>
+template <int T, int PROTO, bool LOCAL>
 __device__ __forceinline__ void deliver_batch(const StreamArgs &a, const Step &g, int64_t base,
-                                              const u32x4 v[kBatch], const u32x4 lv[kBatch])
+                                              const u32x4 v[kBatchOf<T>], const u32x4 lv[kBatchOf<T>])
 {
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-        const int64_t i = base + (int64_t)u * kStreamThreads + threadIdx.x;
+    for (int u = 0; u < kBatchOf<T>; ++u) {
+        const int64_t i = base + (int64_t)u * T + threadIdx.x;
         if constexpr (PROTO == 1) {
             // payload chunk c: line A's chunk c (c < 7); line A's chunk 7
             // data then line B's chunk 0 low half (c == 7); line B's chunk
@@ -488,17 +493,18 @@ __device__ __forceinline__ void deliver_batch(const StreamArgs &a, const Step &g
 
 // The batch's loads have returned (their registers are read by an empty
 // asm statement, so the compiler waits for exactly these loads).
-__device__ __forceinline__ void loads_returned(const u32x4 v[kBatch])
+template <int T>
+__device__ __forceinline__ void loads_returned(const u32x4 v[kBatchOf<T>])
 {
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u)
+    for (int u = 0; u < kBatchOf<T>; ++u)
         asm volatile("" ::"v"(v[u]));
 }
 
 // ---------------------------------------------------------------------------
 // Producer: the batches of the channel's steps in order, each batch's source
 // loads issued before the previous batch's ring stores.
-template <int PROTO>
+template <int T, int PROTO>
 __device__ void produce(const StreamArgs &a, int c, int64_t s0, int64_t steps, uint64_t first,
                         Shared *sh)
 {
@@ -507,18 +513,18 @@ __device__ void produce(const StreamArgs &a, int c, int64_t s0, int64_t steps, u
     uint8_t *ring = a.fifo + (int64_t)c * 8 * a.wire_bytes;
     uint64_t head_seen = first;      // the consumer has taken every step before `first`
     Cursor cur{0, 0, step_at<PROTO>(a, ring, s0, first, 0)};
-    u32x4 d[kBatch];
-    load_src<PROTO>(a, cur.g, 0, d);
+    u32x4 d[kBatchOf<T>];
+    load_src<T, PROTO>(a, cur.g, 0, d);
     for (;;) {
         Cursor nxt;
         const bool more = advance<PROTO>(a, ring, s0, first, steps, cur, &nxt);
-        u32x4 nd[kBatch];
+        u32x4 nd[kBatchOf<T>];
         if (more)
-            load_src<PROTO>(a, nxt.g, nxt.base, nd);
+            load_src<T, PROTO>(a, nxt.g, nxt.base, nd);
         if (cur.base == 0 && cur.j >= 8 &&
             !wait_counter(a, sh, a.head + c, cur.g.k - 7, &head_seen))
             return;
-        store_ring<PROTO>(cur.g, cur.base, d);
+        store_ring<T, PROTO>(cur.g, cur.base, d);
         if (PROTO == 1) {
             // this batch's data is acknowledged before any of its flags
             drain_memory();
@@ -526,7 +532,7 @@ __device__ void produce(const StreamArgs &a, int c, int64_t s0, int64_t steps, u
             const int64_t end = cur.base + kPerBatch < cur.g.items ? cur.base + kPerBatch
                                                                     : cur.g.items;
             const uint64_t f = cur.g.k + 1;
-            for (int64_t l = cur.base / 8 + threadIdx.x; l < end / 8; l += kStreamThreads)
+            for (int64_t l = cur.base / 8 + threadIdx.x; l < end / 8; l += T)
                 store8_sys(cur.g.slot, (uint32_t)(128 * l + 120),
                            u32x2{(uint32_t)f, (uint32_t)(f >> 32)});
         }
@@ -541,7 +547,7 @@ __device__ void produce(const StreamArgs &a, int c, int64_t s0, int64_t steps, u
             return;
         cur = nxt;
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u)
+        for (int u = 0; u < kBatchOf<T>; ++u)
             d[u] = nd[u];
     }
 }
@@ -563,13 +569,13 @@ __device__ bool close_step(const StreamArgs &a, int c, uint64_t k, bool failed)
 // any wait of the launch has failed).  While items are missing, only the
 // earliest of them is polled, since the producer stores a lane's items in
 // that order; once it is valid the missing items are all read again.
-template <typename Offset, typename Valid>
-__device__ bool poll_batch(const StreamArgs &a, u32x4 v[kBatch], bool ok[kBatch], Rsrc slot,
+template <int T, typename Offset, typename Valid>
+__device__ bool poll_batch(const StreamArgs &a, u32x4 v[kBatchOf<T>], bool ok[kBatchOf<T>], Rsrc slot,
                            Offset off, Valid valid)
 {
     bool all = true;
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u)
+    for (int u = 0; u < kBatchOf<T>; ++u)
         all = all && ok[u];
     for (uint32_t s = 0; !all && s < a.max_spins; ++s) {
         respin();
@@ -577,18 +583,18 @@ __device__ bool poll_batch(const StreamArgs &a, u32x4 v[kBatch], bool ok[kBatch]
             break;
         int lead = 0;
 #pragma unroll
-        for (int u = kBatch - 1; u >= 0; --u)
+        for (int u = kBatchOf<T> - 1; u >= 0; --u)
             if (!ok[u])
                 lead = u;
         if (!valid(load16_sys(slot, off(lead))))
             continue;
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u)
+        for (int u = 0; u < kBatchOf<T>; ++u)
             if (!ok[u])
                 v[u] = load16_sys(slot, off(u));
         all = true;
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
+        for (int u = 0; u < kBatchOf<T>; ++u) {
             ok[u] = ok[u] || valid(v[u]);
             all = all && ok[u];
         }
@@ -601,57 +607,57 @@ __device__ bool poll_batch(const StreamArgs &a, u32x4 v[kBatch], bool ok[kBatch]
 // LL: every line validates itself, so the next batch (also of the next step)
 // is loaded before this batch is delivered; lines not yet written are
 // re-polled.
-template <bool LOCAL>
+template <int T, bool LOCAL>
 __device__ void consume_ll(const StreamArgs &a, int c, int64_t s0, int64_t steps, uint64_t first)
 {
     if (steps <= 0)
         return;
     uint8_t *ring = a.fifo + (int64_t)c * 8 * a.wire_bytes;
     Cursor cur{0, 0, step_at<0>(a, ring, s0, first, 0)};
-    u32x4 v[kBatch], lv[kBatch];
-    load_ring<0>(cur.g, 0, v);
-    load_local<0, LOCAL>(a, cur.g, 0, lv);
+    u32x4 v[kBatchOf<T>], lv[kBatchOf<T>];
+    load_ring<T, 0>(cur.g, 0, v);
+    load_local<T, 0, LOCAL>(a, cur.g, 0, lv);
     bool failed = false;
     for (;;) {
         const uint32_t flag = (uint32_t)(cur.g.k + 1);
         const int64_t i0 = cur.base + threadIdx.x;
         auto valid = [&](u32x4 x) { return x.y == flag && x.w == flag; };
-        bool ok[kBatch];
+        bool ok[kBatchOf<T>];
         bool ahead = true;       // every line was there on the first look
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            ok[u] = i0 + (int64_t)u * kStreamThreads >= cur.g.items || valid(v[u]);
+        for (int u = 0; u < kBatchOf<T>; ++u) {
+            ok[u] = i0 + (int64_t)u * T >= cur.g.items || valid(v[u]);
             ahead = ahead && ok[u];
         }
         if (!failed)
-            failed = !poll_batch(
+            failed = !poll_batch<T>(
                 a, v, ok, cur.g.slot,
-                [&](int u) { return (uint32_t)(16 * (i0 + (int64_t)u * kStreamThreads)); },
+                [&](int u) { return (uint32_t)(16 * (i0 + (int64_t)u * T)); },
                 valid);
         Cursor nxt;
         const bool more = advance<0>(a, ring, s0, first, steps, cur, &nxt);
-        loads_returned(v);
+        loads_returned<T>(v);
         if (nxt.j != cur.j && !close_step(a, c, cur.g.k, failed))
             return;
         // With the producer ahead, the next batch is loaded before this one
         // is delivered; a lane that had to wait delivers first, so that its
         // next look does not find lines not yet written.
-        u32x4 nv[kBatch], nlv[kBatch];
+        u32x4 nv[kBatchOf<T>], nlv[kBatchOf<T>];
         if (more && ahead) {
-            load_ring<0>(nxt.g, nxt.base, nv);
-            load_local<0, LOCAL>(a, nxt.g, nxt.base, nlv);
+            load_ring<T, 0>(nxt.g, nxt.base, nv);
+            load_local<T, 0, LOCAL>(a, nxt.g, nxt.base, nlv);
         }
         if (!failed)
-            deliver_batch<0, LOCAL>(a, cur.g, cur.base, v, lv);
+            deliver_batch<T, 0, LOCAL>(a, cur.g, cur.base, v, lv);
         if (more && !ahead) {
-            load_ring<0>(nxt.g, nxt.base, nv);
-            load_local<0, LOCAL>(a, nxt.g, nxt.base, nlv);
+            load_ring<T, 0>(nxt.g, nxt.base, nv);
+            load_local<T, 0, LOCAL>(a, nxt.g, nxt.base, nlv);
         }
         if (!more)
             return;
         cur = nxt;
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
+        for (int u = 0; u < kBatchOf<T>; ++u) {
             v[u] = nv[u];
             lv[u] = nlv[u];
         }
@@ -686,7 +692,7 @@ __device__ __forceinline__ uint64_t read_flag64(Rsrc slot, uint32_t off)
 // line's flag checked, and chunk 7 of lines whose flag has not arrived yet
 // re-read.  Lane 0 reads the next batch's first flag together with this
 // batch's data, and the next batch is loaded before this one is delivered.
-template <bool LOCAL>
+template <int T, bool LOCAL>
 __device__ void consume_ll128(const StreamArgs &a, int c, int64_t s0, int64_t steps,
                               uint64_t first, Shared *sh)
 {
@@ -698,9 +704,9 @@ __device__ void consume_ll128(const StreamArgs &a, int c, int64_t s0, int64_t st
     uint64_t pre = threadIdx.x == 0 ? read_flag64(cur.g.slot, flag_at(0)) : 0;
     if (!wait_flag64(a, sh, cur.g.slot, flag_at(0), cur.g.k + 1, pre))
         return;
-    u32x4 v[kBatch], lv[kBatch];
-    load_ring<1>(cur.g, 0, v);
-    load_local<1, LOCAL>(a, cur.g, 0, lv);
+    u32x4 v[kBatchOf<T>], lv[kBatchOf<T>];
+    load_ring<T, 1>(cur.g, 0, v);
+    load_local<T, 1, LOCAL>(a, cur.g, 0, lv);
     bool failed = false;
     for (;;) {
         Cursor nxt;
@@ -711,38 +717,38 @@ __device__ void consume_ll128(const StreamArgs &a, int c, int64_t s0, int64_t st
         const uint32_t flo = (uint32_t)flag, fhi = (uint32_t)(flag >> 32);
         const int64_t q0 = cur.base + threadIdx.x;
         auto valid = [&](u32x4 x) { return x.z == flo && x.w == fhi; };
-        bool ok[kBatch];
+        bool ok[kBatchOf<T>];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int64_t q = q0 + (int64_t)u * kStreamThreads;
+        for (int u = 0; u < kBatchOf<T>; ++u) {
+            const int64_t q = q0 + (int64_t)u * T;
             ok[u] = q >= cur.g.items || (q & 7) != 7 || valid(v[u]);
         }
         // only flag chunks can be missing; a re-read takes the line's chunk 7
         if (!failed)
-            failed = !poll_batch(
+            failed = !poll_batch<T>(
                 a, v, ok, cur.g.slot,
                 [&](int u) {
-                    const int64_t q = q0 + (int64_t)u * kStreamThreads;
+                    const int64_t q = q0 + (int64_t)u * T;
                     return (uint32_t)(128 * (q >> 3) + 112);
                 },
                 valid);
-        loads_returned(v);
+        loads_returned<T>(v);
         if (nxt.j != cur.j && !close_step(a, c, cur.g.k, failed))
             return;
         if (more && !wait_flag64(a, sh, nxt.g.slot, flag_at(nxt.base), nxt.g.k + 1, pre))
             return;
-        u32x4 nv[kBatch], nlv[kBatch];
+        u32x4 nv[kBatchOf<T>], nlv[kBatchOf<T>];
         if (more) {
-            load_ring<1>(nxt.g, nxt.base, nv);
-            load_local<1, LOCAL>(a, nxt.g, nxt.base, nlv);
+            load_ring<T, 1>(nxt.g, nxt.base, nv);
+            load_local<T, 1, LOCAL>(a, nxt.g, nxt.base, nlv);
         }
         if (!failed)
-            deliver_batch<1, LOCAL>(a, cur.g, cur.base, v, lv);
+            deliver_batch<T, 1, LOCAL>(a, cur.g, cur.base, v, lv);
         if (!more)
             return;
         cur = nxt;
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
+        for (int u = 0; u < kBatchOf<T>; ++u) {
             v[u] = nv[u];
             lv[u] = nlv[u];
         }
@@ -752,7 +758,7 @@ __device__ void consume_ll128(const StreamArgs &a, int c, int64_t s0, int64_t st
 // Simple: a step is read only after its tail; within a step (and across a
 // step boundary when the tail already covers the next step) the next batch
 // is loaded before this one is delivered.
-template <bool LOCAL>
+template <int T, bool LOCAL>
 __device__ void consume_simple(const StreamArgs &a, int c, int64_t s0, int64_t steps,
                                uint64_t first, Shared *sh)
 {
@@ -763,29 +769,29 @@ __device__ void consume_simple(const StreamArgs &a, int c, int64_t s0, int64_t s
     Cursor cur{0, 0, step_at<2>(a, ring, s0, first, 0)};
     if (!wait_counter(a, sh, a.tail + c, cur.g.k + 1, &tail_seen))
         return;
-    u32x4 v[kBatch], lv[kBatch];
-    load_ring<2>(cur.g, 0, v);
-    load_local<2, LOCAL>(a, cur.g, 0, lv);
+    u32x4 v[kBatchOf<T>], lv[kBatchOf<T>];
+    load_ring<T, 2>(cur.g, 0, v);
+    load_local<T, 2, LOCAL>(a, cur.g, 0, lv);
     for (;;) {
         Cursor nxt;
         const bool more = advance<2>(a, ring, s0, first, steps, cur, &nxt);
-        loads_returned(v);
+        loads_returned<T>(v);
         if (nxt.j != cur.j && !close_step(a, c, cur.g.k, false))
             return;
         if (more && nxt.j != cur.j &&
             !wait_counter(a, sh, a.tail + c, nxt.g.k + 1, &tail_seen))
             return;
-        u32x4 nv[kBatch], nlv[kBatch];
+        u32x4 nv[kBatchOf<T>], nlv[kBatchOf<T>];
         if (more) {
-            load_ring<2>(nxt.g, nxt.base, nv);
-            load_local<2, LOCAL>(a, nxt.g, nxt.base, nlv);
+            load_ring<T, 2>(nxt.g, nxt.base, nv);
+            load_local<T, 2, LOCAL>(a, nxt.g, nxt.base, nlv);
         }
-        deliver_batch<2, LOCAL>(a, cur.g, cur.base, v, lv);
+        deliver_batch<T, 2, LOCAL>(a, cur.g, cur.base, v, lv);
         if (!more)
             return;
         cur = nxt;
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
+        for (int u = 0; u < kBatchOf<T>; ++u) {
             v[u] = nv[u];
             lv[u] = nlv[u];
         }
@@ -796,8 +802,8 @@ __device__ void consume_simple(const StreamArgs &a, int c, int64_t s0, int64_t s
 // a local addend the kernel keeps to 128 VGPRs (4 wavefronts per SIMD), so
 // two workgroups fit on a CU and up to 256 channels can run at once; with one
 // it has two wavefronts per SIMD.
-template <int PROTO, bool LOCAL>
-__global__ __launch_bounds__(kStreamThreads, LOCAL ? 2 : 4) void stream_kernel(StreamArgs a)
+template <int T, int PROTO, bool LOCAL>
+__global__ __launch_bounds__(T, T == kWideThreads || !LOCAL ? 4 : 2) void stream_kernel(StreamArgs a)
 {
     __shared__ Shared sh;
     const int b = blockIdx.x;
@@ -817,15 +823,15 @@ __global__ __launch_bounds__(kStreamThreads, LOCAL ? 2 : 4) void stream_kernel(S
     const int64_t s0 = (int64_t)c * a.total_steps / a.channels;
     const int64_t s1 = (int64_t)(c + 1) * a.total_steps / a.channels;
     if (producer) {
-        produce<PROTO>(a, c, s0, s1 - s0, first, &sh);
+        produce<T, PROTO>(a, c, s0, s1 - s0, first, &sh);
         return;
     }
     if (PROTO == 0)
-        consume_ll<LOCAL>(a, c, s0, s1 - s0, first);
+        consume_ll<T, LOCAL>(a, c, s0, s1 - s0, first);
     else if (PROTO == 1)
-        consume_ll128<LOCAL>(a, c, s0, s1 - s0, first, &sh);
+        consume_ll128<T, LOCAL>(a, c, s0, s1 - s0, first, &sh);
     else
-        consume_simple<LOCAL>(a, c, s0, s1 - s0, first, &sh);
+        consume_simple<T, LOCAL>(a, c, s0, s1 - s0, first, &sh);
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint64_t done = __hip_atomic_fetch_add(a.state + 1, (uint64_t)1, __ATOMIC_ACQ_REL,
@@ -839,26 +845,32 @@ __global__ __launch_bounds__(kStreamThreads, LOCAL ? 2 : 4) void stream_kernel(S
     }
 }
 
-static const void *stream_fn(int proto, bool local)
+template <int T>
+static const void *stream_fn_t(int proto, bool local)
 {
     if (local)
-        return proto == 0   ? reinterpret_cast<const void *>(&stream_kernel<0, true>)
-               : proto == 1 ? reinterpret_cast<const void *>(&stream_kernel<1, true>)
-                            : reinterpret_cast<const void *>(&stream_kernel<2, true>);
-    return proto == 0   ? reinterpret_cast<const void *>(&stream_kernel<0, false>)
-           : proto == 1 ? reinterpret_cast<const void *>(&stream_kernel<1, false>)
-                        : reinterpret_cast<const void *>(&stream_kernel<2, false>);
+        return proto == 0   ? reinterpret_cast<const void *>(&stream_kernel<T, 0, true>)
+               : proto == 1 ? reinterpret_cast<const void *>(&stream_kernel<T, 1, true>)
+                            : reinterpret_cast<const void *>(&stream_kernel<T, 2, true>);
+    return proto == 0   ? reinterpret_cast<const void *>(&stream_kernel<T, 0, false>)
+           : proto == 1 ? reinterpret_cast<const void *>(&stream_kernel<T, 1, false>)
+                        : reinterpret_cast<const void *>(&stream_kernel<T, 2, false>);
 }
 
-hipError_t fifo_stream_resident_workgroups(int proto, bool local, int *workgroups)
+static const void *stream_fn(int proto, bool local, bool wide)
+{
+    return wide ? stream_fn_t<kWideThreads>(proto, local) : stream_fn_t<kNarrowThreads>(proto, local);
+}
+
+hipError_t fifo_stream_resident_workgroups(int proto, bool local, bool wide, int *workgroups)
 {
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess)
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stream_fn(proto, local),
-                                                         kStreamThreads, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, stream_fn(proto, local, wide), wide ? kWideThreads : kNarrowThreads, 0);
     *workgroups = e == hipSuccess ? cus * per_cu : 0;
     return e;
 }
@@ -867,7 +879,7 @@ hipError_t launch_fifo_stream(int proto, const float *src, const float *local, f
                               int64_t n, void *fifo, uint64_t *counters, int channels,
                               int64_t step_bytes, int64_t wire_bytes, uint64_t first_step,
                               bool from_state, uint32_t max_spins, uint32_t *errors,
-                              hipStream_t s)
+                              bool wide, hipStream_t s)
 {
     StreamArgs a;
     a.src = reinterpret_cast<const uint32_t *>(src);
@@ -888,8 +900,8 @@ hipError_t launch_fifo_stream(int proto, const float *src, const float *local, f
     a.first_step = first_step;
     a.max_spins = max_spins;
     void *args[] = {&a};
-    return hipLaunchKernel(stream_fn(proto, local != nullptr), dim3(2 * channels),
-                           dim3(kStreamThreads), args, 0, s);
+    return hipLaunchKernel(stream_fn(proto, local != nullptr, wide), dim3(2 * channels),
+                           dim3(wide ? kWideThreads : kNarrowThreads), args, 0, s);
 }
 
 }  // namespace ar

@@ -95,6 +95,18 @@ def test_stream_bench_configurations(gpu, name, step, channels):
     f.run(src, cont=True)
 
 
+@pytest.mark.parametrize("name,step", [("ll", 1024), ("ll128", 1200), ("simple", 1024)])
+def test_stream_256_channels(gpu, name, step):
+    """256 channels need two workgroups per CU: the 512-lane geometry where
+    the 1,024-lane one does not fit twice, with three steps per channel and a
+    ragged tail, called twice from the stored step."""
+    n = 256 * 3 * step // 4 - 3
+    src = synth.wire_payloads(1, n, [107, step])[0]
+    f = Fifo(PROTOS[name], step, 256, gpu)
+    f.run(src, cont=True)
+    f.run(src, cont=True)
+
+
 def test_stream_workgroups_that_cannot_be_resident_are_refused(gpu):
     """256 channels need 512 resident workgroups; where a variant cannot
     have them the call is refused before anything runs, else it is exact."""
