@@ -374,8 +374,10 @@ ar_status_t ll128_unpack_reduce(const void *const *fifos, int W, float *out,
  *               is unspecified and fifo/counters must be zeroed before reuse
  *   src, local, out  n fp32, 4-byte aligned; out may equal local, no other
  *               overlap among the buffers                 else AR_ERR_ARG
- * The 2 * channels workgroups must be resident together: AR_ERR_CAPACITY if
- * the device cannot hold them at once.  Work from other streams that holds
+ * The 2 * channels workgroups must be resident together.  They have 1,024
+ * lanes when the device holds 2 * channels such workgroups at once, else
+ * 512 lanes; AR_ERR_CAPACITY if it cannot hold them in either form (with
+ * local, more than 128 channels on MI355X).  Work from other streams that holds
  * compute units while a call runs can delay a consumer or producer; the
  * bounded waits then end the launch with errors[0] != 0.
  */
