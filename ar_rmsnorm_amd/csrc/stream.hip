@@ -149,11 +149,17 @@ __device__ __forceinline__ bool aborted(const uint32_t *errors)
 {
     return __hip_atomic_load(errors, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
 }
-// The wavefront's loads have returned and its stores are acknowledged (on
-// gfx950 a workgroup-scope release fence is s_waitcnt vmcnt(0) lgkmcnt(0)).
+// The wavefront's loads have returned and its stores are acknowledged: an
+// explicit wait.  A workgroup-scope release fence is not enough here: on
+// gfx950 it emits no wait for vector memory (the waves of a workgroup share
+// one CU), so the stores of a batch could still be in flight when the flags
+// that publish them go out.  System-coherent (sc0 sc1) stores are
+// acknowledged once they are visible at that scope, so no L2 write-back is
+// needed.  The memory clobber keeps the compiler from moving memory
+// accesses across the wait.
 __device__ __forceinline__ void drain_memory()
 {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // Per-workgroup LDS slots for broadcasting lane 0's results.

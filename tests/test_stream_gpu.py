@@ -169,6 +169,46 @@ def test_stream_graph_replays_continue(gpu, name, step, channels):
     del g
 
 
+@pytest.mark.parametrize("name,step", [("ll", 32768), ("ll128", 120000), ("simple", 65536)])
+def test_stream_producers_and_consumers_on_different_xcds(gpu, name, step):
+    """Workgroups go round-robin to the 8 XCDs, whose L2 caches are not
+    coherent with each other; with 100 channels a channel's producer (block
+    c) and consumer (block 100 + c) sit on different XCDs.  Twenty-four
+    calls in a row are captured in a graph, each into its own output, and
+    the graph is replayed twice: every call must deliver the oracle's
+    payload with no failed wait.  Data published before its stores were
+    acknowledged showed up here as a few stale lines in about one call in
+    a hundred."""
+    proto, ch, n, calls = PROTOS[name], 100, 4 * 1024 * 1024 + 5, 24
+    src = synth.wire_payloads(1, n, [108, step])[0]
+    want, _ = orc.fifo_stream(proto, src, ch, step, 0)
+    want = torch.from_numpy(want).to(gpu)
+    f = Fifo(proto, step, ch, gpu)
+    d = torch.from_numpy(src).to(gpu)
+    outs = [torch.zeros(n, dtype=torch.float32, device=gpu) for _ in range(calls)]
+    f.launch(d, outs[0], n, cont=True)      # warm-up call outside the graph
+    sync()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for o in outs:
+            f.launch(d, o, n, cont=True)
+    torch.cuda.current_stream().wait_stream(s)
+    sync()
+    for r in range(2):
+        for o in outs:
+            o.zero_()
+        sync()
+        g.replay()
+        sync()
+        assert int(f.errors.item()) == 0, "a wait timed out"
+        bad = [i for i, o in enumerate(outs) if not torch.equal(o.view(torch.int32),
+                                                                 want.view(torch.int32))]
+        assert not bad, f"replay {r}: calls {bad} delivered wrong payload"
+    del g
+
+
 def test_stream_aborted_launch_ends(gpu):
     """The error count is set before the launch, so every wait gives up at
     once: the launch must end (outputs unspecified)."""
