@@ -169,8 +169,9 @@ def test_stream_graph_replays_continue(gpu, name, step, channels):
     del g
 
 
+@pytest.mark.parametrize("with_local", [False, True])
 @pytest.mark.parametrize("name,step", [("ll", 32768), ("ll128", 120000), ("simple", 65536)])
-def test_stream_producers_and_consumers_on_different_xcds(gpu, name, step):
+def test_stream_producers_and_consumers_on_different_xcds(gpu, name, step, with_local):
     """Workgroups go round-robin to the 8 XCDs, whose L2 caches are not
     coherent with each other; with 100 channels a channel's producer (block
     c) and consumer (block 100 + c) sit on different XCDs.  Twenty-four
@@ -180,20 +181,23 @@ def test_stream_producers_and_consumers_on_different_xcds(gpu, name, step):
     acknowledged showed up here as a few stale lines in about one call in
     a hundred."""
     proto, ch, n, calls = PROTOS[name], 100, 4 * 1024 * 1024 + 5, 24
-    src = synth.wire_payloads(1, n, [108, step])[0]
-    want, _ = orc.fifo_stream(proto, src, ch, step, 0)
+    src, local = synth.wire_payloads(2, n, [108, step])
+    if not with_local:
+        local = None
+    want, _ = orc.fifo_stream(proto, src, ch, step, 0, local=local)
     want = torch.from_numpy(want).to(gpu)
     f = Fifo(proto, step, ch, gpu)
     d = torch.from_numpy(src).to(gpu)
+    dl = None if local is None else torch.from_numpy(local).to(gpu)
     outs = [torch.zeros(n, dtype=torch.float32, device=gpu) for _ in range(calls)]
-    f.launch(d, outs[0], n, cont=True)      # warm-up call outside the graph
+    f.launch(d, outs[0], n, dl, cont=True)      # warm-up call outside the graph
     sync()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         for o in outs:
-            f.launch(d, o, n, cont=True)
+            f.launch(d, o, n, dl, cont=True)
     torch.cuda.current_stream().wait_stream(s)
     sync()
     for r in range(2):
