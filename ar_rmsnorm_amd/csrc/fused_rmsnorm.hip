@@ -21,8 +21,10 @@ namespace ar {
 // Lamport data-as-flag reading ([TRIAR] "Option 2: Lamport"): the inputs are
 // the W slots of this rank's comm buffer, filled by the ranks' pushes; a
 // 16-byte chunk is ready once none of its four words is the sentinel (two
-// bf16 -0.0, which a scrubbed push can never write).  After use, the slots
-// of the previous call's region are reset to the sentinel.
+// bf16 -0.0, which a scrubbed push can never write).  Each call also resets
+// the slots of the previous call's region to the sentinel; that region is
+// neither read nor pushed to by the call, so the reset goes out together
+// with the first loads.
 constexpr uint32_t kLamportSentinel = 0x80008000u;
 
 template <int W>
@@ -151,6 +153,19 @@ __global__ __launch_bounds__(NT) void fused_rmsnorm_kernel(
         }
     }
     if (LAMPORT) {
+        // the previous call's region is neither read nor pushed to by this
+        // call, so its sentinel goes out now, while the loads are in flight
+        const u32x4 sent = {kLamportSentinel, kLamportSentinel, kLamportSentinel,
+                            kLamportSentinel};
+#pragma unroll
+        for (int p = 0; p < PPL; ++p) {
+            const int idx = t + p * NT;
+            if (idx < packs_per_row) {
+#pragma unroll
+                for (int r = 0; r < W; ++r)
+                    st_stream(la.reset[r] + row0 + idx, sent);
+            }
+        }
         uint32_t bad = 0;
 #pragma unroll
         for (int p = 0; p < PPL; ++p) {
@@ -186,13 +201,6 @@ __global__ __launch_bounds__(NT) void fused_rmsnorm_kernel(
         const int idx = t + p * NT;
         if (idx < packs_per_row) {
             norm_out[row0 + idx] = normalize8(h[p], rms, wv[p]);
-            if (LAMPORT) {
-                const u32x4 sent = {kLamportSentinel, kLamportSentinel, kLamportSentinel,
-                                    kLamportSentinel};
-#pragma unroll
-                for (int r = 0; r < W; ++r)
-                    st_stream(la.reset[r] + row0 + idx, sent);
-            }
         }
     }
 }
