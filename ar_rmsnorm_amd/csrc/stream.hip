@@ -16,12 +16,13 @@
 //           16-byte access, so a line is ready once both flags are k + 1.
 //   LL128   128-byte lines, 120 payload bytes + a 64-bit flag.  gfx950 does
 //           not promise that a line written by eight lanes becomes visible
-//           as a whole, so the producer makes the order explicit: all data
-//           of the step, then a release fence, then the flag words.  The
-//           consumer waits for one flag of the step (after which every data
-//           byte of the step is visible), then reads every line and checks
-//           every line's flag, re-reading the flag chunk of lines whose flag
-//           has not arrived yet.
+//           as a whole, so the producer makes the order explicit per batch
+//           of 4,096 chunks: the batch's data, then a wait until those
+//           stores are acknowledged and a barrier, then the batch's flag
+//           words.  The consumer waits for the flag of the batch's first
+//           line (after which every data byte of the batch is visible), then
+//           reads every line and checks every line's flag, re-reading the
+//           flag chunk of lines whose flag has not arrived yet.
 //   Simple  raw payload; the producer publishes a tail step once the step's
 //           data is acknowledged, and the consumer waits for it.
 // For every protocol the consumer publishes a head step (the next step it
@@ -60,9 +61,9 @@
 namespace ar {
 
 // A batch is kPerBatch items of one step.  Two launch geometries cover it:
-// 1,024 lanes with 4 items in flight each when one workgroup per CU is enough
-// for 2 x channels, else 512 lanes with 8 each (two workgroups per CU, up to
-// 256 channels).  The wider one hides more of each batch's round trips.
+// 1,024 lanes with 4 items in flight each when the device holds 2 x channels
+// such workgroups at once, else 512 lanes with 8 each (two workgroups per CU,
+// up to 256 channels).  The wider one hides more of each batch's round trips.
 constexpr int64_t kPerBatch = 4096;
 constexpr int kWideThreads = 1024;
 constexpr int kNarrowThreads = 512;
