@@ -53,7 +53,9 @@ LIBAR_EXPORT const char *ar_status_str(ar_status_t status)
     case AR_ERR_ARG: return "invalid size, flag or buffer aliasing";
     case AR_ERR_ALIGN: return "pointer not aligned as required";
     case AR_ERR_WORLD: return "number of rank buffers W out of range";
-    case AR_ERR_CAPACITY: return "payload does not fit the 8 steps of the FIFO";
+    case AR_ERR_CAPACITY:
+        return "payload does not fit the 8 steps of the FIFO, or the streaming "
+               "workgroups cannot all be resident at once";
     case AR_ERR_HIP: return "HIP runtime rejected the launch";
     default: return "unknown status";
     }

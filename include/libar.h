@@ -49,7 +49,9 @@ typedef int ar_status_t;
 #define AR_ERR_ARG 2       /* a size, flag or aliasing rule is violated */
 #define AR_ERR_ALIGN 3     /* a pointer lacks the required alignment */
 #define AR_ERR_WORLD 4     /* W outside the supported range */
-#define AR_ERR_CAPACITY 5  /* the payload does not fit the FIFO's 8 steps */
+#define AR_ERR_CAPACITY 5  /* the payload does not fit the FIFO's 8 steps, or
+                              (ar_fifo_stream) its workgroups cannot all be
+                              resident at once */
 #define AR_ERR_HIP 6       /* the HIP runtime rejected a launch */
 
 #define AR_MAX_WORLD 8          /* W <= 8 rank buffers */
