@@ -75,6 +75,18 @@ __device__ __forceinline__ u32x4 reload16(const u32x4 *p)
     return *reinterpret_cast<const volatile u32x4 *>(p);
 }
 
+// System-coherent (sc0 sc1) load of 16-byte chunk idx of a row of `count`
+// chunks whose base is the same for the whole workgroup (the buffer
+// descriptor lives in scalar registers).  Unlike a volatile access, which on
+// gfx950 waits for its own completion, several of these can be in flight at
+// once; a poll loop needs a compiler barrier per spin so that it reloads.
+__device__ __forceinline__ u32x4 load16_coherent(const u32x4 *row, int idx, int count)
+{
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u32x4 *>(row), 0, count * 16, 0x00020000 /* 32-bit data format */);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, idx * 16, 0, 1 | 16 /* sc0 | sc1 */);
+}
+
 // Kernel-argument pointer tables, passed by value so no device-side
 // indirection is needed (the W pointers land in SGPRs).
 template <int W>

@@ -166,24 +166,47 @@ __global__ __launch_bounds__(NT) void fused_rmsnorm_kernel(
                     st_stream(la.reset[r] + row0 + idx, sent);
             }
         }
-        uint32_t bad = 0;
+        // Chunks that still hold the sentinel are re-read, all of a lane's
+        // together, with system-coherent loads, a bounded number of times.
+        // The own slot of the one-launch form holds the scrubbed push, which
+        // is never the sentinel.
+        auto missing = [&](int p, int r) {
+            return t + p * NT < packs_per_row && has_sentinel(xv[p][r]);
+        };
+        bool all = true;
 #pragma unroll
-        for (int p = 0; p < PPL; ++p) {
-            const int idx = t + p * NT;
-            if (idx < packs_per_row) {
+        for (int p = 0; p < PPL; ++p)
 #pragma unroll
-                for (int r = 0; r < W; ++r) {
-                    bool ok = (PUSH && r == la.rank) || !has_sentinel(xv[p][r]);
-                    for (uint32_t s = 0; !ok && s < la.max_spins; ++s) {
-                        xv[p][r] = reload16(in.p[r] + row0 + idx);
-                        ok = !has_sentinel(xv[p][r]);
-                    }
-                    bad += ok ? 0u : 1u;
-                }
+            for (int r = 0; r < W; ++r)
+                all = all && !missing(p, r);
+        if (!all) {
+            for (uint32_t s = 0; s < la.max_spins; ++s) {
+                asm volatile("" ::: "memory");   // reload on every spin
+#pragma unroll
+                for (int p = 0; p < PPL; ++p)
+#pragma unroll
+                    for (int r = 0; r < W; ++r)
+                        if (missing(p, r))
+                            xv[p][r] = load16_coherent(in.p[r] + row0, t + p * NT,
+                                                       packs_per_row);
+                all = true;
+#pragma unroll
+                for (int p = 0; p < PPL; ++p)
+#pragma unroll
+                    for (int r = 0; r < W; ++r)
+                        all = all && !missing(p, r);
+                if (all)
+                    break;
             }
+            uint32_t bad = 0;
+#pragma unroll
+            for (int p = 0; p < PPL; ++p)
+#pragma unroll
+                for (int r = 0; r < W; ++r)
+                    bad += missing(p, r) ? 1u : 0u;
+            if (bad && la.bad)
+                atomicAdd(la.bad, bad);
         }
-        if (bad && la.bad)
-            atomicAdd(la.bad, bad);
     }
 
     float h[PPL][8];
