@@ -570,10 +570,12 @@ def main():
                     hfifos = [np.zeros(8 * sl * lsize, np.uint8) for _ in host_payloads]
                     for hp, hf in zip(host_payloads, hfifos):
                         opack(hp, hf, sl)
-                row(f"{tag}_decode", dec_bytes,
-                    [lambda d=d, sl=sl: unpack(d[0], d[1], sl) for d in dsets],
-                    steps=8 * len(dsets),
-                    oracle_fn=orc and (lambda hf=hfifos, nn=nn, sl=sl: ounpack(hf, nn, sl)))
+                r = row(f"{tag}_decode", dec_bytes,
+                        [lambda d=d, sl=sl: unpack(d[0], d[1], sl) for d in dsets],
+                        steps=8 * len(dsets),
+                        oracle_fn=orc and (lambda hf=hfifos, nn=nn, sl=sl: ounpack(hf, nn, sl)))
+                # payload rate: W payloads in, one sum out, at 4 bytes a value
+                r["payload_GBps"] = round((wc["W"] + 1) * 4 * nn / (r["us_per_call"] * 1e3), 1)
                 del dsets
                 pack_bytes = 4 * nn + L * lsize
                 offsets = (0, 1) if nn == wc["n"] else (0,)
