@@ -344,9 +344,10 @@ ar_status_t ll128_unpack_reduce(const void *const *fifos, int W, float *out,
  *   AR_PROTO_LL      16-byte lines of 8 payload bytes + two 32-bit flags
  *                    (k + 1), ready when both flags match
  *   AR_PROTO_LL128   128-byte lines of 120 payload bytes + a 64-bit flag
- *                    (k + 1); the producer writes a step's data, fences,
- *                    then its flags; the consumer acquires one flag of the
- *                    step, then reads every line and checks its flag
+ *                    (k + 1); per batch of 512 lines the producer writes the
+ *                    data, waits until those stores are acknowledged, then
+ *                    writes the flags; the consumer waits for the batch's
+ *                    first flag, then reads every line and checks its flag
  *   AR_PROTO_SIMPLE  raw payload; ready when the channel's tail counter
  *                    reaches k + 1
  * After each step the consumer sets the channel's head counter to k + 1; the
