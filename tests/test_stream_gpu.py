@@ -83,8 +83,10 @@ def test_stream_nccl_default_steps_wire_workload(gpu, name, step, channels):
     Fifo(PROTOS[name], step, channels, gpu).run(src)
 
 
-@pytest.mark.parametrize("name,step,channels", [("ll", 32768, 128), ("ll128", 576000, 128),
-                                                ("simple", 524288, 128), ("ll", 32768, 256)])
+@pytest.mark.parametrize("name,step,channels", [("ll", 32768, 32), ("ll128", 576000, 32),
+                                                ("simple", 524288, 32), ("ll", 32768, 128),
+                                                ("ll128", 576000, 128), ("simple", 524288, 128),
+                                                ("ll", 32768, 256)])
 def test_stream_bench_configurations(gpu, name, step, channels):
     """The channel counts the bench times, on the wire workload's payload,
     twice in a row from the stored step."""
