@@ -29,6 +29,24 @@
 namespace ar {
 
 constexpr int kWireThreads = 256;
+
+// Write-through stores (sc0 sc1): the line goes to memory with the store, so
+// the kernel ends with no dirty L2 lines of it to write back.  Measured per
+// kernel against the nontemporal stores, 16 Mi values, W=4: the LL decoder's
+// output stores gain (98.1 -> 94.4 us from cold HBM); the LL128 encoder's
+// FIFO stores gain when its source is still in the Infinity Cache (23.4 ->
+// 19.5 us) and are even from cold HBM (23.7 -> 23.3 us).  The LL128 decoder
+// (58 -> 62 us), the reduce kernels and the LL encoder lose or do not gain,
+// so they keep nontemporal stores.  These are the last memory operations of
+// their kernels, so nothing waits on them inside the kernel.
+__device__ __forceinline__ void st16_through(u32x4 *p, u32x4 v)
+{
+    asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void st8_through(uint32_t *p, u32x2 v)
+{
+    asm volatile("global_store_dwordx2 %0, %1, off sc0 sc1" ::"v"(p), "v"(v) : "memory");
+}
 // The LL decoder runs 128-lane workgroups: against 256 lanes, 95.9 instead of
 // 101 us for W=4 FIFOs of 16 Mi values in separate allocations, 1% faster
 // with the FIFOs carved from one allocation; 64 and 512 lanes no better.
@@ -109,8 +127,8 @@ __global__ __launch_bounds__(kLLDecodeThreads) void ll_unpack_reduce_kernel(
     }
     const int64_t e = 2 * (int64_t)i;
     if (e + 1 < n) {
-        st2_stream_a4(reinterpret_cast<uint32_t *>(out + e),
-                      u32x2{__float_as_uint(a0), __float_as_uint(a1)});
+        st8_through(reinterpret_cast<uint32_t *>(out + e),
+                    u32x2{__float_as_uint(a0), __float_as_uint(a1)});
     } else {
         out[e] = a0;
     }
@@ -168,7 +186,7 @@ __global__ __launch_bounds__(kWireThreads) void ll128_pack_kernel(
         o = u32x4{hz, hw, d.x, d.y};
     else
         o = u32x4{hz, hw, (uint32_t)flag, (uint32_t)(flag >> 32)};
-    st_stream(fifo + sp.line * 8 + (c & 7), o);
+    st16_through(fifo + sp.line * 8 + (c & 7), o);
 }
 
 // Decode: eight lanes per line, lane j owning wire chunk j (an aligned
