@@ -215,6 +215,30 @@ def test_stream_producers_and_consumers_on_different_xcds(gpu, name, step, with_
     del g
 
 
+@pytest.mark.parametrize("case", range(12))
+def test_stream_seeded_random_configurations(gpu, case):
+    """Seeded random protocol, channel count (1..200), step size, payload
+    length (from a few values to ~3 steps per channel, so channels without a
+    step, partial last steps and single-step channels all occur), local
+    addend or not (up to 128 channels, all a 256-CU device holds with one),
+    and first step (explicit, then the stored one): two calls
+    on one set of rings, each checked against the oracle, ring bytes
+    included."""
+    rng = np.random.default_rng([109, case])
+    name = ["ll", "ll128", "simple"][case % 3]
+    unit = {"ll": 8, "ll128": 120, "simple": 16}[name]
+    step = unit * int(rng.integers(1, 400))
+    channels = int(rng.integers(1, 201))
+    f = Fifo(PROTOS[name], step, channels, gpu)
+    f.first = int(rng.integers(0, 1 << 20))
+    for call in range(2):
+        n = int(rng.integers(1, 3 * channels * step // 4 + 2))
+        src, local = synth.wire_payloads(2, n, [110, case, call])
+        # with a local addend one workgroup fits per CU: at most 128 channels
+        with_local = channels <= 128 and bool(rng.integers(0, 2))
+        f.run(src, local=local if with_local else None, cont=call == 1)
+
+
 def test_stream_aborted_launch_ends(gpu):
     """The error count is set before the launch, so every wait gives up at
     once: the launch must end (outputs unspecified)."""
