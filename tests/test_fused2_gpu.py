@@ -86,6 +86,16 @@ def test_fused_2stage_shapes(gpu, W, M, N):
     check(xs, res, w, 1e-6, gpu)
 
 
+@pytest.mark.parametrize("case", range(8))
+def test_fused_2stage_seeded_random_shapes(gpu, case):
+    """Seeded random W (2..8), M (1..60, so M < W and remainders occur) and
+    N (any multiple of 8 up to 16,384)."""
+    rng = np.random.default_rng([87, case])
+    W, M, N = int(rng.integers(2, 9)), int(rng.integers(1, 61)), 8 * int(rng.integers(1, 2049))
+    xs, res, w = synth.fused_inputs(W, M, N, [88, case])
+    check(xs, res, w, 1e-6, gpu)
+
+
 def test_fused_2stage_rank_order_matches_one_shot_kernel(gpu):
     """In rank order the two-shot rows come from the same arithmetic as the
     one-shot kernel: both outputs are bit-identical to it."""

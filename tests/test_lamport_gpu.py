@@ -160,8 +160,14 @@ def test_lamport_argument_errors_with_device_buffers(gpu):
     sync()
 
 
+def _random_shapes(seed, count):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(2, 9)), int(rng.integers(1, 9)), 8 * int(rng.integers(1, 2049)))
+            for _ in range(count)]
+
+
 @pytest.mark.parametrize("W,M,N", [(4, 1, 2048), (4, 128, 2048), (2, 3, 8), (8, 2, 16384),
-                                   (3, 5, 1000)])
+                                   (3, 5, 1000)] + _random_shapes(97, 5))
 def test_lamport_oneshot_call(gpu, W, M, N):
     """One rank (a different one each call) makes the one-launch call after
     the other ranks pushed; then the others read.  Everything matches the

@@ -215,6 +215,16 @@ def test_fused_shapes(gpu, W, M, N):
     check_fused(xs, res, w, 1e-6, gpu)
 
 
+@pytest.mark.parametrize("case", range(10))
+def test_fused_seeded_random_shapes(gpu, case):
+    """Seeded random W (2..8), M (1..40) and N (any multiple of 8 up to
+    16,384), so every launch shape and its idle lanes are exercised."""
+    rng = np.random.default_rng([85, case])
+    W, M, N = int(rng.integers(2, 9)), int(rng.integers(1, 41)), 8 * int(rng.integers(1, 2049))
+    xs, res, w = synth.fused_inputs(W, M, N, [86, case])
+    check_fused(xs, res, w, 1e-6, gpu)
+
+
 def test_fused_in_place_and_constant_rows(gpu):
     xs, res, w = synth.fused_inputs(4, 8, 2048, [84])
     check_fused(xs, res, w, 1e-6, gpu, in_place=True)
