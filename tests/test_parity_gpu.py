@@ -146,6 +146,20 @@ def test_2stage_cap_workload_full_compare(gpu):
         assert np.array_equal(tmps[s][:ts.size], ts), f"shard {s}"
 
 
+@pytest.mark.parametrize("case", range(8))
+def test_reduce_seeded_random_sizes(gpu, case):
+    """Seeded random W (2..8) and pack counts (1..200,000): the one-stage
+    result and every rank's two-stage result against the oracle."""
+    rng = np.random.default_rng([89, case])
+    W, P = int(rng.integers(2, 9)), int(rng.integers(1, 200001))
+    xs = synth.reduce_inputs(W, 8 * P, [90, case])
+    assert np.array_equal(run_1stage(xs, gpu), orc.reduce_1stage(xs))
+    outs, _ = run_2stage_all_ranks(xs, gpu)
+    want = orc.reduce_2stage(xs)
+    for o in outs:
+        assert np.array_equal(o, want)
+
+
 @pytest.mark.parametrize("W,P", [(2, 1027), (3, 8 * 300 + 5), (4, 3), (5, 5 * 256 + 4),
                                  (7, 7 * 1000 + 6), (8, 8 * 1000 + 5), (8, 8)])
 def test_2stage_partitions_and_remainders(gpu, W, P):
@@ -299,6 +313,35 @@ def test_wire_small_geometries(gpu, fmt, n, sl, first):
     fifos = []
     for x in xs:
         gf = gpu_pack(fmt, x, sl, first, gpu)
+        want = np.full(8 * sl * f["size"], 0xEE, np.uint8)
+        f["opack"](x, want, sl, first)
+        assert np.array_equal(gf.cpu().numpy(), want)
+        fifos.append(gf)
+    out, bad = gpu_unpack(fmt, fifos, n, sl, first, gpu)
+    wout, _, wbad = f["ounpack"]([fi.cpu().numpy() for fi in fifos], n, sl, first)
+    assert bad == wbad == 0
+    assert np.array_equal(out.view(np.uint32), wout.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", ["ll", "ll128"])
+@pytest.mark.parametrize("case", range(5))
+def test_wire_seeded_random_geometries(gpu, fmt, case):
+    """Seeded random payload length, step length (from the smallest that
+    holds the payload to 3x that), first step (up to 2^40), FIFO count
+    W (1..8) and source offset (0/4/8/12 bytes): wire bytes and decoded sums
+    against the oracle."""
+    f = FMT[fmt]
+    rng = np.random.default_rng([91, case, fmt == "ll128"])
+    n = int(rng.integers(1, 300001))
+    need = -(-f["lines"](n) // 8)
+    sl = int(rng.integers(need, 3 * need + 1))
+    first = int(rng.integers(0, 1 << 40))
+    W = int(rng.integers(1, 9))
+    off = 4 * int(rng.integers(0, 4))
+    xs = [rng.standard_normal(n).astype(np.float32) for _ in range(W)]
+    fifos = []
+    for x in xs:
+        gf = gpu_pack(fmt, x, sl, first, gpu, src_offset=off)
         want = np.full(8 * sl * f["size"], 0xEE, np.uint8)
         f["opack"](x, want, sl, first)
         assert np.array_equal(gf.cpu().numpy(), want)
