@@ -121,34 +121,40 @@ __global__ __launch_bounds__(NT) void fused_rmsnorm_kernel(
     const int t = threadIdx.x;
     const int64_t row0 = (int64_t)blockIdx.x * packs_per_row;
 
-    u32x4 xv[PPL][W], rv[PPL], wv[PPL];
+    // Every load of the row is issued before any store, so the one-launch
+    // call's push (which needs its own pack first) does not delay the reads
+    // of the peer slots; those are slots other than `rank` of this rank's
+    // buffer, never a push target.
+    u32x4 xv[PPL][W], rv[PPL], wv[PPL], own[PPL];
 #pragma unroll
     for (int p = 0; p < PPL; ++p) {
         const int idx = t + p * NT;
+        own[p] = u32x4{0u, 0u, 0u, 0u};
         if (idx < packs_per_row) {
-            // every load of the row is issued before any store, so the
-            // one-launch call's push (which needs its own pack first) does
-            // not delay the reads of the peer slots; those are slots other
-            // than `rank` of this rank's buffer, never a push target
-            u32x4 own = {0u, 0u, 0u, 0u};
             if (PUSH)
-                own = ld_stream(la.x_self + row0 + idx);
+                own[p] = ld_stream(la.x_self + row0 + idx);
 #pragma unroll
             for (int r = 0; r < W; ++r)
                 xv[p][r] = (PUSH && r == la.rank) ? u32x4{0u, 0u, 0u, 0u} : in.p[r][row0 + idx];
             rv[p] = residual[row0 + idx];
             wv[p] = weight[idx];
-            if (PUSH) {
-                // one-launch Lamport call: push this rank's scrubbed pack to
-                // every rank's buffer and keep it for the own slot
-                own = scrub_negative_zero(own);
+        }
+    }
+    if (PUSH) {
+        // one-launch Lamport call: push this rank's scrubbed packs to every
+        // rank's buffer and keep them for the own slot
+#pragma unroll
+        for (int p = 0; p < PPL; ++p) {
+            const int idx = t + p * NT;
+            if (idx < packs_per_row) {
+                own[p] = scrub_negative_zero(own[p]);
 #pragma unroll
                 for (int q = 0; q < W; ++q)
-                    st_stream(la.push[q] + row0 + idx, own);
+                    st_stream(la.push[q] + row0 + idx, own[p]);
 #pragma unroll
                 for (int r = 0; r < W; ++r)
                     if (r == la.rank)
-                        xv[p][r] = own;
+                        xv[p][r] = own[p];
             }
         }
     }
