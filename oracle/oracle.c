@@ -34,6 +34,16 @@
  *   orc_ll_* / ll128_*  hand-written golden wire bytes (tests/golden), the
  *                       buffer/step constants printed on [NCCL14], round trip,
  *                       exact bad-line counts for planted corruptions.
+ *   orc_lamport_*       hand-packed words, exhaustive check that no packed
+ *                       word equals the sentinel, a hand-derived W=2 region
+ *                       example, equality with the (pinned) fused operator
+ *                       when no input is -0.0, exact missing-push counts.
+ *   orc_fused_2stage*   row partition numbers, equality with the one-shot
+ *                       fused operator for W=2 or rank order, a hand-derived
+ *                       rotated case.
+ *   orc_fifo_*          payload delivered bit for bit, one lap equal to the
+ *                       (pinned) packers, the last-lap ring contents and the
+ *                       channel split derived by hand, [NCCL14]'s step table.
  * No function here is "parity unpinned".
  */
 #include <math.h>
