@@ -263,6 +263,13 @@ def main():
     log(f"two-stage per-replay: {stats}")
     src_hash = kernel_source_hash()
     traffic = traffic_from_profile(src_hash)
+    # the per-launch floor on this device, measured the same way: a one-stage
+    # reduce of a single 16-byte pack, launched back to back in a graph
+    fd = [to_dev(x[:8]) for x in synth.reduce_small()]
+    fo = torch.empty_like(fd[0])
+    floor_ms = graph_time([lambda: ar.ar_reduce_1stage(fd, fo)], 200, args.warmup)
+    above = ms - floor_ms
+    log(f"launch floor {floor_ms * 1e3:.3f} us; headline above it: {above * 1e3:.3f} us")
 
     result = {
         "metric": METRIC,
@@ -299,6 +306,11 @@ def main():
             "kernel": "reduce_2stage_kernel<8,true,true>",
             "kernel_us": round(ms * 1e3, 3),
             "source_hash": src_hash,
+            "launch_floor_us": round(floor_ms * 1e3, 3),
+            "achieved_above_launch_floor": round(bytes_2stage / (above * 1e-3) / 1e9, 1)
+            if above > 0 else None,
+            "note": "frac is the whole per-launch time; achieved_above_launch_floor "
+                    "divides the same bytes by the time above a one-pack launch",
         },
     }
     # the same call on one buffer set, launch after launch: its 24 MiB stay in
