@@ -437,6 +437,40 @@ def main():
             del comms
         result["lamport_m1_us_per_call"] = rows["lamport_oneshot_W4_M1_N2048"]["us_per_call"]
 
+        # the grid of shapes the fused operator's source page benchmarks
+        # (M in {1, 8, 128} x N in {2048, 4096, 8192}, W=4, the same buffers
+        # every call as in its CUDA-graph replays): the one-shot fused call
+        # and the one-launch Lamport call, median of 5 graph replays each
+        def med_us(fns, steps=200):
+            first, each = graph_time_stats(fns, steps, args.warmup, extra=4)
+            return round(float(np.median([first] + each)) * 1e3, 3)
+
+        grid = {}
+        for N in (2048, 4096, 8192):
+            for M in (1, 8, 128):
+                Wf = fc["W"]
+                gx, gr, gw = synth.fused_inputs(Wf, M, N, [1000 + fc["id"], M, N])
+                d = [to_dev(x) for x in gx]
+                dr, dw = to_dev(gr), to_dev(gw)
+                ro, no = torch.empty_like(dr), torch.empty_like(dr)
+                comms = [torch.empty(ar.ar_lamport_comm_bytes(Wf, M, N) // 4,
+                                     dtype=torch.int32, device=dev) for _ in range(Wf)]
+                for c in comms:
+                    ar.ar_lamport_fill(c, Wf, M, N)
+                for r in range(Wf):
+                    ar.ar_lamport_push(d[r], r, comms, 1)
+                one = med_us([lambda d=d, dr=dr, dw=dw, ro=ro, no=no:
+                              ar.ar_fused_residual_rmsnorm(d, dr, dw, ro, no, fc["eps"])])
+                lam = med_us([lambda d=d, comms=comms, dr=dr, dw=dw, ro=ro, no=no:
+                              ar.ar_lamport_oneshot_residual_rmsnorm(d[0], 0, comms, dr, dw,
+                                                                     ro, no, fc["eps"], 1)])
+                grid[f"M{M}_N{N}"] = {"one_shot_fused_us": one, "lamport_one_launch_us": lam}
+                log(f"fused grid M={M} N={N}: one-shot {one} us, Lamport {lam} us")
+                del comms
+        rows["fused_grid_W4_warm"] = {
+            "us_per_call": grid,
+            "note": "same buffers every call (warm), as the source page's CUDA-graph method"}
+
         # one-shot against two-shot fused, one rank's call, at the workload's
         # M=128 and at a large M (2048 rows of 8192); cold buffer sets
         for M, N in ((128, 2048), (2048, 8192)):
