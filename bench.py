@@ -25,8 +25,7 @@ work: single-threaded for about 10 s, then on every host core of this GPU's
 share at once (up to 16 threads, each doing whole steps) for about 3 s; the
 all-core aggregate is `value`, the single-thread rate `single_core`.
 
-Context rows: the runtime's own device copy of the headline's bytes and of
-256 MiB, and the launch floor (a one-pack reduce).
+Context row: the launch floor (a one-pack reduce).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
                        [--rows all|none|stream] [--eager] [--calib-copy] [--warm]
@@ -572,20 +571,6 @@ def main():
         o = torch.empty_like(d[0])
         row("launch_floor_1stage_W2_n8", 48, [lambda d=d, o=o: ar.ar_reduce_1stage(d, o)],
             steps=200)
-        # context for the headline: the runtime's own device-to-device copy
-        # (a blit kernel) moving the same bytes as one two-stage call
-        # (12 MiB read + 12 MiB written), on rotated cold sets, and a large
-        # copy for the streaming rate without the per-launch floor
-        for cname, cbytes in (("copy_12MiB_cold", bytes_2stage // 2),
-                              ("copy_256MiB", 256 << 20)):
-            cs = [(torch.empty(cbytes, dtype=torch.uint8, device=dev),
-                   torch.empty(cbytes, dtype=torch.uint8, device=dev))
-                  for _ in range(sets_for(2 * cbytes))]
-            row(cname, 2 * cbytes, [lambda c=c: c[1].copy_(c[0]) for c in cs],
-                steps=max(60, 4 * len(cs)),
-                extra={"note": "the HIP runtime's device copy, for context; not a libar call"})
-            del cs
-        torch.cuda.empty_cache()
         nb = (W + 1) * n * 2
         k1 = sets_for(nb)
         s1 = []
