@@ -223,3 +223,139 @@ def test_wire_single_violations(fmt, seed):
         assert status(pack, src, fifo, sl, 0, n=n) == want_p, ("pack", kind, n, sl)
         assert status(unpack, fifos, out, sl, 0, spins, bad, n=n) == want_u, \
             ("unpack", kind, n, sl, W)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_fused_2stage_single_violations(seed):
+    g = np.random.default_rng([504, seed])
+    for _ in range(CASES):
+        W = int(g.integers(2, 9))
+        M = int(g.integers(0, 2048))
+        N = 8 * int(g.integers(1, 2049))
+        rank = int(g.integers(0, W))
+        flags = int(g.choice([0, ar.AR_STAGE_RS, ar.AR_STAGE_AG])) | \
+            int(g.choice([0, ar.AR_ORDER_RANK]))
+        stages = flags & 3 or 3
+        rs, ag = bool(stages & 1), bool(stages & 2)
+        ins = [addr(i) for i in range(W)]
+        tms = [addr(8 + i) for i in range(W)]
+        res, w, ro, no = addr(16), addr(17), addr(18), addr(19)
+        tmp_bytes = 2 * (M // W + M % W) * N * 2
+        want = launched(M)
+        kind = int(g.integers(0, 9))
+        if kind == 1:
+            tms[int(g.integers(0, W))] = None
+            want = ar.AR_ERR_NULL
+        elif kind == 2 and ag:
+            no = None
+            want = ar.AR_ERR_NULL
+        elif kind == 3:
+            rank = int(g.choice([-1, W]))
+            want = ar.AR_ERR_ARG
+        elif kind == 4:
+            N = int(g.choice([N + 2, 16392]))
+            want = ar.AR_ERR_ARG
+        elif kind == 5:
+            flags |= 16
+            want = ar.AR_ERR_ARG
+        elif kind == 6:
+            tms[int(g.integers(0, W))] += 8
+            want = ar.AR_ERR_ALIGN
+        elif kind == 7 and rs and M > 0:
+            tms[rank] = ins[int(g.integers(0, W))]
+            want = ar.AR_ERR_ARG
+        elif kind == 8 and ag and M > 0 and tmp_bytes > 0:
+            ro = tms[int(g.integers(0, W))] + 16 * int(g.integers(0, tmp_bytes // 16))
+            want = ar.AR_ERR_ARG
+        assert status(ar.ar_fused_residual_rmsnorm_2stage, ins, tms, rank, res, w, ro, no,
+                      1e-6, flags, M, N) == want, (kind, W, M, N, rank, flags)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_lamport_single_violations(seed):
+    g = np.random.default_rng([505, seed])
+    for _ in range(CASES):
+        W = int(g.integers(2, 9))
+        M = int(g.integers(0, 1024))
+        N = 8 * int(g.integers(1, 2049))
+        rank = int(g.integers(0, W))
+        x = addr(0)
+        comms = [addr(1 + i) for i in range(W)]
+        res, w, ro, no, bad = addr(10), addr(11), addr(12), addr(13), addr(14)
+        spins = int(g.integers(0, ar.AR_MAX_SPINS + 1))
+        cb = ar.ar_lamport_comm_bytes(W, M, N)
+        assert cb == 3 * W * M * N * 2
+        want_push = want_read = want_one = launched(M)
+        kind = int(g.integers(0, 8))
+        if kind == 1:
+            comms[int(g.integers(0, W))] = None
+            want_push = want_one = ar.AR_ERR_NULL
+        elif kind == 2:
+            N = N + 4
+            want_push = want_read = want_one = ar.AR_ERR_ARG
+        elif kind == 3:
+            rank = int(g.choice([-1, W]))
+            want_push = want_one = ar.AR_ERR_ARG
+        elif kind == 4:
+            spins = ar.AR_MAX_SPINS + 1
+            want_read = want_one = ar.AR_ERR_ARG
+        elif kind == 5:
+            bad += 2
+            want_read = want_one = ar.AR_ERR_ALIGN
+        elif kind == 6 and M > 0:
+            q = int(g.integers(1, W))
+            comms[q] = comms[0] + 16 * int(g.integers(0, cb // 16))   # two buffers overlap
+            want_push = want_one = ar.AR_ERR_ARG
+        elif kind == 7 and M > 0:
+            no = comms[rank] + 16 * int(g.integers(0, cb // 16))      # output inside comm
+            want_read = want_one = ar.AR_ERR_ARG
+        own = comms[rank] if 0 <= rank < W else comms[0]
+        if own is not None:
+            assert status(ar.ar_lamport_fused_residual_rmsnorm, own, W, res, w, ro, no,
+                          1e-6, 1, spins, bad, M, N) == want_read, ("read", kind, W, M, N)
+        assert status(ar.ar_lamport_push, x, rank, comms, 1, M, N) == want_push, \
+            ("push", kind, W, M, N, rank)
+        assert status(ar.ar_lamport_oneshot_residual_rmsnorm, x, rank, comms, res, w, ro, no,
+                      1e-6, 1, spins, bad, M, N) == want_one, ("oneshot", kind, W, M, N, rank)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_stream_single_violations(seed):
+    g = np.random.default_rng([506, seed])
+    units = {ar.AR_PROTO_LL: 8, ar.AR_PROTO_LL128: 120, ar.AR_PROTO_SIMPLE: 16}
+    for _ in range(CASES):
+        proto = int(g.integers(0, 3))
+        n = int(g.integers(0, 1 << 22))
+        step = units[proto] * int(g.integers(1, 5000))
+        channels = int(g.integers(1, ar.AR_FIFO_MAX_CHANNELS + 1))
+        src, out, fifo, cnt, err = addr(0), addr(1), addr(2), addr(3), addr(4)
+        local = addr(5) if g.integers(0, 2) else None
+        spins = int(g.integers(0, ar.AR_MAX_SPINS + 1))
+        want = launched(n)
+        kind = int(g.integers(0, 9))
+        if kind == 1:
+            err = None
+            want = ar.AR_ERR_NULL
+        elif kind == 2:
+            step = units[proto] * int(g.integers(1, 100)) + int(g.integers(1, units[proto]))
+            want = ar.AR_ERR_ARG
+        elif kind == 3:
+            channels = int(g.choice([0, ar.AR_FIFO_MAX_CHANNELS + 1]))
+            want = ar.AR_ERR_ARG
+        elif kind == 4:
+            spins = ar.AR_MAX_SPINS + 1
+            want = ar.AR_ERR_ARG
+        elif kind == 5:
+            cnt += 4
+            want = ar.AR_ERR_ALIGN
+        elif kind == 6:
+            fifo += 64 if proto == ar.AR_PROTO_LL128 else 8
+            want = ar.AR_ERR_ALIGN
+        elif kind == 7 and n > 0:
+            out = src + 4 * int(g.integers(0, n))
+            want = ar.AR_ERR_ARG
+        elif kind == 8 and n > 0:
+            cnt = fifo                                              # counters in the ring
+            want = ar.AR_ERR_ARG
+        assert status(ar.ar_fifo_stream, proto, src, out, fifo, cnt, channels, step, 0, spins,
+                      err, local, n=n) == want, (kind, proto, n, step, channels)
