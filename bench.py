@@ -28,7 +28,7 @@ all-core aggregate is `value`, the single-thread rate `single_core`.
 Context row: the launch floor (a one-pack reduce).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                       [--rows all|none|stream] [--eager] [--calib-copy] [--warm]
+                       [--rows all|none|stream|wire] [--eager] [--calib-copy] [--warm]
 """
 from __future__ import annotations
 
@@ -64,8 +64,9 @@ def parse():
     p.add_argument("--steps", type=int, default=240)
     p.add_argument("--warmup", type=int, default=24)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--rows", choices=["all", "none", "stream"], default="all",
-                   help="which rows besides the headline: all, none, or only the streaming rows")
+    p.add_argument("--rows", choices=["all", "none", "stream", "wire"], default="all",
+                   help="which rows besides the headline: all, none, or only the streaming "
+                        "or the wire-format rows")
     p.add_argument("--eager", action="store_true",
                    help="time eager launches instead of a HIP graph replay")
     p.add_argument("--calib-copy", action="store_true",
@@ -610,6 +611,7 @@ def main():
         del s4, big
         torch.cuda.empty_cache()
 
+    if args.rows in ("all", "wire"):
         # wire formats: W=4 fp32 payloads of 16 Mi values (and the +13 tail);
         # every row rotates buffer sets so each call streams from HBM
         wc = synth.WIRE
