@@ -99,6 +99,34 @@ def traffic_from_profile(source_hash: str):
     return float(t.group(1))
 
 
+WIRE_COUNTERS = os.path.join(ROOT, "profiles", "wire_16Mi_counters.txt")
+WIRE_SOURCES = [os.path.join(ROOT, "ar_rmsnorm_amd", "csrc", f) for f in ("wire.hip", "device.h")]
+
+
+def wire_traffic():
+    """Scaled HBM bytes per dispatch of the wire kernels from the committed
+    counter summary, keyed by (kernel, grid lanes); empty when the wire
+    kernel sources changed since the counters were taken."""
+    try:
+        text = open(WIRE_COUNTERS).read()
+    except OSError:
+        return {}
+    h = hashlib.sha256()
+    for f in WIRE_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    m = re.search(r"^wire\.hip \+ device\.h sha256\[:16\]: (\S+)", text, re.M)
+    if not m or m.group(1) != h.hexdigest()[:16]:
+        return {}
+    out = {}
+    for line in text.splitlines():
+        t = re.match(r"\s*\d+\s+\d+\s+[\d.]+\s+[\d.]+\s+(\d+)\s+\S+\s+\S+\s+(ar::\S+) "
+                     r"\[(\d+), \d+\]", line)
+        if t:
+            out[(t.group(2), int(t.group(3)))] = float(t.group(1))
+    return out
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -615,6 +643,16 @@ def main():
         # wire formats: W=4 fp32 payloads of 16 Mi values (and the +13 tail);
         # every row rotates buffer sets so each call streams from HBM
         wc = synth.WIRE
+        # counter-measured HBM bytes per dispatch (profiles/), by kernel and
+        # grid lanes, attached to the rows while the kernel sources match
+        wt = wire_traffic()
+
+        def add_traffic(r, kernel, lanes, wg, nbytes):
+            tb = wt.get((kernel, -(-lanes // wg) * wg))
+            if tb:
+                r["traffic"] = tb
+                r["traffic_over_algorithmic"] = round(tb / nbytes, 4)
+
         for nn in (wc["n"], wc["n"] + wc["tail"]):
             host_payloads = synth.wire(nn)
             payloads = [torch.from_numpy(p).to(dev) for p in host_payloads]
@@ -645,6 +683,10 @@ def main():
                         oracle_fn=orc and (lambda hf=hfifos, nn=nn, sl=sl: ounpack(hf, nn, sl)))
                 # payload rate: W payloads in, one sum out, at 4 bytes a value
                 r["payload_GBps"] = round((wc["W"] + 1) * 4 * nn / (r["us_per_call"] * 1e3), 1)
+                if fmt == "ll128":
+                    add_traffic(r, "ar::ll128_unpack_reduce_kernel<4>", 8 * L, 256, dec_bytes)
+                else:
+                    add_traffic(r, "ar::ll_unpack_reduce_kernel<4>", L, 128, dec_bytes)
                 del dsets
                 pack_bytes = 4 * nn + L * lsize
                 offsets = (0, 1) if nn == wc["n"] else (0,)
@@ -657,12 +699,18 @@ def main():
                         psets.append((raw, src, torch.empty(8 * sl * lsize, dtype=torch.uint8,
                                                             device=dev)))
                     name = f"{fmt}_n{nn}_pack" + ("_src_offset4" if off else "")
-                    row(name, pack_bytes,
+                    rp = row(name, pack_bytes,
                         [lambda q=q, sl=sl: pack(q[1], q[2], sl) for q in psets],
                         steps=8 * len(psets),
                         oracle_fn=(orc and not off and
                                    (lambda hp=host_payloads[0], hf=hfifos[0], sl=sl:
                                     opack(hp, hf, sl))) or None)
+                    if not off:
+                        if fmt == "ll128":
+                            add_traffic(rp, "ar::ll128_pack_kernel", 16 * ((L + 1) // 2), 256,
+                                        pack_bytes)
+                        else:
+                            add_traffic(rp, "ar::ll_pack_kernel", L, 256, pack_bytes)
                     del psets
                 del hfifos
             del payloads
