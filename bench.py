@@ -144,7 +144,7 @@ def log(msg: str) -> None:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+        print(f"bench.py: libar runs on one GPU only; --gpus {args.gpus} is not "
               "supported (the W rank buffers all live in one GPU's HBM)", file=sys.stderr)
         sys.exit(2)
 

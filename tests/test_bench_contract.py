@@ -1,4 +1,4 @@
-"""The bench's command-line contract that holds without a GPU: this build
+"""The bench's command-line contract that holds without a GPU: the library
 runs on one GPU, so any other GPU count is refused with a message, before
 torch is imported or any device is touched."""
 import os
