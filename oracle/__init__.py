@@ -90,6 +90,8 @@ def lib():
                                       _u64]
         L.orc_lamport_pack.argtypes = [ctypes.c_uint16, ctypes.c_uint16]
         L.orc_lamport_pack.restype = ctypes.c_uint32
+        L.orc_lamport_next_flag.argtypes = [ctypes.c_uint32]
+        L.orc_lamport_next_flag.restype = ctypes.c_uint32
         L.orc_lamport_push.argtypes = [_p, ctypes.c_int, ctypes.c_int, _p, _i64, _i64,
                                        ctypes.c_uint32]
         L.orc_lamport_fused_residual_rmsnorm.argtypes = [_p, ctypes.c_int, _p, _p, _p, _p, _p,
@@ -298,6 +300,11 @@ def ll128_unpack_reduce(fifos, n: int, step_lines: int, first_step: int = 0):
 # Lamport data-as-flag wire for the fused one-shot
 # --------------------------------------------------------------------------
 LAMPORT_SENTINEL = 0x80008000
+LAMPORT_FLAG_PERIOD = 0xC0000000      # 3 * 2^30: the 32-bit flag wraps here
+
+
+def lamport_next_flag(flag: int) -> int:
+    return int(lib().orc_lamport_next_flag(flag))
 
 
 def lamport_comm(W: int, M: int, N: int) -> np.ndarray:
@@ -317,12 +324,16 @@ def lamport_push(x, rank: int, comms, flag: int) -> None:
     M, N = x.shape
     for c in comms:
         assert c.dtype == np.uint32 and c.flags.c_contiguous
+    if not 0 <= flag < LAMPORT_FLAG_PERIOD:
+        raise ValueError(f"Lamport flag {flag} outside [0, 3 * 2^30)")
     lib().orc_lamport_push(_ptr(x), len(comms), rank, _ptr_table(comms), M, N, flag)
 
 
 def lamport_fused_residual_rmsnorm(comm, W: int, residual, weight, eps: float, flag: int):
     """Reader side for one rank; returns (residual_out, norm_out, norm_exact,
-    bad_chunks).  Resets region (flag + 2) % 3 of `comm` in place."""
+    bad_chunks).  Resets region (flag % 3 + 2) % 3 of `comm` in place."""
+    if not 0 <= flag < LAMPORT_FLAG_PERIOD:
+        raise ValueError(f"Lamport flag {flag} outside [0, 3 * 2^30)")
     residual = _u16(residual)
     M, N = residual.shape
     weight = _u16(weight).reshape(N)

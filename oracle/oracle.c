@@ -452,14 +452,25 @@ void orc_bf16_from_f64_array(const double *x, uint16_t *out, int64_t n)
  * packing, a bf16 -0.0 (0x8000) is scrubbed to +0.0, so no word can equal
  * the sentinel 0x80008000 (two -0.0) that fills an empty comm buffer; a
  * reader polls until no word is the sentinel.  The buffer is used in three
- * regions selected by flag mod 3.
+ * regions selected by flag mod 3, the flag growing by one per launch.
  * Layout read here: comm[region][slot r][row m][word j], region = flag % 3,
  * slot = the pushing rank.  After reading region flag % 3 the reader resets
- * region (flag + 2) % 3 (the region of the previous call) to the sentinel:
- * every peer finished writing it before the previous call could complete,
- * and peers write it again only two calls later.
+ * the region before it, (region + 2) % 3 (the region of the previous call),
+ * to the sentinel: every peer finished writing it before the previous call
+ * could complete, and peers write it again only two calls later.
+ * Reading taken for the counter's width: a 32-bit flag wraps at
+ * ORC_LAMPORT_FLAG_PERIOD = 3 * 2^30, a multiple of 3, so that "one more per
+ * launch" keeps the region sequence 0, 1, 2, 0, ... across the wrap; flags at
+ * or above the period are not valid and the functions below refuse them
+ * (push: nothing written; reader: returns -1, nothing written).
  * ------------------------------------------------------------------------- */
 #define ORC_LAMPORT_SENTINEL 0x80008000u
+#define ORC_LAMPORT_FLAG_PERIOD 0xC0000000u
+
+uint32_t orc_lamport_next_flag(uint32_t flag)
+{
+    return flag + 1u >= ORC_LAMPORT_FLAG_PERIOD ? 0u : flag + 1u;
+}
 
 uint32_t orc_lamport_pack(uint16_t lo, uint16_t hi)
 {
@@ -474,6 +485,8 @@ uint32_t orc_lamport_pack(uint16_t lo, uint16_t hi)
 void orc_lamport_push(const uint16_t *x, int W, int rank, uint32_t *const *comms,
                       int64_t M, int64_t N, uint32_t flag)
 {
+    if (flag >= ORC_LAMPORT_FLAG_PERIOD)
+        return;
     const int64_t words = M * N / 2;
     const int64_t region = (int64_t)(flag % 3u);
     for (int p = 0; p < W; ++p) {
@@ -495,6 +508,8 @@ int64_t orc_lamport_fused_residual_rmsnorm(uint32_t *comm, int W,
                                            int64_t M, int64_t N, double eps,
                                            uint32_t flag)
 {
+    if (flag >= ORC_LAMPORT_FLAG_PERIOD)
+        return -1;
     const int64_t words = M * N / 2;
     const int64_t region = (int64_t)(flag % 3u);
     int64_t bad = 0;
@@ -519,7 +534,7 @@ int64_t orc_lamport_fused_residual_rmsnorm(uint32_t *comm, int W,
     free(h);
     for (int r = 0; r < W; ++r)
         free(xs[r]);
-    const int64_t stale = (int64_t)((flag + 2u) % 3u);
+    const int64_t stale = (region + 2) % 3;
     for (int64_t q = 0; q < (int64_t)W * words; ++q)
         comm[stale * W * words + q] = ORC_LAMPORT_SENTINEL;
     return bad;

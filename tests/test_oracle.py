@@ -631,6 +631,60 @@ def test_lamport_triple_buffer_invariant_over_calls():
             assert bad == 0 and np.array_equal(ro, want[0]) and np.array_equal(no, want[1])
 
 
+def test_lamport_flag_sequence_across_the_wrap():
+    """[TRIAR] "Option 2: Lamport": region = flag % 3 and the flag grows by one
+    per launch.  The counter wraps at 3 * 2^30, a multiple of 3, so the
+    region sequence runs on across the wrap (2, 0, 1, 2, ...) and every
+    call still finds its region all sentinel before its pushes.  A plain
+    32-bit wrap would give region 0 twice in a row (2^32 - 1 = 0 mod 3)."""
+    P = orc.LAMPORT_FLAG_PERIOD
+    assert P == 3 << 30 and P % 3 == 0
+    assert (2 ** 32 - 1) % 3 == 0 % 3          # the collision a 2^32 wrap has
+    assert orc.lamport_next_flag(P - 1) == 0
+    assert orc.lamport_next_flag(P - 2) == P - 1
+    assert orc.lamport_next_flag(5) == 6
+    W, M, N = 2, 1, 16
+    words = M * N // 2
+    comms = [orc.lamport_comm(W, M, N) for _ in range(W)]
+    f = P - 4
+    regions = []
+    for call in range(8):
+        xs, res, w = synth.fused_inputs(W, M, N, [93, call])
+        regions.append(f % 3)
+        for c in comms:
+            assert np.all(c.reshape(3, W * words)[f % 3] == SENT), (call, f)
+        for r, x in enumerate(xs):
+            orc.lamport_push(x, r, comms, f)
+        want = orc.fused_residual_rmsnorm(xs, res, w, 1e-6)
+        for p in range(W):
+            ro, no, _, bad = orc.lamport_fused_residual_rmsnorm(comms[p], W, res, w, 1e-6, f)
+            assert bad == 0 and np.array_equal(ro, want[0]) and np.array_equal(no, want[1])
+        f = orc.lamport_next_flag(f)
+    assert regions == [2, 0, 1, 2, 0, 1, 2, 0]          # flags P-4 .. P-1, 0 .. 3
+
+
+def test_lamport_flags_past_the_period_are_refused():
+    """A flag at or above the period is not a valid counter value: the push
+    writes nothing and the reader returns -1 without touching the buffer."""
+    W, M, N = 2, 1, 8
+    xs, res, w = synth.fused_inputs(W, M, N, [94])
+    comm = orc.lamport_comm(W, M, N)
+    before = comm.copy()
+    lib = orc.lib()
+    lib.orc_lamport_push(orc._ptr(np.ascontiguousarray(xs[0])), 1, 0,
+                         orc._ptr_table([comm]), M, N, orc.LAMPORT_FLAG_PERIOD)
+    assert np.array_equal(comm, before)
+    ro = np.empty((M, N), np.uint16)
+    no = np.empty((M, N), np.uint16)
+    ne = np.empty((M, N), np.float64)
+    got = lib.orc_lamport_fused_residual_rmsnorm(
+        orc._ptr(comm), W, orc._ptr(np.ascontiguousarray(res)), orc._ptr(np.ascontiguousarray(w)),
+        orc._ptr(ro), orc._ptr(no), orc._ptr(ne), M, N, 1e-6, 0xFFFFFFFF)
+    assert got == -1 and np.array_equal(comm, before)
+    with pytest.raises(ValueError):
+        orc.lamport_push(xs[0], 0, [comm, comm.copy()], orc.LAMPORT_FLAG_PERIOD)
+
+
 # ---------------------------------------------------------------------------
 # two-shot fused (rows sharded as [SGLv1]'s two-stage form, [TRIAR] operator)
 # ---------------------------------------------------------------------------

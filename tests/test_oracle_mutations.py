@@ -110,9 +110,14 @@ MUTATIONS = [
      "uint32_t *slot = comms[p] + (region * W + rank) * words;",
      "uint32_t *slot = comms[p] + (region * W + p) * words;", LAMPORT),
     ("Lamport: reset of the wrong region",
-     "const int64_t stale = (int64_t)((flag + 2u) % 3u);",
-     "const int64_t stale = (int64_t)((flag + 1u) % 3u);", LAMPORT),
+     "const int64_t stale = (region + 2) % 3;",
+     "const int64_t stale = (region + 1) % 3;", LAMPORT),
     ("Lamport: bad words instead of chunks", "bad += any;", "bad += 4 * any;", LAMPORT),
+    ("Lamport: flag wraps at 2^32",
+     "return flag + 1u >= ORC_LAMPORT_FLAG_PERIOD ? 0u : flag + 1u;", "return flag + 1u;",
+     LAMPORT),
+    ("Lamport: reader takes flags past the period",
+     "if (flag >= ORC_LAMPORT_FLAG_PERIOD)\n        return -1;", "", LAMPORT),
     ("two-shot: no rotation",
      "xs[i] = x[rank_order ? i : (s + i) % W] + m0 * N;", "xs[i] = x[i] + m0 * N;", FUSED2),
     ("two-shot: no row offset",
