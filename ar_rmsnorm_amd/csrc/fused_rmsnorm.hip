@@ -297,7 +297,9 @@ static hipError_t launch_lamport_w(void *comm, const void *residual, const void 
 {
     u32x4 *base = static_cast<u32x4 *>(comm);
     const int64_t chunks = M * N / 8;
-    const int64_t use = flag % 3u, reset = (flag + 2u) % 3u;
+    // the region of this call and the one before it (the caller keeps flag
+    // below a multiple of 3, so the sequence of regions never repeats one)
+    const int64_t use = flag % 3u, reset = (use + 2) % 3;
     InTable<W> in;
     LamportArgs<W> la{};
     for (int r = 0; r < W; ++r) {

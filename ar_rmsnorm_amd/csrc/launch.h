@@ -51,6 +51,9 @@ hipError_t launch_fifo_stream(int proto, const float *src, const float *local, f
 // device holds at once.
 hipError_t fifo_stream_resident_workgroups(int proto, bool local, bool wide, int *workgroups);
 
+// dst[0 .. 16 * packs) = src[0 .. 16 * packs)
+hipError_t launch_copy(const void *src, void *dst, int64_t packs, hipStream_t s);
+
 hipError_t launch_ll_pack(const float *src, int64_t n, void *fifo,
                           int64_t step_lines, uint64_t first_step, hipStream_t s);
 hipError_t launch_ll_unpack_reduce(const void *const *fifos, int W, float *out,

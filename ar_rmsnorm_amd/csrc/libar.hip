@@ -237,6 +237,26 @@ LIBAR_EXPORT ar_status_t ar_fused_residual_rmsnorm_2stage(
                                             static_cast<hipStream_t>(stream)));
 }
 
+// One-GPU choice between the fused forms.  Per rank the one-shot call reads
+// W input rows, the residual and writes two outputs for every row: (W + 3)
+// rows of traffic per row.  The two-shot call does that only for its M / W
+// own rows (plus staging them) and copies two staged rows for every other
+// row: about 4 + (W + 5) / W rows per row, less for W >= 3.  With M < W one
+// owner takes every row and nothing is saved; at small M both calls are
+// bound by the launch, and the two-shot call's extra workgroups cost more
+// than its saved bytes.  The row counts below are where the two-shot call
+// measured faster for one rank on one MI355X.
+LIBAR_EXPORT int ar_fused_prefers_two_shot(int W, int64_t M, int64_t N)
+{
+    if (W < 2 || W > AR_MAX_WORLD || M < 0 || M > 0x7FFFFFFF || N < 8 ||
+        N > AR_FUSED_MAX_N || N % 8 != 0)
+        return -1;
+    if (W == 2 || M < W)
+        return 0;
+    const int64_t min_rows = N <= 2048 ? 16 : 32;
+    return M >= min_rows ? 1 : 0;
+}
+
 // ---------------------------------------------------------------------------
 // Lamport data-as-flag fused one-shot
 // ---------------------------------------------------------------------------
@@ -249,6 +269,11 @@ bool fused_shape_ok(int64_t M, int64_t N)
 }
 
 }  // namespace
+
+LIBAR_EXPORT uint32_t ar_lamport_next_flag(uint32_t flag)
+{
+    return flag + 1u >= AR_LAMPORT_FLAG_PERIOD ? 0u : flag + 1u;
+}
 
 LIBAR_EXPORT int64_t ar_lamport_comm_bytes(int W, int64_t M, int64_t N)
 {
@@ -285,7 +310,7 @@ LIBAR_EXPORT ar_status_t ar_lamport_push(const void *x, int W, int rank, void *c
     for (int p = 0; p < W; ++p)
         if (!comms[p])
             return AR_ERR_NULL;
-    if (rank < 0 || rank >= W || !fused_shape_ok(M, N))
+    if (rank < 0 || rank >= W || !fused_shape_ok(M, N) || flag >= AR_LAMPORT_FLAG_PERIOD)
         return AR_ERR_ARG;
     if (!aligned(x, 16))
         return AR_ERR_ALIGN;
@@ -315,7 +340,7 @@ LIBAR_EXPORT ar_status_t ar_lamport_fused_residual_rmsnorm(
         return AR_ERR_NULL;
     if (W < 2 || W > AR_MAX_WORLD)
         return AR_ERR_WORLD;
-    if (!fused_shape_ok(M, N) || max_spins > AR_MAX_SPINS)
+    if (!fused_shape_ok(M, N) || max_spins > AR_MAX_SPINS || flag >= AR_LAMPORT_FLAG_PERIOD)
         return AR_ERR_ARG;
     if (!(eps >= 0.0f) || eps > 3.0e38f)
         return AR_ERR_ARG;
@@ -357,7 +382,8 @@ LIBAR_EXPORT ar_status_t ar_lamport_oneshot_residual_rmsnorm(
     // the reader's checks, on this rank's own buffer
     if (!residual || !weight || !residual_out || !norm_out)
         return AR_ERR_NULL;
-    if (!fused_shape_ok(M, N) || max_spins > AR_MAX_SPINS || !(eps >= 0.0f) || eps > 3.0e38f)
+    if (!fused_shape_ok(M, N) || max_spins > AR_MAX_SPINS || !(eps >= 0.0f) || eps > 3.0e38f ||
+        flag >= AR_LAMPORT_FLAG_PERIOD)
         return AR_ERR_ARG;
     if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(weight, 16) ||
         !aligned(residual_out, 16) || !aligned(norm_out, 16) ||
@@ -516,6 +542,25 @@ LIBAR_EXPORT ar_status_t ll128_unpack_reduce(const void *const *fifos, int W, fl
     return from_hip(ar::launch_ll128_unpack_reduce(fifos, W, out, n, step_lines,
                                                    first_step, max_spins, bad_lines,
                                                    static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// plain copy (the achievable-copy reference of the measurements)
+// ---------------------------------------------------------------------------
+LIBAR_EXPORT ar_status_t ar_copy(const void *src, void *dst, int64_t nbytes,
+                                 ar_stream_t stream)
+{
+    if (!src || !dst)
+        return AR_ERR_NULL;
+    if (nbytes < 0 || nbytes % 16 != 0 || nbytes > ((int64_t)1 << 44))
+        return AR_ERR_ARG;
+    if (!aligned(src, 16) || !aligned(dst, 16))
+        return AR_ERR_ALIGN;
+    if (overlaps(src, nbytes, dst, nbytes))
+        return AR_ERR_ARG;
+    if (nbytes == 0)
+        return AR_OK;
+    return from_hip(ar::launch_copy(src, dst, nbytes / 16, static_cast<hipStream_t>(stream)));
 }
 
 // ---------------------------------------------------------------------------

@@ -14,8 +14,16 @@
  *
  * Conventions shared by every entry point
  *   Ownership  The caller owns every buffer.  The library never allocates,
- *              frees or synchronizes, and keeps no state between calls except
- *              a thread-local copy of the last HIP error.
+ *              frees or synchronizes.
+ *   State      No call depends on an earlier call except through the
+ *              caller's buffers.  The library keeps two things of its own:
+ *              a thread-local copy of the last HIP error, and, per device,
+ *              how many streaming workgroups (ar_fifo_stream) the device
+ *              holds at once.  The latter is looked up once per (device,
+ *              protocol, geometry) with the HIP occupancy API and stored in
+ *              a process-wide table of atomics: concurrent first calls may
+ *              each look it up and store the same value; it is only read
+ *              afterwards.
  *   Pointers   Data pointers are device pointers.  Pointer tables (inputs,
  *              tmps, fifos) are HOST arrays of W device pointers; they are
  *              read during the call and copied into the kernel arguments, so
@@ -181,12 +189,31 @@ ar_status_t ar_fused_residual_rmsnorm_2stage(const void *const *inputs,
                                              unsigned flags, ar_stream_t stream);
 
 /*
+ * Which fused form to call on one GPU ([SGLv1] "Algorithm switching and
+ * admission limits" chooses between its one-stage and two-stage kernels from
+ * W and the message size, with thresholds its authors measured on NVLink-era
+ * parts; [TRIAR] "overall design" keeps the one-shot form for small batches).
+ * Returns 1 when ar_fused_residual_rmsnorm_2stage is expected to finish a
+ * rank's M x N call sooner than ar_fused_residual_rmsnorm on one MI355X, 0
+ * when the one-shot call is, and -1 for arguments either call rejects.  The
+ * thresholds come from timing both calls for one rank on one MI355X (cold
+ * buffers); on several GPUs the two-shot form also pays an exchange between
+ * its stages, which this one-GPU choice does not include.
+ */
+int ar_fused_prefers_two_shot(int W, int64_t M, int64_t N);
+
+/*
  * Lamport data-as-flag form of the fused one-shot ([TRIAR] "Option 2:
  * Lamport").  Each rank owns a comm buffer of u32 words
  * [3 regions][W slots][M][N / 2] (ar_lamport_comm_bytes), filled with the
  * sentinel 0x80008000 (two bf16 -0.0) before first use (ar_lamport_fill).
- * A call with counter `flag` (incremented by one per call on every rank)
- * uses region flag mod 3:
+ * A call with counter `flag` uses region flag mod 3.  The page advances the
+ * flag by one per launch; here it must stay below AR_LAMPORT_FLAG_PERIOD
+ * (3 * 2^30, a multiple of 3) and the next call's flag is
+ * ar_lamport_next_flag(flag), which wraps to 0 after PERIOD - 1.  Because
+ * the period is a multiple of 3, the region sequence 0, 1, 2, 0, ... runs on
+ * unbroken across the wrap (a 32-bit counter wrapping at 2^32 would use
+ * region 0 twice in a row).  Flags at or above the period -> AR_ERR_ARG.
  *   push   rank r writes its bf16 [M, N] rows into slot r of that region of
  *          every rank's buffer, as u32 words of two bf16 (element 2j in the
  *          low half) with every -0.0 turned into +0.0, so no word can equal
@@ -195,13 +222,19 @@ ar_status_t ar_fused_residual_rmsnorm_2stage(const void *const *inputs,
  *          most max_spins re-reads per 16-byte chunk, never a hang), sums the
  *          W slots in slot order 0..W-1 in fp32 and applies the residual add
  *          and RMSNorm exactly as ar_fused_residual_rmsnorm; it then refills
- *          region (flag + 2) mod 3, the previous call's region, with the
- *          sentinel.  Every peer finished writing that region before the
+ *          region ((flag mod 3) + 2) mod 3, the previous call's region, with
+ *          the sentinel.  Every peer finished writing that region before the
  *          previous call could complete, and writes it again only two calls
  *          later, so three regions make the buffer reusable without a barrier.
  * On one GPU the W comm buffers are ordinary device buffers and the pushes
  * are separate launches ahead of the fused call.
  */
+
+#define AR_LAMPORT_FLAG_PERIOD 0xC0000000u   /* 3 * 2^30 */
+
+/* The flag of the call after `flag`: (flag + 1) mod AR_LAMPORT_FLAG_PERIOD
+ * (flags at or above the period give 0). */
+uint32_t ar_lamport_next_flag(uint32_t flag);
 
 /* Bytes of one rank's comm buffer: 3 * W * M * N * 2 (0 for invalid sizes). */
 int64_t ar_lamport_comm_bytes(int W, int64_t M, int64_t N);
@@ -221,7 +254,7 @@ ar_status_t ar_lamport_fill(void *comm, int W, int64_t M, int64_t N,
  *   comms  host table of the W ranks' comm buffers (16-byte aligned)
  *   W      2 <= W <= 8                                  else AR_ERR_WORLD
  *   rank   0 <= rank < W; 0 <= M < 2^31, M * N <= 2^40; 8 <= N <= 16384,
- *          N multiple of 8
+ *          N multiple of 8; flag < AR_LAMPORT_FLAG_PERIOD
  *                                                       else AR_ERR_ARG
  */
 ar_status_t ar_lamport_push(const void *x, int W, int rank, void *const *comms,
@@ -230,7 +263,8 @@ ar_status_t ar_lamport_push(const void *x, int W, int rank, void *const *comms,
 
 /*
  * Read this rank's comm buffer (region flag mod 3), reduce, add the residual,
- * normalise, and reset region (flag + 2) mod 3 to the sentinel.
+ * normalise, and reset region ((flag mod 3) + 2) mod 3 to the sentinel.
+ *   flag          < AR_LAMPORT_FLAG_PERIOD               else AR_ERR_ARG
  *   comm          this rank's comm buffer (16-byte aligned)
  *   residual, weight, residual_out, norm_out, M, N, eps
  *                 as ar_fused_residual_rmsnorm; no output may overlap comm
@@ -406,6 +440,17 @@ int64_t ar_fifo_step_wire_bytes(int proto, int64_t step_bytes);
 /* Ring steps a call advances every channel's numbering by:
  * ceil(ceil(4n / step_bytes) / channels) (0 for invalid arguments). */
 int64_t ar_fifo_steps_per_channel(int64_t n, int64_t step_bytes, int channels);
+
+/*
+ * Plain device copy, dst[0 .. nbytes) = src[0 .. nbytes), one 16-byte load
+ * and store per lane.  Not an operation of the pages: it is the
+ * achievable-copy reference that the measurements report beside the reduce
+ * and wire kernels (what a kernel moving each byte once reaches here).
+ *   src, dst  device pointers, 16-byte aligned            else AR_ERR_ALIGN
+ *   nbytes    multiple of 16, 0 <= nbytes <= 2^44; the two ranges must not
+ *             overlap                                     else AR_ERR_ARG
+ */
+ar_status_t ar_copy(const void *src, void *dst, int64_t nbytes, ar_stream_t stream);
 
 /* Geometry helpers ([NCCL14] "Default buffers and effective data per
  * step": the default buffers give 4096 LL lines and 4800 LL128 lines per

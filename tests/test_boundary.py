@@ -75,8 +75,11 @@ F = A + (5 << 30)
 
 
 def st(fn, *args):
+    """Status of a call with fake addresses: the binding's own buffer checks
+    are off, so the C ABI's validation is what answers."""
     try:
-        fn(*args)
+        with ar.checks_disabled():
+            fn(*args)
     except ar.ArError as e:
         return e.status
     return ar.AR_OK
@@ -223,3 +226,81 @@ def test_lamport_shape_limits():
     assert ar.ar_lamport_comm_bytes(4, 1 << 26, 16384) == 3 * 4 * (1 << 40) * 2
     assert ar.ar_lamport_comm_bytes(4, (1 << 26) + 1, 16384) == 0     # M * N > 2^40
     assert ar.ar_lamport_comm_bytes(4, 1 << 31, 8) == 0               # M >= 2^31
+
+
+# --------------------------------------------------------------------------
+# the binding's own checks, the Lamport flag period, the copy reference and
+# the one-GPU fused-form choice
+# --------------------------------------------------------------------------
+def test_binding_refuses_host_tensors_and_integer_addresses():
+    """With its checks on (the default) the binding passes only contiguous
+    GPU tensors: a host tensor or a bare integer address is refused with
+    AR_ERR_ARG before the C ABI is called."""
+    host = torch.zeros(64, dtype=torch.int16)
+    with pytest.raises(ar.ArError) as e:
+        ar.ar_reduce_1stage([host, host], host, stream=0)
+    assert e.value.status == ar.AR_ERR_ARG and "not on a GPU" in str(e.value)
+    with pytest.raises(ar.ArError) as e:
+        ar.ar_reduce_1stage([A, B], C, 8, 0)
+    assert e.value.status == ar.AR_ERR_ARG and "torch tensor" in str(e.value)
+    with pytest.raises(ar.ArError) as e:
+        ar.ll_pack(torch.zeros(8), A, 1, stream=0)
+    assert e.value.status == ar.AR_ERR_ARG
+
+
+def test_lamport_next_flag_wraps_at_a_multiple_of_three():
+    P = ar.AR_LAMPORT_FLAG_PERIOD
+    assert P == 3 << 30
+    assert ar.ar_lamport_next_flag(0) == 1
+    assert ar.ar_lamport_next_flag(P - 2) == P - 1
+    assert ar.ar_lamport_next_flag(P - 1) == 0
+    assert ar.ar_lamport_next_flag(0xFFFFFFFF) == 0
+    f, regions = P - 3, []
+    for _ in range(6):
+        regions.append(f % 3)
+        f = ar.ar_lamport_next_flag(f)
+    assert regions == [0, 1, 2, 0, 1, 2]
+    with pytest.raises(ar.ArError):
+        ar.ar_lamport_next_flag(1 << 32)
+
+
+@cpu_only
+def test_lamport_flags_at_or_past_the_period_are_rejected():
+    P = ar.AR_LAMPORT_FLAG_PERIOD
+    W, M, N = 2, 1, 8
+    for flag in (P, P + 1, 0xFFFFFFFF):
+        assert st(ar.ar_lamport_push, A, 0, [B, C], flag, M, N, 0) == ar.AR_ERR_ARG
+        assert st(ar.ar_lamport_fused_residual_rmsnorm, B, W, D, E, F, F + 4096, 1e-6, flag,
+                  0, None, M, N, 0) == ar.AR_ERR_ARG
+        assert st(ar.ar_lamport_oneshot_residual_rmsnorm, A, 0, [B, C], D, E, F, F + 4096,
+                  1e-6, flag, 0, None, M, N, 0) == ar.AR_ERR_ARG
+    # the last valid flag reaches the launch (rejected by the runtime here)
+    assert st(ar.ar_lamport_push, A, 0, [B, C], P - 1, M, N, 0) == ar.AR_ERR_HIP
+
+
+@cpu_only
+def test_copy_argument_errors():
+    f = ar.ar_copy
+    assert st(f, None, B, 16, 0) == ar.AR_ERR_NULL
+    assert st(f, A, None, 16, 0) == ar.AR_ERR_NULL
+    assert st(f, A, B, 8, 0) == ar.AR_ERR_ARG                 # not whole 16-byte packs
+    assert st(f, A, B, -16, 0) == ar.AR_ERR_ARG
+    assert st(f, A, B, (1 << 44) + 16, 0) == ar.AR_ERR_ARG
+    assert st(f, A + 4, B, 16, 0) == ar.AR_ERR_ALIGN
+    assert st(f, A, B + 8, 16, 0) == ar.AR_ERR_ALIGN
+    assert st(f, A, A + 16, 32, 0) == ar.AR_ERR_ARG           # overlapping ranges
+    assert st(f, A, B, 0, 0) == ar.AR_OK                      # nothing to launch
+    assert st(f, A, B, 16, 0) == ar.AR_ERR_HIP                # reaches the launch
+
+
+def test_fused_form_choice():
+    f = ar.ar_fused_prefers_two_shot
+    assert f(1, 16, 2048) == -1 and f(9, 16, 2048) == -1
+    assert f(4, -1, 2048) == -1 and f(4, 16, 2049) == -1 and f(4, 16, 16392) == -1
+    # W = 2: the two-shot form moves more bytes than the one-shot form
+    assert all(f(2, M, N) == 0 for M in (1, 16, 1024, 8192) for N in (2048, 8192))
+    # fewer rows than ranks: one owner would take every row
+    assert f(8, 7, 2048) == 0 and f(4, 3, 8192) == 0
+    for W in (3, 4, 8):
+        assert f(W, 1, 2048) == 0
+        assert f(W, 8192, 2048) == 1 and f(W, 2048, 8192) == 1

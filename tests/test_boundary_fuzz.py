@@ -28,7 +28,8 @@ def addr(i: int) -> int:
 def status(fn, *args, **kw):
     kw.setdefault("stream", 0)       # the null stream: no torch device needed
     try:
-        fn(*args, **kw)
+        with ar.checks_disabled():   # fake addresses: the C ABI's checks answer
+            fn(*args, **kw)
     except ar.ArError as e:
         return e.status
     return ar.AR_OK
