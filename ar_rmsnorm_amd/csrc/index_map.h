@@ -1,0 +1,97 @@
+// Block and lane index map of the two-stage reduce, as plain C++17 constexpr
+// functions.  HIP device code may call constexpr functions, so the kernel
+// uses exactly these; the host can compile them with any C++17 compiler, so
+// every (block, lane) of a launch can be enumerated and bounds-checked on a
+// CPU.  No HIP header is needed here.
+//
+// Source (web page; cited by tag and section):
+//   [SGLv1] "SGLang Custom AllReduce v1 线程模型和工作原理细节" (todaynews.cc),
+//           "2stage: sharding, rotation, and why no exit barrier"
+//
+// The message is P packs of 16 bytes; part = P / W; shard s covers packs
+// [s * part, s * part + part), the last shard also the P mod W remainder.
+// The launch is one-dimensional:
+//   reduce blocks [0, rs_blocks): lane t of block b reduces pack
+//     idx = b * threads + t of this rank's shard (idx < own), reading pack
+//     rank * part + idx of every input, writing pack idx of tmps[rank] and,
+//     when the gather runs in the same launch, the same pack of out;
+//   copy blocks: cp_blocks per shard copied (W - 1 shards after a reduce, the
+//     W shards for a gather alone); block k of them copies shard
+//     g = (rank + i) mod W, i = (reduce ? 1 : 0) + k / cp_blocks, lane t
+//     taking packs idx0 + c * threads, c < cpl, idx0 = (k mod cp_blocks) *
+//     threads * cpl + t, those below the shard's size: tmps[g][idx] ->
+//     out[g * part + idx].
+#pragma once
+
+#include <stdint.h>
+
+namespace ar {
+
+struct TwoStageGrid {
+    int64_t part;        // packs per shard (the last one has rem more)
+    int64_t rem;         // P mod W
+    int64_t own;         // packs of this rank's shard
+    int64_t cap;         // part + rem: packs a staging buffer must hold
+    int64_t rs_blocks;   // reduce blocks (0 without the reduce stage)
+    int64_t cp_blocks;   // copy blocks per gathered shard
+    int64_t blocks;      // the whole grid
+};
+
+constexpr TwoStageGrid two_stage_grid(int W, int rank, int64_t packs, bool rs, bool ag,
+                                      int threads, int cpl)
+{
+    TwoStageGrid g{};
+    g.part = packs / W;
+    g.rem = packs % W;
+    g.own = g.part + (rank == W - 1 ? g.rem : 0);
+    g.cap = g.part + g.rem;
+    g.rs_blocks = rs ? (g.own + threads - 1) / threads : 0;
+    const int64_t per_block = (int64_t)threads * cpl;
+    g.cp_blocks = (g.cap + per_block - 1) / per_block;
+    g.blocks = g.rs_blocks + (ag ? (int64_t)(rs ? W - 1 : W) * g.cp_blocks : 0);
+    return g;
+}
+
+// What one lane does for its c-th pack (c < cpl; reduce lanes have one).
+struct TwoStageLane {
+    int kind;            // 0: nothing, 1: reduce, 2: copy
+    int shard;           // copy: the shard g read from tmps[g]
+    int64_t read;        // reduce: pack of every input; copy: pack of tmps[g]
+    int64_t tmp;         // reduce: pack written in tmps[rank]
+    int64_t out;         // pack written in out (reduce with a gather, copy)
+};
+
+constexpr TwoStageLane two_stage_lane(const TwoStageGrid &g, int W, int rank, bool rs,
+                                      int threads, int cpl, int64_t b, int t, int c)
+{
+    TwoStageLane l{};
+    if (rs && b < g.rs_blocks) {
+        const int64_t idx = b * threads + t;
+        if (c == 0 && idx < g.own) {
+            l.kind = 1;
+            l.read = (int64_t)rank * g.part + idx;
+            l.tmp = idx;
+            l.out = (int64_t)rank * g.part + idx;
+        }
+        return l;
+    }
+    // block numbers fit 32 bits (a grid is at most 2^32 - 1 blocks), and
+    // 32-bit division is far cheaper on the GPU than 64-bit
+    const uint32_t k = (uint32_t)(rs ? b - g.rs_blocks : b);
+    const uint32_t per_shard = (uint32_t)g.cp_blocks;
+    const int i = (rs ? 1 : 0) + (int)(k / per_shard);
+    const int64_t idx = (int64_t)(k % per_shard) * threads * cpl + (int64_t)c * threads + t;
+    int s = rank + i;
+    if (s >= W)
+        s -= W;
+    const int64_t size = g.part + (s == W - 1 ? g.rem : 0);
+    if (idx < size) {
+        l.kind = 2;
+        l.shard = s;
+        l.read = idx;
+        l.out = (int64_t)s * g.part + idx;
+    }
+    return l;
+}
+
+}  // namespace ar

@@ -15,6 +15,7 @@
 // with the message, so an 8 MB x 8 reduce fills all 256 CUs with thousands
 // of wavefronts, each lane keeping its W loads in flight at once.
 #include "device.h"
+#include "index_map.h"
 #include "launch.h"
 
 namespace ar {
@@ -57,52 +58,52 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_1stage_kernel(
 }
 
 // Two-stage reduce for one rank ([SGLv1] "2stage: sharding, rotation, and
-// why no exit barrier").  One-dimensional grid, reduce blocks first:
-//   blocks [0, rs_blocks) (RS): reduce this rank's shard, inputs in `in`
-//       order (the owner's rotation), store to tmps[rank] and, with AG, to
-//       out.  The value goes from registers to out and each lane gathers
-//       exactly the packs it reduced (the pages' same-thread mapping), so no
-//       barrier is needed inside the launch.
-//   the remaining blocks (AG): cp_blocks per shard, copying shard
-//       g = (rank + i) mod W from tmps[g] to out, for i = 1..W-1 after an RS,
-//       or i = 0..W-1 for an all-gather alone.
+// why no exit barrier").  One-dimensional grid, reduce blocks first; which
+// packs a lane touches is two_stage_lane() (index_map.h), the same function
+// the host-side checks enumerate:
+//   reduce blocks (RS): this rank's shard, inputs in `in` order (the owner's
+//       rotation), stored to tmps[rank] and, with AG, to out.  The value goes
+//       from registers to out and each lane gathers exactly the packs it
+//       reduced (the pages' same-thread mapping), so no barrier is needed
+//       inside the launch.
+//   copy blocks (AG): CPL packs per lane of the other shards (of every shard
+//       for a gather alone), tmps[g] -> out.
 // The gather reads use plain loads and everything else streams: on cold
 // data that measured fastest among the cache-policy combinations.
-template <int W, bool RS, bool AG>
+template <int W, bool RS, bool AG, int CPL>
 __global__ __launch_bounds__(kReduceThreads) void reduce_2stage_kernel(
-    InTable<W> in, OutTable<W> tmps, int rank, u32x4 *out, int64_t part,
-    int64_t rem, uint32_t rs_blocks, uint32_t cp_blocks)
+    InTable<W> in, OutTable<W> tmps, int rank, u32x4 *out, TwoStageGrid grid)
 {
-    const uint32_t b = blockIdx.x;
+    const int64_t b = blockIdx.x;
     const int t = threadIdx.x;
-    if (RS && b < rs_blocks) {
-        const int64_t idx = (int64_t)b * kReduceThreads + t;
-        const int64_t own = part + (rank == W - 1 ? rem : 0);
-        if (idx >= own)
+    if (RS && b < grid.rs_blocks) {
+        const TwoStageLane l = two_stage_lane(grid, W, rank, RS, kReduceThreads, CPL, b, t, 0);
+        if (l.kind != 1)
             return;
-        const int64_t dst = (int64_t)rank * part + idx;
         u32x4 v[W];
 #pragma unroll
         for (int r = 0; r < W; ++r)
-            v[r] = ld_stream(in.p[r] + dst);
+            v[r] = ld_stream(in.p[r] + l.read);
         const u32x4 s = reduce_column<W>(v);
-        st_stream(tmps.p[rank] + idx, s);
+        st_stream(tmps.p[rank] + l.tmp, s);
         if (AG)
-            st_stream(out + dst, s);
+            st_stream(out + l.out, s);
         return;
     }
     if (!AG)
         return;
-    const uint32_t k = RS ? b - rs_blocks : b;
-    const int i = (RS ? 1 : 0) + (int)(k / cp_blocks);
-    const int64_t idx = (int64_t)(k % cp_blocks) * kReduceThreads + t;
-    int g = rank + i;
-    if (g >= W)
-        g -= W;
-    const int64_t size = part + (g == W - 1 ? rem : 0);
-    if (idx >= size)
-        return;
-    st_stream(out + (int64_t)g * part + idx, tmps.p[g][idx]);
+    TwoStageLane l[CPL];
+    u32x4 v[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        l[c] = two_stage_lane(grid, W, rank, RS, kReduceThreads, CPL, b, t, c);
+        if (l[c].kind == 2)
+            v[c] = tmps.p[l[c].shard][l[c].read];
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+        if (l[c].kind == 2)
+            st_stream(out + l[c].out, v[c]);
 }
 
 template <int W>
@@ -135,18 +136,14 @@ hipError_t launch_reduce_1stage(const void *const *inputs, int W, void *out,
 
 template <int W, bool RS, bool AG>
 static hipError_t launch_2stage_mode(const InTable<W> &in, const OutTable<W> &tmps,
-                                     int rank, void *out, int64_t part,
-                                     int64_t rem, hipStream_t s)
+                                     int rank, void *out, int64_t packs, hipStream_t s)
 {
-    const int64_t own = part + (rank == W - 1 ? rem : 0);
-    const int64_t rs_blocks = RS ? (own + kReduceThreads - 1) / kReduceThreads : 0;
-    const int64_t cp_blocks = (part + rem + kReduceThreads - 1) / kReduceThreads;
-    const int64_t blocks = rs_blocks + (AG ? (RS ? W - 1 : W) * cp_blocks : 0);
-    if (blocks == 0)
+    constexpr int kCpl = 1;
+    const TwoStageGrid g = two_stage_grid(W, rank, packs, RS, AG, kReduceThreads, kCpl);
+    if (g.blocks == 0)
         return hipSuccess;
-    reduce_2stage_kernel<W, RS, AG><<<dim3((unsigned)blocks), dim3(kReduceThreads), 0, s>>>(
-        in, tmps, rank, static_cast<u32x4 *>(out), part, rem, (uint32_t)rs_blocks,
-        (uint32_t)cp_blocks);
+    reduce_2stage_kernel<W, RS, AG, kCpl><<<dim3((unsigned)g.blocks), dim3(kReduceThreads), 0,
+                                           s>>>(in, tmps, rank, static_cast<u32x4 *>(out), g);
     return hipGetLastError();
 }
 
@@ -161,12 +158,11 @@ static hipError_t launch_2stage_w(const void *const *inputs, const int *order,
         in.p[r] = static_cast<const u32x4 *>(inputs[order[r]]);
         tp.p[r] = static_cast<u32x4 *>(tmps[r]);
     }
-    const int64_t part = packs / W, rem = packs % W;
     if (rs && ag)
-        return launch_2stage_mode<W, true, true>(in, tp, rank, out, part, rem, s);
+        return launch_2stage_mode<W, true, true>(in, tp, rank, out, packs, s);
     if (rs)
-        return launch_2stage_mode<W, true, false>(in, tp, rank, out, part, rem, s);
-    return launch_2stage_mode<W, false, true>(in, tp, rank, out, part, rem, s);
+        return launch_2stage_mode<W, true, false>(in, tp, rank, out, packs, s);
+    return launch_2stage_mode<W, false, true>(in, tp, rank, out, packs, s);
 }
 
 hipError_t launch_reduce_2stage(const void *const *inputs, const int *order,

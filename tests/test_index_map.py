@@ -1,0 +1,74 @@
+"""CPU enumeration of the two-stage reduce's launches.
+
+The kernel decides which packs a lane reads and writes with the constexpr
+functions of ar_rmsnorm_amd/csrc/index_map.h.  tests/index_map_check.cpp
+compiles those same functions with g++ and walks every (block, lane, pack)
+of a launch: every input, staging and output access must fall inside the
+buffer sizes the header requires, reduce lanes must gather the packs they
+reduced, and every output and staging pack must be written exactly once.
+
+Cases: the message size of the 8 MB cap (W = 8, 4,194,304 bf16 = 524,288
+packs) for every rank as reduce-scatter alone, all-gather alone and both, with
+1, 2 and 4 packs per copy lane -- including the stage-only launches a bench
+row ran back to back over 23 buffer sets (the sets differ only in their
+addresses, not in any index) -- and every W from 2 to 8 with pack counts that
+leave remainders, down to fewer packs than ranks.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.fixture(scope="module")
+def checker(tmp_path_factory):
+    if shutil.which("g++") is None:
+        pytest.skip("g++ not available")
+    exe = str(tmp_path_factory.mktemp("imap") / "index_map_check")
+    subprocess.run(["g++", "-std=c++17", "-O2", "-Wall", "-o", exe,
+                    os.path.join(HERE, "index_map_check.cpp")], check=True)
+    return exe
+
+
+def run(exe, *args):
+    r = subprocess.run([exe, *map(str, args)], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout + r.stderr
+    return r.stdout
+
+
+def test_cap_message_every_rank_and_stage(checker):
+    out = run(checker, 256, 8, 524_288)
+    assert "72 launches checked, 0 failures" in out        # 8 ranks x 3 stages x 3 widths
+
+
+@pytest.mark.parametrize("W", range(2, 9))
+def test_ragged_sizes_every_world_size(checker, W):
+    sizes = [0, 1, W - 1, W, W + 1, 255 * W + W - 1, 256 * W, 257 * W + 1, 1024 * W + 3,
+             8 * (8 * 300 + 5), 65_536 * W + W - 1]
+    args = []
+    for P in sizes:
+        args += [W, P]
+    out = run(checker, 256, *args)
+    assert f"{len(sizes) * W * 9} launches checked, 0 failures" in out
+
+
+def test_the_checker_catches_a_planted_out_of_range_map(checker, tmp_path):
+    """Plant an off-by-one in a copy of the map (the last shard's remainder
+    given to every shard) and make sure the enumeration reports it."""
+    src = open(os.path.join(HERE, "..", "ar_rmsnorm_amd", "csrc", "index_map.h")).read()
+    old = "const int64_t size = g.part + (s == W - 1 ? g.rem : 0);"
+    assert src.count(old) == 1
+    bad_dir = tmp_path / "ar_rmsnorm_amd" / "csrc"
+    bad_dir.mkdir(parents=True)
+    (bad_dir / "index_map.h").write_text(src.replace(old, "const int64_t size = g.part + g.rem;"))
+    tests_dir = tmp_path / "tests"
+    tests_dir.mkdir()
+    shutil.copy(os.path.join(HERE, "index_map_check.cpp"), tests_dir)
+    exe = str(tmp_path / "bad_check")
+    subprocess.run(["g++", "-std=c++17", "-O2", "-o", exe,
+                    str(tests_dir / "index_map_check.cpp")], check=True)
+    r = subprocess.run([exe, "256", "8", str(8 * 100 + 5)], capture_output=True, text=True)
+    assert r.returncode == 1 and "FAIL" in r.stdout
