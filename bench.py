@@ -55,14 +55,15 @@ MALL_BYTES = 256 << 20
 RANK_GAP = 4096 + 512
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "reduce_2stage_w8_8MiB_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "ar_rmsnorm_amd", "csrc", f)
-                  for f in ("reduce.hip", "device.h")]
+                  for f in ("reduce.hip", "device.h", "index_map.h")]
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=240)
-    p.add_argument("--warmup", type=int, default=24)
+    p.add_argument("--steps", type=int, default=10,
+                   help="headline steps timed; a step is one call on each rotated buffer set")
+    p.add_argument("--warmup", type=int, default=2, help="untimed headline steps first")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--rows", choices=["all", "none", "stream", "wire"], default="all",
                    help="which rows besides the headline: all, none, or only the streaming "
@@ -71,6 +72,10 @@ def parse():
                    help="time eager launches instead of a HIP graph replay")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (counter calibration)")
+    p.add_argument("--trace-summary", metavar="DIR",
+                   help="no GPU work: summarize the rocprofv3 kernel trace (kernel_trace.csv) "
+                        "under DIR per kernel and launch shape, and the back-to-back spacing "
+                        "of the headline kernel's dispatches")
     p.add_argument("--warm", action="store_true",
                    help="also time the headline call on one reused buffer set (its bytes "
                         "then come from the Infinity Cache); off by default so that a "
@@ -127,6 +132,67 @@ def wire_traffic():
     return out
 
 
+def trace_summary(d: str) -> str:
+    """Per-dispatch statistics from a rocprofv3 --kernel-trace CSV: for every
+    kernel and launch shape the dispatch count and the median, mean, min,
+    P5, P95, max and coefficient of variation of the durations (end - start);
+    then, for the headline kernel, the spacing of dispatches that follow one
+    another directly: start-to-start interval, duration, and the gap from one
+    dispatch's end to the next one's start."""
+    import csv
+    import glob
+    import numpy as np
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"bench.py: no kernel_trace.csv under {d}")
+    recs = []
+    for f in files:
+        with open(f) as fh:
+            recs += list(csv.DictReader(fh))
+    groups = {}
+    for r in recs:
+        name = r["Kernel_Name"]
+        name = name[5:] if name.startswith("void ") else name
+        key = (name.split("(")[0][:80], r["Grid_Size_X"], r["Grid_Size_Y"],
+               r["Workgroup_Size_X"])
+        groups.setdefault(key, []).append(
+            (int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    out = ["per kernel and launch shape: dispatches, then duration statistics in us "
+           "(median, mean, min, P5, P95, max) and the coefficient of variation",
+           "%6s %9s %9s %8s %8s %9s %9s %6s  %s" % ("n", "median", "mean", "min", "p5", "p95",
+                                                   "max", "cv", "kernel [grid x, grid y, wg]")]
+    stats = {}
+    for key, v in groups.items():
+        a = np.array([(e - b) / 1000.0 for b, e in v])
+        stats[key] = a
+    for key, a in sorted(stats.items(), key=lambda kv: -np.median(kv[1])):
+        out.append("%6d %9.3f %9.3f %8.3f %8.3f %9.3f %9.3f %6.3f  %s [%s, %s, %s]" % (
+            len(a), np.median(a), a.mean(), a.min(), np.percentile(a, 5),
+            np.percentile(a, 95), a.max(), a.std() / a.mean(), *key))
+    # back-to-back spacing of the headline kernel: consecutive dispatches in
+    # start order where both are the headline's launch shape
+    allv = sorted((b, e, key) for key, v in groups.items() for b, e in v)
+    head = [k for k in groups if "reduce_2stage_kernel<8, true, true" in k[0]
+            and k[1] == "524288"]
+    for hk in head:
+        iv, du, gp = [], [], []
+        for (b0, e0, k0), (b1, e1, k1) in zip(allv, allv[1:]):
+            if k0 == hk and k1 == hk:
+                iv.append((b1 - b0) / 1000.0)
+                du.append((e0 - b0) / 1000.0)
+                gp.append((b1 - e0) / 1000.0)
+        if iv:
+            out.append("")
+            out.append(f"headline {hk[0]} [{hk[1]}, {hk[2]}, {hk[3]}]: {len(iv)} pairs of "
+                       "directly consecutive dispatches (us)")
+            for name, a in (("start-to-start interval", iv), ("duration", du),
+                            ("end-to-next-start gap", gp)):
+                a = np.array(a)
+                out.append("  %-24s median %8.3f  mean %8.3f  p5 %8.3f  p95 %8.3f" % (
+                    name, np.median(a), a.mean(), np.percentile(a, 5), np.percentile(a, 95)))
+    return "\n".join(out)
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -143,6 +209,9 @@ def log(msg: str) -> None:
 
 def main():
     args = parse()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return
     if args.gpus != 1:
         print(f"bench.py: libar runs on one GPU only; --gpus {args.gpus} is not "
               "supported (the W rank buffers all live in one GPU's HBM)", file=sys.stderr)
@@ -251,13 +320,14 @@ def main():
     xs = synth.reduce_cap()
     P = n // 8
     part, rem = P // W, P % W
-    # bytes the launch must move: RS reads W slices of `part` packs and writes
-    # the own shard to tmp and out; AG reads the W-1 peer shards and writes
-    # them to out (the own shard goes from registers to out).
     shard = part * 16
-    bytes_2stage = W * shard + 2 * shard + (W - 1) * shard + (W - 1) * shard
-    touched = bytes_2stage
-    nsets = sets_for(touched)
+    # algorithmic bytes of one rank's call, as the method states it: RS reads
+    # the W slices of its shard and writes the shard to tmp; AG reads all W
+    # staged shards and writes them to out.  The kernel moves one shard less
+    # each way (its own shard goes from registers to out): moved_bytes.
+    bytes_2stage = W * shard + shard + W * shard + W * shard
+    moved_2stage = W * shard + 2 * shard + (W - 1) * shard + (W - 1) * shard
+    nsets = sets_for(moved_2stage)
     base = [to_dev(x) for x in xs]
     sets = []
     for k in range(nsets):
@@ -269,19 +339,25 @@ def main():
         sets.append((ins, tmps, out))
     torch.cuda.synchronize()
     calls = [(lambda s=s: ar.ar_reduce_2stage(s[0], s[1], 0, s[2])) for s in sets]
-    steps = max(args.steps, nsets)
-    steps -= steps % nsets
-    log(f"two-stage W=8 8MiB: {nsets} buffer sets staged, timing {steps} launches")
+    # one step = the call on each of the nsets cold buffer sets (a batch of
+    # nsets messages); --steps K steps are timed as K * nsets launches
+    steps = max(1, args.steps)
+    launches = steps * nsets
+    log(f"two-stage W=8 8MiB: {nsets} buffer sets staged; {args.warmup} warm-up steps, "
+        f"timing {steps} steps = {launches} launches")
     if args.eager:
-        ms = graph_time(calls, steps, args.warmup)
-        each = [ms]
+        ms_launch = graph_time(calls, launches, args.warmup * nsets)
+        each = [ms_launch]
     else:
-        ms, each = graph_time_stats(calls, steps, args.warmup)
-    gbps = bytes_2stage / (ms * 1e-3) / 1e9
-    log(f"two-stage: {ms * 1e3:.3f} us/launch, {gbps:.1f} GB/s")
+        ms_launch, each = graph_time_stats(calls, launches, args.warmup * nsets)
+    ms = ms_launch * nsets                  # per step
+    gbps = bytes_2stage / (ms_launch * 1e-3) / 1e9
+    log(f"two-stage: {ms_launch * 1e3:.3f} us/launch, {gbps:.1f} GB/s "
+        f"({moved_2stage / (ms_launch * 1e-3) / 1e9:.1f} GB/s moved)")
     us = np.sort(np.array(each) * 1e3)
     stats = {
-        "spread_over": f"{len(us)} further replays of the timed graph of {steps} launches",
+        "spread_over": f"{len(us)} further replays of the timed graph of {launches} launches, "
+                       "us per launch",
         "median_us": round(float(np.median(us)), 3),
         "p5_us": round(float(np.percentile(us, 5)), 3),
         "p95_us": round(float(np.percentile(us, 95)), 3),
@@ -296,7 +372,7 @@ def main():
     fd = [to_dev(x[:8]) for x in synth.reduce_small()]
     fo = torch.empty_like(fd[0])
     floor_ms = graph_time([lambda: ar.ar_reduce_1stage(fd, fo)], 200, args.warmup)
-    above = ms - floor_ms
+    above = ms_launch - floor_ms
     log(f"launch floor {floor_ms * 1e3:.3f} us; headline above it: {above * 1e3:.3f} us")
 
     result = {
@@ -317,7 +393,13 @@ def main():
             "workload": "two-stage reduce at the 8 MB cap: W=8 rank buffers of "
                         "4,194,304 bf16 ~U(-1,1), one rank's reduce-scatter of its 1/8 "
                         "shard + all-gather of the 8 shards, HBM-resident, cold",
-            "W": W, "n": n, "bytes_per_launch": bytes_2stage,
+            "W": W, "n": n,
+            "step": f"one call on each of {nsets} rotated buffer sets ({nsets} launches)",
+            "launches_per_step": nsets,
+            "launches_timed": launches,
+            "us_per_launch": round(ms_launch * 1e3, 3),
+            "bytes_per_launch": bytes_2stage,
+            "bytes_moved_per_launch": moved_2stage,
             "layout": f"per set, the 8 inputs and the 8 staging shards each in one "
                       f"allocation, {RANK_GAP} B apart",
             "buffer_sets_rotated": nsets,
@@ -331,19 +413,26 @@ def main():
             "unit": "GB/s",
             "frac": round(gbps / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "reduce_2stage_kernel<8,true,true>",
-            "kernel_us": round(ms * 1e3, 3),
+            "kernel": "reduce_2stage_kernel<8,true,true,1>",
+            "kernel_us": round(ms_launch * 1e3, 3),
+            "kernel_us_timer": "HIP events around the graph replay on the launch stream, "
+                               "divided by the launches it holds",
+            "bytes_per_launch": bytes_2stage,
+            "bytes_moved_per_launch": moved_2stage,
+            "achieved_moved": round(moved_2stage / (ms_launch * 1e-3) / 1e9, 1),
             "source_hash": src_hash,
             "launch_floor_us": round(floor_ms * 1e3, 3),
             "achieved_above_launch_floor": round(bytes_2stage / (above * 1e-3) / 1e9, 1)
             if above > 0 else None,
-            "note": "frac is the whole per-launch time; achieved_above_launch_floor "
-                    "divides the same bytes by the time above a one-pack launch",
+            "note": "achieved = the method's bytes per launch (26,214,400) / us per launch; "
+                    "achieved_moved counts the bytes the kernel moves (own shard not "
+                    "re-read); achieved_above_launch_floor divides the method's bytes by "
+                    "the time above a one-pack launch",
         },
     }
     # the same call on one buffer set, launch after launch: its 24 MiB stay in
     # the 256 MB Infinity Cache, so this is a cache rate, not HBM bandwidth
-    warm_ms = graph_time(calls[:1], steps, args.warmup) if args.warm else None
+    warm_ms = graph_time(calls[:1], launches, args.warmup) if args.warm else None
     del sets, calls
     torch.cuda.empty_cache()
 
@@ -364,8 +453,10 @@ def main():
         whose CV exceeds 5 % is timed once more and flagged if it still does.
         With the CPU leg on, also time the oracle doing the same work
         (repeated until ~0.3 s, single-threaded)."""
-        k = steps or max(60, len(fns))
-        k -= k % len(fns)
+        # at least 40 launches per replay, so the 5 timed replays hold >= 200
+        # dispatches (the per-dispatch statistics come from the kernel trace)
+        k = max(steps or 60, 40)
+        k = -(-k // len(fns)) * len(fns)
         if args.eager:
             t, cv, reruns = graph_time(fns, k, args.warmup), None, 0
         else:
@@ -465,6 +556,50 @@ def main():
             del comms
         result["lamport_m1_us_per_call"] = rows["lamport_oneshot_W4_M1_N2048"]["us_per_call"]
 
+        # Lamport with the peers' pushes landing while the readers poll: the W
+        # ranks' one-launch calls of a step go out together, one stream per
+        # rank (parallel branches of the captured graph), so a rank's kernel
+        # can find peer slots still holding the sentinel and take the re-read
+        # path.  A step is one call of every rank; the steps' flags run
+        # through six consecutive values (a multiple of 3), so every replay of
+        # the graph finds its regions reset as on a live run.  `bad_chunks`
+        # counts the chunks still missing after max_spins re-reads (none are
+        # expected when the branches run concurrently).
+        lam_streams = [torch.cuda.Stream() for _ in range(fc["W"])]
+        for M in fc["Ms"]:
+            fx, fr, fw = synth.fused(M)
+            Wf, N = fc["W"], fc["N"]
+            d = [to_dev(x) for x in fx]
+            dr, dw = to_dev(fr), to_dev(fw)
+            outs = [(torch.empty_like(dr), torch.empty_like(dr)) for _ in range(Wf)]
+            comms = [torch.empty(ar.ar_lamport_comm_bytes(Wf, M, N) // 4, dtype=torch.int32,
+                                 device=dev) for _ in range(Wf)]
+            for c in comms:
+                ar.ar_lamport_fill(c, Wf, M, N)
+            bad = torch.zeros(1, dtype=torch.int32, device=dev)
+            torch.cuda.synchronize()
+
+            def step(f, d=d, dr=dr, dw=dw, outs=outs, comms=comms, bad=bad, Wf=Wf):
+                cur = torch.cuda.current_stream()
+                for st in lam_streams:
+                    st.wait_stream(cur)
+                for r, st in enumerate(lam_streams):
+                    with torch.cuda.stream(st):
+                        ar.ar_lamport_oneshot_residual_rmsnorm(
+                            d[r], r, comms, dr, dw, outs[r][0], outs[r][1], fc["eps"], f,
+                            max_spins=4096, bad_chunks=bad)
+                for st in lam_streams:
+                    cur.wait_stream(st)
+
+            flags = [1, 2, 3, 4, 5, 6]
+            r = row(f"lamport_all_ranks_W4_M{M}_N2048", Wf * (2 * M * N + Wf * 2 * M * N),
+                    [lambda f=f, step=step: step(f) for f in flags], steps=60)
+            torch.cuda.synchronize()
+            r["bad_chunks"] = int(bad.item())
+            r["note"] = ("W one-launch calls per step, one stream per rank; bytes = each "
+                         "rank's row read and pushed to W buffers")
+            del comms
+
         # the grid of shapes the fused operator's source page benchmarks
         # (M in {1, 8, 128} x N in {2048, 4096, 8192}, W=4, the same buffers
         # every call as in its CUDA-graph replays): the one-shot fused call
@@ -545,11 +680,10 @@ def main():
             del s2, base_x
             torch.cuda.empty_cache()
 
-        def fused_crossover(N, Ms):
+        def fused_crossover(Wf, N, Ms):
             cross = {}
-            Wf = fc["W"]
             for M in Ms:
-                fx, fr, fw = synth.fused_inputs(Wf, M, N, [1000 + fc["id"], M, N])
+                fx, fr, fw = synth.fused_inputs(Wf, M, N, [1000 + fc["id"], Wf, M, N])
                 mat = M * N * 2
                 part, rem = M // Wf, M % Wf
                 base_x = [to_dev(x) for x in fx]
@@ -565,26 +699,35 @@ def main():
                                                             fc["eps"], flags=ar.AR_STAGE_RS)
                     s1.append((xx, rr, torch.empty_like(rr), torch.empty_like(rr)))
                     s2.append((xx, rr, tmps, torch.empty_like(rr), torch.empty_like(rr)))
-                k = 8 * nsets_f
+                k = max(8 * nsets_f, 40)
+                k = -(-k // nsets_f) * nsets_f
                 t1 = graph_time([lambda q=q: ar.ar_fused_residual_rmsnorm(
                     q[0], q[1], dw, q[2], q[3], fc["eps"]) for q in s1], k, args.warmup)
                 t2 = graph_time([lambda q=q: ar.ar_fused_residual_rmsnorm_2stage(
                     q[0], q[2], 0, q[1], dw, q[3], q[4], fc["eps"]) for q in s2], k, args.warmup)
                 cross[str(M)] = {"one_shot_us": round(t1 * 1e3, 3),
-                                 "two_shot_us": round(t2 * 1e3, 3)}
+                                 "two_shot_us": round(t2 * 1e3, 3),
+                                 "library_picks_two_shot": ar.ar_fused_prefers_two_shot(Wf, M, N)}
                 del s1, s2, base_x
                 torch.cuda.empty_cache()
             won = [int(m) for m, v in cross.items() if v["two_shot_us"] < v["one_shot_us"]]
-            rows[f"fused_one_vs_two_shot_W4_N{N}"] = {
-                "us_per_call": cross, "two_shot_faster_from_M": min(won) if won else None}
-            log(f"fused one-shot vs two-shot, N={N}: {cross}")
+            lost = [int(m) for m, v in cross.items() if v["two_shot_us"] >= v["one_shot_us"]]
+            # the smallest M from which the two-shot call won at every larger M tried
+            from_m = min((m for m in won if all(x < m for x in lost)), default=None)
+            rows[f"fused_one_vs_two_shot_W{Wf}_N{N}"] = {
+                "us_per_call": cross, "two_shot_faster_from_M": from_m}
+            log(f"fused one-shot vs two-shot, W={Wf} N={N}: {cross}")
 
         # where the two-shot fused form overtakes the one-shot form for one
-        # rank's call on this device: W=4, N = 2048 and 8192, M from 16 to
-        # 8192 rows (cold sets, graph-timed); the crossover M is reported
-        for N, Ms in ((2048, (16, 128, 512, 1024, 2048, 4096, 8192)),
-                      (8192, (32, 64, 128, 256, 512, 1024, 2048))):
-            fused_crossover(N, Ms)
+        # rank's call on this device: W = 2, 4, 8, N = 2048 and 8192, M from W
+        # rows up (cold sets, graph-timed); the crossover M is reported, and
+        # what ar_fused_prefers_two_shot picks for each shape beside it
+        for Wf in (2, 4, 8):
+            for N in (2048, 8192):
+                Ms = [m for m in (2, 4, 8, 12, 16, 24, 32, 64, 128, 512, 2048) if m >= Wf]
+                if Wf == 2:
+                    Ms = [2, 16, 128, 2048]
+                fused_crossover(Wf, N, Ms)
 
         # one-stage reduce: small, decode shape, and the cap message
         for name, maker in (("1stage_W2_n8192", synth.reduce_small),
@@ -620,24 +763,56 @@ def main():
             [lambda s=s: ar.ar_reduce_1stage(s[0], s[1]) for s in s1], steps=8 * k1)
         del s1
 
-        # the same per-rank two-stage call on 4x larger buffers (W=8 x 32 MiB):
-        # separates the kernel's streaming rate from the per-launch floor
-        n4 = 4 * n
-        part4 = n4 // 8 // W
-        nb4 = (W + 2 + 2 * (W - 1)) * part4 * 16
-        big = [torch.cat([b] * 4) for b in base]
-        s4 = []
-        for k in range(sets_for(nb4)):
-            ins = rank_buffers(W, 2 * n4, torch.int16, big)
-            tmps = rank_buffers(W, part4 * 16, torch.int16)
-            for r in range(1, W):
-                ar.ar_reduce_2stage(ins, tmps, r, None, flags=ar.AR_STAGE_RS)
-            s4.append((ins, tmps, torch.empty(n4, dtype=torch.int16, device=dev)))
-        row("2stage_W8_n16777216_per_rank", nb4,
-            [lambda s=s: ar.ar_reduce_2stage(s[0], s[1], 0, s[2]) for s in s4],
-            steps=8 * len(s4))
-        del s4, big
-        torch.cuda.empty_cache()
+        # the same per-rank two-stage call over message sizes of 1 to 32 MiB per
+        # rank buffer (cold sets): a straight-line fit of us per launch against
+        # bytes splits the launch into a fixed part and a streaming rate
+        fit_x, fit_y = [], []
+        for mib in (1, 2, 4, 8, 16, 32):
+            nm = mib << 19                      # bf16 elements of `mib` MiB
+            pm = nm // 8 // W
+            nbm = (3 * W + 1) * pm * 16
+            movedm = (W + 2 + 2 * (W - 1)) * pm * 16
+            rep = -(-nm // n) if nm > n else 1
+            src = [torch.cat([b] * rep)[:nm] for b in base] if nm >= n else [b[:nm] for b in base]
+            sm = []
+            for k in range(sets_for(movedm)):
+                ins = rank_buffers(W, 2 * nm, torch.int16, src)
+                tmps = rank_buffers(W, pm * 16, torch.int16)
+                for r in range(1, W):
+                    ar.ar_reduce_2stage(ins, tmps, r, None, flags=ar.AR_STAGE_RS)
+                sm.append((ins, tmps, torch.empty(nm, dtype=torch.int16, device=dev)))
+            rr = row(f"2stage_W8_n{nm}_per_rank", nbm,
+                     [lambda s=s: ar.ar_reduce_2stage(s[0], s[1], 0, s[2]) for s in sm],
+                     steps=8 * len(sm), extra={"bytes_moved": movedm, "sets": len(sm)})
+            fit_x.append(nbm)
+            fit_y.append(rr["us_per_call"])
+            del sm, src
+            torch.cuda.empty_cache()
+        slope, icept = np.polyfit(np.array(fit_x, float), np.array(fit_y, float), 1)
+        rows["2stage_W8_size_fit"] = {
+            "fixed_us": round(float(icept), 3),
+            "streaming_GBps": round(1e-3 / float(slope), 1),
+            "points": {str(x): y for x, y in zip(fit_x, fit_y)},
+            "note": "least-squares line through us per launch against the method's bytes "
+                    "per launch, 1 to 32 MiB per rank buffer, cold sets"}
+        log(f"two-stage size fit: {rows['2stage_W8_size_fit']}")
+
+        # achievable-copy reference: a plain 16-byte copy kernel (ar_copy), cold
+        # sets, moving the headline's bytes (12 MiB read + 12 MiB written) and
+        # 512 MiB (256 + 256)
+        for half_mib in (12, 256):
+            nbc = half_mib << 20
+            cs = []
+            for k in range(sets_for(2 * nbc)):
+                cs.append((torch.empty(nbc, dtype=torch.uint8, device=dev),
+                           torch.empty(nbc, dtype=torch.uint8, device=dev)))
+            for a, _ in cs:
+                a.fill_(1)
+            row(f"copy_{2 * half_mib}MiB_traffic", 2 * nbc,
+                [lambda q=q: ar.ar_copy(q[0], q[1]) for q in cs], steps=8 * len(cs),
+                extra={"note": "ar_copy of %d MiB into %d MiB, cold sets" % (half_mib, half_mib)})
+            del cs
+            torch.cuda.empty_cache()
 
     if args.rows in ("all", "wire"):
         # wire formats: W=4 fp32 payloads of 16 Mi values (and the +13 tail);
@@ -689,7 +864,8 @@ def main():
                     add_traffic(r, "ar::ll_unpack_reduce_kernel<4>", L, 128, dec_bytes)
                 del dsets
                 pack_bytes = 4 * nn + L * lsize
-                offsets = (0, 1) if nn == wc["n"] else (0,)
+                # source offsets of 0, 4, 8 and 12 bytes ([NCCL14]'s alignment sweep)
+                offsets = (0, 1, 2, 3) if nn == wc["n"] else (0,)
                 for off in offsets:
                     psets = []
                     for _ in range(sets_for(pack_bytes)):
@@ -698,7 +874,7 @@ def main():
                         src.copy_(payloads[0])
                         psets.append((raw, src, torch.empty(8 * sl * lsize, dtype=torch.uint8,
                                                             device=dev)))
-                    name = f"{fmt}_n{nn}_pack" + ("_src_offset4" if off else "")
+                    name = f"{fmt}_n{nn}_pack" + (f"_src_offset{4 * off}" if off else "")
                     rp = row(name, pack_bytes,
                         [lambda q=q, sl=sl: pack(q[1], q[2], sl) for q in psets],
                         steps=8 * len(psets),
