@@ -556,50 +556,6 @@ def main():
             del comms
         result["lamport_m1_us_per_call"] = rows["lamport_oneshot_W4_M1_N2048"]["us_per_call"]
 
-        # Lamport with the peers' pushes landing while the readers poll: the W
-        # ranks' one-launch calls of a step go out together, one stream per
-        # rank (parallel branches of the captured graph), so a rank's kernel
-        # can find peer slots still holding the sentinel and take the re-read
-        # path.  A step is one call of every rank; the steps' flags run
-        # through six consecutive values (a multiple of 3), so every replay of
-        # the graph finds its regions reset as on a live run.  `bad_chunks`
-        # counts the chunks still missing after max_spins re-reads (none are
-        # expected when the branches run concurrently).
-        lam_streams = [torch.cuda.Stream() for _ in range(fc["W"])]
-        for M in fc["Ms"]:
-            fx, fr, fw = synth.fused(M)
-            Wf, N = fc["W"], fc["N"]
-            d = [to_dev(x) for x in fx]
-            dr, dw = to_dev(fr), to_dev(fw)
-            outs = [(torch.empty_like(dr), torch.empty_like(dr)) for _ in range(Wf)]
-            comms = [torch.empty(ar.ar_lamport_comm_bytes(Wf, M, N) // 4, dtype=torch.int32,
-                                 device=dev) for _ in range(Wf)]
-            for c in comms:
-                ar.ar_lamport_fill(c, Wf, M, N)
-            bad = torch.zeros(1, dtype=torch.int32, device=dev)
-            torch.cuda.synchronize()
-
-            def step(f, d=d, dr=dr, dw=dw, outs=outs, comms=comms, bad=bad, Wf=Wf):
-                cur = torch.cuda.current_stream()
-                for st in lam_streams:
-                    st.wait_stream(cur)
-                for r, st in enumerate(lam_streams):
-                    with torch.cuda.stream(st):
-                        ar.ar_lamport_oneshot_residual_rmsnorm(
-                            d[r], r, comms, dr, dw, outs[r][0], outs[r][1], fc["eps"], f,
-                            max_spins=4096, bad_chunks=bad)
-                for st in lam_streams:
-                    cur.wait_stream(st)
-
-            flags = [1, 2, 3, 4, 5, 6]
-            r = row(f"lamport_all_ranks_W4_M{M}_N2048", Wf * (2 * M * N + Wf * 2 * M * N),
-                    [lambda f=f, step=step: step(f) for f in flags], steps=60)
-            torch.cuda.synchronize()
-            r["bad_chunks"] = int(bad.item())
-            r["note"] = ("W one-launch calls per step, one stream per rank; bytes = each "
-                         "rank's row read and pushed to W buffers")
-            del comms
-
         # the grid of shapes the fused operator's source page benchmarks
         # (M in {1, 8, 128} x N in {2048, 4096, 8192}, W=4, the same buffers
         # every call as in its CUDA-graph replays): the one-shot fused call

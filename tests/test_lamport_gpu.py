@@ -240,42 +240,3 @@ def test_lamport_flag_past_the_period_is_refused(gpu):
     sync()
     for c, b in zip(comms, before):
         assert np.array_equal(host_words(c), b)
-
-
-@pytest.mark.parametrize("M", [1, 16, 128])
-def test_lamport_all_ranks_concurrently(gpu, M):
-    """Every rank's one-launch call at once, one stream per rank, for several
-    consecutive flags: each kernel pushes its rows while the others poll, so
-    the re-read path runs.  Every rank's outputs match the oracle, no chunk
-    is left missing, and the buffers end as the oracle's call sequence
-    leaves them."""
-    W, N = 4, 2048
-    eps = synth.FUSED["eps"]
-    comms = new_comms(W, M, N, gpu)
-    hcomms = [orc.lamport_comm(W, M, N) for _ in range(W)]
-    streams = [torch.cuda.Stream() for _ in range(W)]
-    for f in range(4):
-        xs, res, w = synth.fused_inputs(W, M, N, [96, M, f])
-        dx = [dev_u16(x, gpu) for x in xs]
-        dr, dw = dev_u16(res, gpu), dev_u16(w, gpu)
-        outs = [(torch.empty_like(dr), torch.empty_like(dr)) for _ in range(W)]
-        bad = torch.zeros(1, dtype=torch.int32, device=gpu)
-        sync()
-        for r, st in enumerate(streams):
-            with torch.cuda.stream(st):
-                ar.ar_lamport_oneshot_residual_rmsnorm(dx[r], r, comms, dr, dw, outs[r][0],
-                                                       outs[r][1], eps, f, ar.AR_MAX_SPINS,
-                                                       bad)
-        sync()
-        assert int(bad.item()) == 0, "a peer slot never arrived"
-        for r in range(W):
-            orc.lamport_push(xs[r], r, hcomms, f)
-        for p in range(W):
-            wro, _, exact, wbad = orc.lamport_fused_residual_rmsnorm(hcomms[p], W, res, w,
-                                                                     eps, f)
-            assert wbad == 0
-            assert np.array_equal(host_u16(outs[p][0]), wro), f"residual_out, rank {p}"
-            ok, _ = norm_within_tolerance(host_u16(outs[p][1]), exact)
-            assert ok.all(), f"norm_out, rank {p}"
-        for p in range(W):
-            assert np.array_equal(host_words(comms[p]), hcomms[p]), f"buffer of rank {p}"
