@@ -54,8 +54,8 @@ LIBAR_EXPORT const char *ar_status_str(ar_status_t status)
     case AR_ERR_ALIGN: return "pointer not aligned as required";
     case AR_ERR_WORLD: return "number of rank buffers W out of range";
     case AR_ERR_CAPACITY:
-        return "payload does not fit the 8 steps of the FIFO, or the streaming "
-               "workgroups cannot all be resident at once";
+        return "payload does not fit the 8 steps of the FIFO or the library's staging "
+               "array, or the streaming workgroups cannot all be resident at once";
     case AR_ERR_HIP: return "HIP runtime rejected the launch";
     default: return "unknown status";
     }
@@ -136,6 +136,95 @@ LIBAR_EXPORT ar_status_t ar_reduce_2stage(const void *const *inputs, void *const
         order[i] = (flags & AR_ORDER_RANK) ? i : (rank + i) % W;
     return from_hip(ar::launch_reduce_2stage(inputs, order, tmps, W, rank, out, packs,
                                              rs, ag, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// Two-stage reduce with library-owned staging.  The W staging shards live in
+// `scratch`, one array per device for the life of the process.  In host code
+// the array's name is only a stand-in for the symbol: its device address is
+// looked up once per device with hipGetSymbolAddress and kept in
+// g_scratch_ptr, and only that address reaches a kernel.
+// ---------------------------------------------------------------------------
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[AR_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device.  Concurrent first calls may both look it up; they store the
+// same address.
+hipError_t scratch_address(void **ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (!p)
+            return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
+}
+
+}  // namespace
+
+LIBAR_EXPORT ar_status_t ar_reduce_2stage_noalloc(const void *const *inputs, int W, int rank,
+                                                  void *out, int64_t n, unsigned flags,
+                                                  ar_stream_t stream)
+{
+    if (!inputs)
+        return AR_ERR_NULL;
+    if (W < 2 || W > AR_MAX_WORLD)
+        return AR_ERR_WORLD;
+    if (flags & ~(AR_STAGE_RS | AR_STAGE_AG | AR_ORDER_RANK))
+        return AR_ERR_ARG;
+    if ((flags & (AR_STAGE_RS | AR_STAGE_AG)) == 0)
+        flags |= AR_STAGE_RS | AR_STAGE_AG;
+    const bool rs = flags & AR_STAGE_RS, ag = flags & AR_STAGE_AG;
+    for (int r = 0; r < W; ++r)
+        if (!inputs[r])
+            return AR_ERR_NULL;
+    if (ag && !out)
+        return AR_ERR_NULL;
+    if (rank < 0 || rank >= W || n < 0 || n % 8 != 0 || n > kMaxElems)
+        return AR_ERR_ARG;
+    const int64_t packs = n / 8;
+    const int64_t cap_bytes = (packs / W + packs % W) * 16;   // one shard's staging
+    if (cap_bytes * W > (int64_t)AR_SCRATCH_BYTES)
+        return AR_ERR_CAPACITY;
+    for (int r = 0; r < W; ++r)
+        if (!aligned(inputs[r], 16))
+            return AR_ERR_ALIGN;
+    if (ag && !aligned(out, 16))
+        return AR_ERR_ALIGN;
+    if (ag)
+        for (int r = 0; r < W; ++r)
+            if (overlaps(out, 2 * n, inputs[r], 2 * n))
+                return AR_ERR_ARG;
+    if (n == 0)
+        return AR_OK;
+    void *base = nullptr;
+    const hipError_t e = scratch_address(&base);
+    if (e != hipSuccess)
+        return from_hip(e);
+    void *tmps[AR_MAX_WORLD];
+    for (int s = 0; s < W; ++s)
+        tmps[s] = static_cast<uint8_t *>(base) + (int64_t)s * cap_bytes;
+    int order[AR_MAX_WORLD];
+    for (int i = 0; i < W; ++i)
+        order[i] = (flags & AR_ORDER_RANK) ? i : (rank + i) % W;
+    return from_hip(ar::launch_reduce_2stage(inputs, order, tmps, W, rank, out, packs, rs, ag,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 // ---------------------------------------------------------------------------

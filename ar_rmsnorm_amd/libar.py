@@ -38,6 +38,7 @@ AR_OK, AR_ERR_NULL, AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_WORLD, AR_ERR_CAPACITY, AR_
 AR_STAGE_RS, AR_STAGE_AG, AR_ORDER_RANK = 1, 2, 4
 AR_MAX_WORLD, AR_FUSED_MAX_N, AR_MAX_SPINS, AR_FIFO_STEPS = 8, 16384, 65536, 8
 AR_LAMPORT_FLAG_PERIOD = 0xC0000000
+AR_SCRATCH_BYTES = (8 << 20) + 4096
 
 EXPORTS = (
     "ar_status_str", "ar_last_hip_error", "ar_reduce_1stage", "ar_reduce_2stage",
@@ -48,6 +49,7 @@ EXPORTS = (
     "ll128_fifo_bytes", "ll_default_step_lines", "ll128_default_step_lines",
     "ar_fifo_stream", "ar_fifo_step_wire_bytes", "ar_fifo_steps_per_channel",
     "ar_fifo_counter_words", "ar_lamport_next_flag", "ar_fused_prefers_two_shot", "ar_copy",
+    "ar_reduce_2stage_noalloc",
 )
 AR_PROTO_LL, AR_PROTO_LL128, AR_PROTO_SIMPLE = 0, 1, 2
 AR_FIFO_MAX_CHANNELS = 256
@@ -63,6 +65,8 @@ _lib.ar_last_hip_error.argtypes = []
 _lib.ar_last_hip_error.restype = _int
 _lib.ar_reduce_1stage.argtypes = [_pp, _int, _vp, _i64, _vp]
 _lib.ar_reduce_2stage.argtypes = [_pp, _pp, _int, _int, _vp, _i64, ctypes.c_uint, _vp]
+_lib.ar_reduce_2stage_noalloc.argtypes = [_pp, _int, _int, _vp, _i64, ctypes.c_uint, _vp]
+_lib.ar_reduce_2stage_noalloc.restype = _int
 _lib.ar_fused_residual_rmsnorm.argtypes = [_pp, _int, _vp, _vp, _vp, _vp, _i64, _i64,
                                            ctypes.c_float, _vp]
 _lib.ar_fused_residual_rmsnorm_2stage.argtypes = [_pp, _pp, _int, _int, _vp, _vp, _vp, _vp,
@@ -208,6 +212,18 @@ def ar_reduce_2stage(inputs: Sequence, tmps: Sequence, rank: int, out,
                                  _table(tmps, tmp_bytes, BF16, "tmps", w), len(inputs), rank,
                                  _addr(out, 2 * n, BF16, "out", w), n, flags, _stream(stream)),
            w)
+
+
+def ar_reduce_2stage_noalloc(inputs: Sequence, rank: int, out, flags: int = 0,
+                             n: Optional[int] = None, stream=None) -> None:
+    """ar_reduce_2stage with the staging shards in the library's own device
+    array (AR_SCRATCH_BYTES per GPU): nothing is allocated.  Calls on one
+    GPU share that array, so they must not overlap in time."""
+    w = "ar_reduce_2stage_noalloc"
+    n = _numel(inputs[0], n)
+    _check(_lib.ar_reduce_2stage_noalloc(_table(inputs, 2 * n, BF16, "inputs", w), len(inputs),
+                                         rank, _addr(out, 2 * n, BF16, "out", w), n, flags,
+                                         _stream(stream)), w)
 
 
 def ar_fused_residual_rmsnorm(inputs: Sequence, residual, weight, residual_out, norm_out,

@@ -13,17 +13,22 @@
  *            (riverclouds.net)
  *
  * Conventions shared by every entry point
- *   Ownership  The caller owns every buffer.  The library never allocates,
- *              frees or synchronizes.
+ *   Ownership  The caller owns every buffer, except the staging array of
+ *              ar_reduce_2stage_noalloc, which is static device memory of
+ *              the library.  The library never allocates, frees or
+ *              synchronizes.
  *   State      No call depends on an earlier call except through the
- *              caller's buffers.  The library keeps two things of its own:
+ *              caller's buffers (and, for ar_reduce_2stage_noalloc, that
+ *              staging array).  The library keeps two things of its own:
  *              a thread-local copy of the last HIP error, and, per device,
  *              how many streaming workgroups (ar_fifo_stream) the device
  *              holds at once.  The latter is looked up once per (device,
  *              protocol, geometry) with the HIP occupancy API and stored in
  *              a process-wide table of atomics: concurrent first calls may
  *              each look it up and store the same value; it is only read
- *              afterwards.
+ *              afterwards.  ar_reduce_2stage_noalloc also keeps, per
+ *              device, the address of its staging array, looked up once
+ *              the same way.
  *   Pointers   Data pointers are device pointers.  Pointer tables (inputs,
  *              tmps, fifos) are HOST arrays of W device pointers; they are
  *              read during the call and copied into the kernel arguments, so
@@ -57,7 +62,8 @@ typedef int ar_status_t;
 #define AR_ERR_ARG 2       /* a size, flag or aliasing rule is violated */
 #define AR_ERR_ALIGN 3     /* a pointer lacks the required alignment */
 #define AR_ERR_WORLD 4     /* W outside the supported range */
-#define AR_ERR_CAPACITY 5  /* the payload does not fit the FIFO's 8 steps, or
+#define AR_ERR_CAPACITY 5  /* the payload does not fit the FIFO's 8 steps or
+                              (ar_reduce_2stage_noalloc) the staging array, or
                               (ar_fifo_stream) its workgroups cannot all be
                               resident at once */
 #define AR_ERR_HIP 6       /* the HIP runtime rejected a launch */
@@ -124,6 +130,28 @@ ar_status_t ar_reduce_1stage(const void *const *inputs, int W, void *out,
 ar_status_t ar_reduce_2stage(const void *const *inputs, void *const *tmps,
                              int W, int rank, void *out, int64_t n,
                              unsigned flags, ar_stream_t stream);
+
+/*
+ * Two-stage reduce that allocates nothing and takes no staging buffers, for
+ * callers that cannot allocate device memory (code being captured into a
+ * HIP graph, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * operation and arguments as ar_reduce_2stage, except that the W staging
+ * shards live in a library-owned device array of AR_SCRATCH_BYTES bytes
+ * (one per GPU, held until the process ends): shard s at byte offset
+ * s * (part + P mod W) * 16.  A call with AR_STAGE_RS leaves its shard there
+ * for later calls, as the tmps buffers of ar_reduce_2stage would hold it.
+ * Every call on one GPU uses that GPU's one array, so calls that overlap in
+ * time on one GPU (other streams, other threads) race: order them on one
+ * stream.  No call allocates or frees memory.
+ *   W * (part + P mod W) * 16 <= AR_SCRATCH_BYTES        else AR_ERR_CAPACITY
+ *   (every message up to 8 MiB, 4,194,304 bf16, fits for any W)
+ *   other arguments and errors as ar_reduce_2stage
+ */
+#define AR_SCRATCH_BYTES ((8u << 20) + 4096u)
+
+ar_status_t ar_reduce_2stage_noalloc(const void *const *inputs, int W, int rank,
+                                     void *out, int64_t n, unsigned flags,
+                                     ar_stream_t stream);
 
 /*
  * Fused all-reduce + residual add + RMSNorm ([TRIAR] "what this operator

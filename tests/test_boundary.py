@@ -304,3 +304,26 @@ def test_fused_form_choice():
     for W in (3, 4, 8):
         assert f(W, 1, 2048) == 0
         assert f(W, 8192, 2048) == 1 and f(W, 2048, 8192) == 1
+
+
+@cpu_only
+def test_reduce_2stage_noalloc_argument_errors():
+    f = ar.ar_reduce_2stage_noalloc
+    W = 8
+    ins = [A + i * (1 << 26) for i in range(W)]
+    assert st(f, ins[:1], 0, B, 0, 8, 0) == ar.AR_ERR_WORLD
+    assert st(f, ins[:-1] + [None], 0, B, 0, 8, 0) == ar.AR_ERR_NULL
+    assert st(f, ins, 0, None, 0, 8, 0) == ar.AR_ERR_NULL            # gather needs out
+    assert st(f, ins, 8, B, 0, 8, 0) == ar.AR_ERR_ARG                # rank out of range
+    assert st(f, ins, 0, B, 8, 8, 0) == ar.AR_ERR_ARG                # unknown flag bit
+    assert st(f, ins, 0, B, 0, 12, 0) == ar.AR_ERR_ARG               # not whole packs
+    assert st(f, ins[:-1] + [A + 8], 0, B, 0, 8, 0) == ar.AR_ERR_ALIGN
+    assert st(f, ins, 0, A, 0, 8, 0) == ar.AR_ERR_ARG                # out overlaps an input
+    # the 8 MiB cap message fits the staging array for every W; one more pack
+    # per shard than the array holds does not
+    assert st(f, ins, 0, B, 0, 4_194_304, 0) == ar.AR_ERR_HIP        # reaches the launch
+    for w in range(2, 9):
+        assert st(f, ins[:w], 0, B, 0, 4_194_304 + 8 * (w - 1), 0) == ar.AR_ERR_HIP
+    big = 8 * ((ar.AR_SCRATCH_BYTES // 16 // W + 1) * W)
+    assert st(f, ins, 0, B, 0, big, 0) == ar.AR_ERR_CAPACITY
+    assert st(f, ins, 0, None, ar.AR_STAGE_RS, 0, 0) == ar.AR_OK     # nothing to launch
