@@ -11,10 +11,11 @@
 // The message is P packs of 16 bytes; part = P / W; shard s covers packs
 // [s * part, s * part + part), the last shard also the P mod W remainder.
 // The launch is one-dimensional:
-//   reduce blocks [0, rs_blocks): lane t of block b reduces pack
-//     idx = b * threads + t of this rank's shard (idx < own), reading pack
-//     rank * part + idx of every input, writing pack idx of tmps[rank] and,
-//     when the gather runs in the same launch, the same pack of out;
+//   reduce blocks [0, rs_blocks): lane t of block b reduces packs
+//     idx = b * threads * rpl + c * threads + t, c < rpl, of this rank's
+//     shard (idx < own), reading pack rank * part + idx of every input,
+//     writing pack idx of tmps[rank] and, when the gather runs in the same
+//     launch, the same pack of out;
 //   copy blocks: cp_blocks per shard copied (W - 1 shards after a reduce, the
 //     W shards for a gather alone); block k of them copies shard
 //     g = (rank + i) mod W, i = (reduce ? 1 : 0) + k / cp_blocks, lane t
@@ -38,21 +39,23 @@ struct TwoStageGrid {
 };
 
 constexpr TwoStageGrid two_stage_grid(int W, int rank, int64_t packs, bool rs, bool ag,
-                                      int threads, int cpl)
+                                      int threads, int rpl, int cpl)
 {
     TwoStageGrid g{};
     g.part = packs / W;
     g.rem = packs % W;
     g.own = g.part + (rank == W - 1 ? g.rem : 0);
     g.cap = g.part + g.rem;
-    g.rs_blocks = rs ? (g.own + threads - 1) / threads : 0;
+    const int64_t per_rs_block = (int64_t)threads * rpl;
+    g.rs_blocks = rs ? (g.own + per_rs_block - 1) / per_rs_block : 0;
     const int64_t per_block = (int64_t)threads * cpl;
     g.cp_blocks = (g.cap + per_block - 1) / per_block;
     g.blocks = g.rs_blocks + (ag ? (int64_t)(rs ? W - 1 : W) * g.cp_blocks : 0);
     return g;
 }
 
-// What one lane does for its c-th pack (c < cpl; reduce lanes have one).
+// What one lane does for its c-th pack (c < rpl in a reduce block, c < cpl
+// in a copy block).
 struct TwoStageLane {
     int kind;            // 0: nothing, 1: reduce, 2: copy
     int shard;           // copy: the shard g read from tmps[g]
@@ -62,12 +65,12 @@ struct TwoStageLane {
 };
 
 constexpr TwoStageLane two_stage_lane(const TwoStageGrid &g, int W, int rank, bool rs,
-                                      int threads, int cpl, int64_t b, int t, int c)
+                                      int threads, int rpl, int cpl, int64_t b, int t, int c)
 {
     TwoStageLane l{};
     if (rs && b < g.rs_blocks) {
-        const int64_t idx = b * threads + t;
-        if (c == 0 && idx < g.own) {
+        const int64_t idx = b * threads * rpl + (int64_t)c * threads + t;
+        if (c < rpl && idx < g.own) {
             l.kind = 1;
             l.read = (int64_t)rank * g.part + idx;
             l.tmp = idx;
@@ -75,6 +78,8 @@ constexpr TwoStageLane two_stage_lane(const TwoStageGrid &g, int W, int rank, bo
         }
         return l;
     }
+    if (c >= cpl)
+        return l;
     // block numbers fit 32 bits (a grid is at most 2^32 - 1 blocks), and
     // 32-bit division is far cheaper on the GPU than 64-bit
     const uint32_t k = (uint32_t)(rs ? b - g.rs_blocks : b);

@@ -68,26 +68,36 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_1stage_kernel(
 //       inside the launch.
 //   copy blocks (AG): CPL packs per lane of the other shards (of every shard
 //       for a gather alone), tmps[g] -> out.
+// A reduce lane takes RPL packs, all of their W loads issued before any sum.
 // The gather reads use plain loads and everything else streams: on cold
 // data that measured fastest among the cache-policy combinations.
-template <int W, bool RS, bool AG, int CPL>
-__global__ __launch_bounds__(kReduceThreads) void reduce_2stage_kernel(
+template <int W, bool RS, bool AG, int T, int RPL, int CPL>
+__global__ __launch_bounds__(T) void reduce_2stage_kernel(
     InTable<W> in, OutTable<W> tmps, int rank, u32x4 *out, TwoStageGrid grid)
 {
     const int64_t b = blockIdx.x;
     const int t = threadIdx.x;
     if (RS && b < grid.rs_blocks) {
-        const TwoStageLane l = two_stage_lane(grid, W, rank, RS, kReduceThreads, CPL, b, t, 0);
-        if (l.kind != 1)
-            return;
-        u32x4 v[W];
+        TwoStageLane l[RPL];
+        u32x4 v[RPL][W];
 #pragma unroll
-        for (int r = 0; r < W; ++r)
-            v[r] = ld_stream(in.p[r] + l.read);
-        const u32x4 s = reduce_column<W>(v);
-        st_stream(tmps.p[rank] + l.tmp, s);
-        if (AG)
-            st_stream(out + l.out, s);
+        for (int c = 0; c < RPL; ++c) {
+            l[c] = two_stage_lane(grid, W, rank, RS, T, RPL, CPL, b, t, c);
+            if (l[c].kind == 1) {
+#pragma unroll
+                for (int r = 0; r < W; ++r)
+                    v[c][r] = ld_stream(in.p[r] + l[c].read);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < RPL; ++c) {
+            if (l[c].kind != 1)
+                continue;
+            const u32x4 s = reduce_column<W>(v[c]);
+            st_stream(tmps.p[rank] + l[c].tmp, s);
+            if (AG)
+                st_stream(out + l[c].out, s);
+        }
         return;
     }
     if (!AG)
@@ -96,7 +106,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_2stage_kernel(
     u32x4 v[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-        l[c] = two_stage_lane(grid, W, rank, RS, kReduceThreads, CPL, b, t, c);
+        l[c] = two_stage_lane(grid, W, rank, RS, T, RPL, CPL, b, t, c);
         if (l[c].kind == 2)
             v[c] = tmps.p[l[c].shard][l[c].read];
     }
@@ -134,17 +144,28 @@ hipError_t launch_reduce_1stage(const void *const *inputs, int W, void *out,
     }
 }
 
+template <int W, bool RS, bool AG, int T, int RPL, int CPL>
+static hipError_t launch_2stage_shape(const InTable<W> &in, const OutTable<W> &tmps,
+                                      int rank, void *out, int64_t packs, hipStream_t s)
+{
+    const TwoStageGrid g = two_stage_grid(W, rank, packs, RS, AG, T, RPL, CPL);
+    if (g.blocks == 0)
+        return hipSuccess;
+    reduce_2stage_kernel<W, RS, AG, T, RPL, CPL><<<dim3((unsigned)g.blocks), dim3(T), 0, s>>>(
+        in, tmps, rank, static_cast<u32x4 *>(out), g);
+    return hipGetLastError();
+}
+
+// 256 lanes, one pack per reduce lane and two per gather lane.  Timed at the
+// 8 MB cap (W = 8, cold buffers, back to back), this beat every other shape
+// tried: 5.10 us against 5.22 us with one gather pack per lane; four gather
+// packs, two reduce packs, and 128-, 512- or 1,024-lane workgroups were all
+// slower (5.8-7.2 us).
 template <int W, bool RS, bool AG>
 static hipError_t launch_2stage_mode(const InTable<W> &in, const OutTable<W> &tmps,
                                      int rank, void *out, int64_t packs, hipStream_t s)
 {
-    constexpr int kCpl = 1;
-    const TwoStageGrid g = two_stage_grid(W, rank, packs, RS, AG, kReduceThreads, kCpl);
-    if (g.blocks == 0)
-        return hipSuccess;
-    reduce_2stage_kernel<W, RS, AG, kCpl><<<dim3((unsigned)g.blocks), dim3(kReduceThreads), 0,
-                                           s>>>(in, tmps, rank, static_cast<u32x4 *>(out), g);
-    return hipGetLastError();
+    return launch_2stage_shape<W, RS, AG, kReduceThreads, 1, 2>(in, tmps, rank, out, packs, s);
 }
 
 template <int W>

@@ -19,8 +19,8 @@ static long g_failures = 0;
     do {                                                           \
         if (!(cond)) {                                             \
             if (g_failures < 20) {                                 \
-                std::printf("FAIL W=%d P=%lld rank=%d rs=%d ag=%d cpl=%d: ", W, (long long)P, \
-                            rank, (int)rs, (int)ag, cpl);          \
+                std::printf("FAIL W=%d P=%lld rank=%d rs=%d ag=%d threads=%d rpl=%d cpl=%d: ", \
+                            W, (long long)P, rank, (int)rs, (int)ag, threads, rpl, cpl); \
                 std::printf(__VA_ARGS__);                          \
                 std::printf("\n");                                 \
             }                                                      \
@@ -30,20 +30,22 @@ static long g_failures = 0;
 
 // One launch of one rank.  Buffers: W inputs of P packs, W staging buffers of
 // cap packs (the header's minimum), out of P packs.
-static void check_launch(int W, long long P, int rank, bool rs, bool ag, int threads, int cpl)
+static void check_launch(int W, long long P, int rank, bool rs, bool ag, int threads, int rpl,
+                         int cpl)
 {
-    const TwoStageGrid g = ar::two_stage_grid(W, rank, P, rs, ag, threads, cpl);
+    const TwoStageGrid g = ar::two_stage_grid(W, rank, P, rs, ag, threads, rpl, cpl);
     CHECK(g.blocks >= 0 && g.blocks < (1LL << 32), "grid of %lld blocks", (long long)g.blocks);
     CHECK(g.cap == g.part + g.rem && g.part == P / W && g.rem == P % W, "partition");
     std::vector<unsigned char> out_writes((size_t)P, 0), tmp_writes((size_t)g.cap, 0);
     for (long long b = 0; b < g.blocks; ++b) {
         for (int t = 0; t < threads; ++t) {
-            for (int c = 0; c < cpl; ++c) {
-                const TwoStageLane l = ar::two_stage_lane(g, W, rank, rs, threads, cpl, b, t, c);
+            for (int c = 0; c < (rpl > cpl ? rpl : cpl); ++c) {
+                const TwoStageLane l =
+                    ar::two_stage_lane(g, W, rank, rs, threads, rpl, cpl, b, t, c);
                 if (l.kind == 0)
                     continue;
                 if (l.kind == 1) {
-                    CHECK(rs && b < g.rs_blocks && c == 0, "reduce lane outside the reduce blocks");
+                    CHECK(rs && b < g.rs_blocks && c < rpl, "reduce lane outside the reduce blocks");
                     CHECK(l.read >= 0 && l.read < P, "input pack %lld of %lld", (long long)l.read, P);
                     CHECK(l.tmp >= 0 && l.tmp < g.own && g.own <= g.cap,
                           "staging pack %lld of %lld", (long long)l.tmp, (long long)g.cap);
@@ -56,7 +58,8 @@ static void check_launch(int W, long long P, int rank, bool rs, bool ag, int thr
                             ++out_writes[(size_t)l.out];
                     }
                 } else {
-                    CHECK(ag && !(rs && b < g.rs_blocks), "copy lane outside the copy blocks");
+                    CHECK(ag && !(rs && b < g.rs_blocks) && c < cpl,
+                          "copy lane outside the copy blocks");
                     CHECK(l.shard >= 0 && l.shard < W, "shard %d", l.shard);
                     CHECK(!(rs && l.shard == rank), "own shard copied after the reduce");
                     const long long size = g.part + (l.shard == W - 1 ? g.rem : 0);
@@ -81,7 +84,8 @@ static void check_launch(int W, long long P, int rank, bool rs, bool ag, int thr
 int main(int argc, char **argv)
 {
     // argv: threads, then any number of "W P" pairs; every rank, every stage
-    // combination and 1, 2 and 4 packs per copy lane are checked for each.
+    // combination, 1 and 2 packs per reduce lane and 1, 2 and 4 packs per
+    // copy lane are checked for each.
     if (argc < 4 || (argc - 2) % 2 != 0) {
         std::printf("usage: %s threads W P [W P ...]\n", argv[0]);
         return 2;
@@ -93,11 +97,12 @@ int main(int argc, char **argv)
         const long long P = std::atoll(argv[a + 1]);
         for (int rank = 0; rank < W; ++rank)
             for (int mode = 0; mode < 3; ++mode)
-                for (int cpl : {1, 2, 4}) {
-                    const bool rs = mode != 1, ag = mode != 0;
-                    check_launch(W, P, rank, rs, ag, threads, cpl);
-                    ++launches;
-                }
+                for (int rpl : {1, 2})
+                    for (int cpl : {1, 2, 4}) {
+                        const bool rs = mode != 1, ag = mode != 0;
+                        check_launch(W, P, rank, rs, ag, threads, rpl, cpl);
+                        ++launches;
+                    }
     }
     std::printf("%ld launches checked, %ld failures\n", launches, g_failures);
     return g_failures == 0 ? 0 : 1;

@@ -9,7 +9,8 @@ reduced, and every output and staging pack must be written exactly once.
 
 Cases: the message size of the 8 MB cap (W = 8, 4,194,304 bf16 = 524,288
 packs) for every rank as reduce-scatter alone, all-gather alone and both, with
-1, 2 and 4 packs per copy lane -- including the stage-only launches a bench
+1 and 2 packs per reduce lane and 1, 2 and 4 per copy lane, on 256- and
+512-lane workgroups -- including the stage-only launches a bench
 row ran back to back over 23 buffer sets (the sets differ only in their
 addresses, not in any index) -- and every W from 2 to 8 with pack counts that
 leave remainders, down to fewer packs than ranks.
@@ -39,9 +40,10 @@ def run(exe, *args):
     return r.stdout
 
 
-def test_cap_message_every_rank_and_stage(checker):
-    out = run(checker, 256, 8, 524_288)
-    assert "72 launches checked, 0 failures" in out        # 8 ranks x 3 stages x 3 widths
+@pytest.mark.parametrize("threads", [256, 512])
+def test_cap_message_every_rank_and_stage(checker, threads):
+    out = run(checker, threads, 8, 524_288)
+    assert "144 launches checked, 0 failures" in out     # 8 ranks x 3 stages x 6 widths
 
 
 @pytest.mark.parametrize("W", range(2, 9))
@@ -52,7 +54,7 @@ def test_ragged_sizes_every_world_size(checker, W):
     for P in sizes:
         args += [W, P]
     out = run(checker, 256, *args)
-    assert f"{len(sizes) * W * 9} launches checked, 0 failures" in out
+    assert f"{len(sizes) * W * 18} launches checked, 0 failures" in out
 
 
 def test_the_checker_catches_a_planted_out_of_range_map(checker, tmp_path):
