@@ -87,6 +87,17 @@ __device__ __forceinline__ u32x4 load16_coherent(const u32x4 *row, int idx, int 
     return __builtin_amdgcn_raw_buffer_load_b128(r, idx * 16, 0, 1 | 16 /* sc0 | sc1 */);
 }
 
+// System-coherent (sc0 sc1) store of 16-byte chunk idx of a row of `count`
+// chunks: acknowledged only once visible to every XCD, so a reader in
+// another workgroup of the same launch (possibly on another XCD, whose L2 is
+// not coherent with the writer's) sees it with system-coherent loads.
+__device__ __forceinline__ void store16_coherent(u32x4 *row, int idx, int count, u32x4 v)
+{
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        row, 0, count * 16, 0x00020000 /* 32-bit data format */);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, idx * 16, 0, 1 | 16 /* sc0 | sc1 */);
+}
+
 // Kernel-argument pointer tables, passed by value so no device-side
 // indirection is needed (the W pointers land in SGPRs).
 template <int W>

@@ -110,16 +110,19 @@ __device__ __forceinline__ u32x4 normalize8(const float (&h)[8], float rms, u32x
     return narrow8(y);
 }
 
-// NT lanes per row, each lane owning PPL packs: packs t, t + NT, ... so a
-// wavefront's loads of one pack index are 1 KiB contiguous.
-template <int W, int NT, int PPL, bool LAMPORT, bool PUSH>
-__global__ __launch_bounds__(NT) void fused_rmsnorm_kernel(
-    InTable<W> in, const u32x4 *residual, const u32x4 *weight,
+// One row for one workgroup.  NT lanes per row, each lane owning PPL packs:
+// packs t, t + NT, ... so a wavefront's loads of one pack index are 1 KiB
+// contiguous.
+// With COHERENT_PUSH the push stores are system-coherent, for readers in
+// the same launch; otherwise they stream, for readers in later launches.
+template <int W, int NT, int PPL, bool LAMPORT, bool PUSH, bool COHERENT_PUSH = false>
+__device__ __forceinline__ void fused_row(
+    const InTable<W> &in, const u32x4 *residual, const u32x4 *weight,
     u32x4 *residual_out, u32x4 *norm_out, int packs_per_row, float n_cols,
-    float eps, LamportArgs<W> la)
+    float eps, const LamportArgs<W> &la, int64_t row)
 {
     const int t = threadIdx.x;
-    const int64_t row0 = (int64_t)blockIdx.x * packs_per_row;
+    const int64_t row0 = row * packs_per_row;
 
     // Every load of the row is issued before any store, so the one-launch
     // call's push (which needs its own pack first) does not delay the reads
@@ -149,8 +152,12 @@ __global__ __launch_bounds__(NT) void fused_rmsnorm_kernel(
             if (idx < packs_per_row) {
                 own[p] = scrub_negative_zero(own[p]);
 #pragma unroll
-                for (int q = 0; q < W; ++q)
-                    st_stream(la.push[q] + row0 + idx, own[p]);
+                for (int q = 0; q < W; ++q) {
+                    if (COHERENT_PUSH)
+                        store16_coherent(la.push[q] + row0, idx, packs_per_row, own[p]);
+                    else
+                        st_stream(la.push[q] + row0 + idx, own[p]);
+                }
 #pragma unroll
                 for (int r = 0; r < W; ++r)
                     if (r == la.rank)
@@ -232,6 +239,64 @@ __global__ __launch_bounds__(NT) void fused_rmsnorm_kernel(
             norm_out[row0 + idx] = normalize8(h[p], rms, wv[p]);
         }
     }
+}
+
+// One workgroup per row.
+template <int W, int NT, int PPL, bool LAMPORT, bool PUSH>
+__global__ __launch_bounds__(NT) void fused_rmsnorm_kernel(
+    InTable<W> in, const u32x4 *residual, const u32x4 *weight,
+    u32x4 *residual_out, u32x4 *norm_out, int packs_per_row, float n_cols,
+    float eps, LamportArgs<W> la)
+{
+    fused_row<W, NT, PPL, LAMPORT, PUSH>(in, residual, weight, residual_out, norm_out,
+                                         packs_per_row, n_cols, eps, la, blockIdx.x);
+}
+
+// The Lamport exchange of all W ranks in one launch, as W GPUs run it at the
+// same time ([TRIAR] "Option 2: Lamport"): workgroup (row m, rank r) runs
+// rank r's one-launch program on row m -- push row m of x[r] into slot r of
+// the region in use of every comm buffer, wait for the W - 1 peer slots of
+// row m in comm[r], reduce, add the residual, normalise into rank r's
+// outputs, and reset row m of the previous region of comm[r].  The peers'
+// pushes land while the reader polls, so the re-read path runs.  The
+// workgroups of one row sit on different XCDs, whose L2 caches are not
+// coherent with each other inside a launch, so the pushes are
+// system-coherent stores and the re-reads system-coherent loads.  Every
+// workgroup of the launch is resident at once (checked by the host), so
+// every push is made and every wait ends.
+template <int W>
+struct LamportAllArgs {
+    const u32x4 *x[W];            // rank r's rows
+    u32x4 *comm[W];               // rank r's comm buffer
+    u32x4 *residual_out[W];
+    u32x4 *norm_out[W];
+    int64_t chunks;               // 16-byte chunks of one slot (M * N / 8)
+    int use, reset;               // regions of this call and of the previous one
+    uint32_t max_spins;
+    uint32_t *bad;
+};
+
+template <int W, int NT, int PPL>
+__global__ __launch_bounds__(NT) void lamport_all_ranks_kernel(
+    const u32x4 *residual, const u32x4 *weight, int packs_per_row, float n_cols, float eps,
+    LamportAllArgs<W> a)
+{
+    const int rank = blockIdx.y;
+    InTable<W> in;
+    LamportArgs<W> la;
+#pragma unroll
+    for (int r = 0; r < W; ++r) {
+        in.p[r] = a.comm[rank] + ((int64_t)a.use * W + r) * a.chunks;
+        la.reset[r] = a.comm[rank] + ((int64_t)a.reset * W + r) * a.chunks;
+        la.push[r] = a.comm[r] + ((int64_t)a.use * W + rank) * a.chunks;
+    }
+    la.max_spins = a.max_spins;
+    la.bad = a.bad;
+    la.x_self = a.x[rank];
+    la.rank = rank;
+    fused_row<W, NT, PPL, true, true, true>(in, residual, weight, a.residual_out[rank],
+                                            a.norm_out[rank], packs_per_row, n_cols, eps, la,
+                                            blockIdx.x);
 }
 
 template <int W, int NT, int PPL, bool LAMPORT, bool PUSH>
@@ -317,6 +382,92 @@ static hipError_t launch_lamport_w(void *comm, const void *residual, const void 
         la.push[q] = static_cast<u32x4 *>(comms[q]) + (use * W + rank) * chunks;
     return launch_fused_w<W, true, true>(in, residual, weight, residual_out, norm_out, M, N,
                                          eps, la, s);
+}
+
+template <int W, int NT, int PPL>
+static hipError_t launch_all_ranks_shape(const void *const *xs, void *const *comms,
+                                         const void *residual, const void *weight,
+                                         void *const *residual_outs, void *const *norm_outs,
+                                         int64_t M, int64_t N, float eps, uint32_t flag,
+                                         uint32_t max_spins, uint32_t *bad, bool check_only,
+                                         int *resident, hipStream_t s)
+{
+    const void *fn = reinterpret_cast<const void *>(&lamport_all_ranks_kernel<W, NT, PPL>);
+    if (check_only) {
+        int dev = 0, cus = 0, per_cu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess)
+            e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, 0);
+        *resident = e == hipSuccess ? cus * per_cu : 0;
+        return e;
+    }
+    LamportAllArgs<W> a{};
+    for (int r = 0; r < W; ++r) {
+        a.x[r] = static_cast<const u32x4 *>(xs[r]);
+        a.comm[r] = static_cast<u32x4 *>(comms[r]);
+        a.residual_out[r] = static_cast<u32x4 *>(residual_outs[r]);
+        a.norm_out[r] = static_cast<u32x4 *>(norm_outs[r]);
+    }
+    a.chunks = M * N / 8;
+    a.use = (int)(flag % 3u);
+    a.reset = (a.use + 2) % 3;
+    a.max_spins = max_spins;
+    a.bad = bad;
+    lamport_all_ranks_kernel<W, NT, PPL><<<dim3((unsigned)M, (unsigned)W), dim3(NT), 0, s>>>(
+        static_cast<const u32x4 *>(residual), static_cast<const u32x4 *>(weight), (int)(N / 8),
+        (float)N, eps, a);
+    return hipGetLastError();
+}
+
+template <int W>
+static hipError_t launch_all_ranks_w(const void *const *xs, void *const *comms,
+                                     const void *residual, const void *weight,
+                                     void *const *residual_outs, void *const *norm_outs,
+                                     int64_t M, int64_t N, float eps, uint32_t flag,
+                                     uint32_t max_spins, uint32_t *bad, bool check_only,
+                                     int *resident, hipStream_t s)
+{
+    const int64_t packs = N / 8;
+#define AR_ALL_RANKS(NT, PPL)                                                             \
+    return launch_all_ranks_shape<W, NT, PPL>(xs, comms, residual, weight, residual_outs, \
+                                              norm_outs, M, N, eps, flag, max_spins, bad,  \
+                                              check_only, resident, s)
+    if (packs <= 64)
+        AR_ALL_RANKS(64, 1);
+    if (packs <= 256)
+        AR_ALL_RANKS(256, 1);
+    if (packs <= 512)
+        AR_ALL_RANKS(512, 1);
+    if (packs <= 1024)
+        AR_ALL_RANKS(1024, 1);
+    AR_ALL_RANKS(1024, 2);
+#undef AR_ALL_RANKS
+}
+
+hipError_t launch_lamport_all_ranks(const void *const *xs, void *const *comms, int W,
+                                    const void *residual, const void *weight,
+                                    void *const *residual_outs, void *const *norm_outs,
+                                    int64_t M, int64_t N, float eps, uint32_t flag,
+                                    uint32_t max_spins, uint32_t *bad, bool check_only,
+                                    int *resident, hipStream_t s)
+{
+    switch (W) {
+#define AR_ALL_CASE(w)                                                                     \
+    case w:                                                                                \
+        return launch_all_ranks_w<w>(xs, comms, residual, weight, residual_outs, norm_outs, \
+                                     M, N, eps, flag, max_spins, bad, check_only, resident, s);
+    AR_ALL_CASE(2)
+    AR_ALL_CASE(3)
+    AR_ALL_CASE(4)
+    AR_ALL_CASE(5)
+    AR_ALL_CASE(6)
+    AR_ALL_CASE(7)
+    AR_ALL_CASE(8)
+#undef AR_ALL_CASE
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_fused_rmsnorm(const void *const *inputs, int W,

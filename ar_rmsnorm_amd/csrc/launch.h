@@ -39,6 +39,16 @@ hipError_t launch_lamport_fused(void *comm, int W, const void *residual,
                                 uint32_t max_spins, uint32_t *bad, const void *x_self,
                                 int rank, void *const *comms, hipStream_t s);
 
+// The Lamport exchange of all W ranks in one launch (M x W workgroups).
+// With check_only nothing is launched: *resident receives how many of its
+// workgroups the current device holds at once.
+hipError_t launch_lamport_all_ranks(const void *const *xs, void *const *comms, int W,
+                                    const void *residual, const void *weight,
+                                    void *const *residual_outs, void *const *norm_outs,
+                                    int64_t M, int64_t N, float eps, uint32_t flag,
+                                    uint32_t max_spins, uint32_t *bad, bool check_only,
+                                    int *resident, hipStream_t s);
+
 // One launch of 2 * channels workgroups (producers, then consumers), all of
 // which the caller has checked can be resident at once in the chosen
 // geometry (wide: 1,024 lanes per workgroup, else 512).

@@ -327,23 +327,22 @@ LIBAR_EXPORT ar_status_t ar_fused_residual_rmsnorm_2stage(
 }
 
 // One-GPU choice between the fused forms.  Per rank the one-shot call reads
-// W input rows, the residual and writes two outputs for every row: (W + 3)
+// W input rows and the residual and writes two outputs for every row: W + 3
 // rows of traffic per row.  The two-shot call does that only for its M / W
 // own rows (plus staging them) and copies two staged rows for every other
-// row: about 4 + (W + 5) / W rows per row, less for W >= 3.  With M < W one
-// owner takes every row and nothing is saved; at small M both calls are
-// bound by the launch, and the two-shot call's extra workgroups cost more
-// than its saved bytes.  The row counts below are where the two-shot call
-// measured faster for one rank on one MI355X.
+// row: about 4 + 5 / W rows per row, fewer from W = 3 on, and its per-row
+// latency chain is one row's loads, not W rows'.  Timed for one rank on one
+// MI355X (cold buffers, N = 2048 and 8192, M from W to 2048 rows), the
+// two-shot call was faster at every M >= W for W = 4 and W = 8, by 6-60 %;
+// for W = 2 the two forms were within 3 % either way, and the one-shot call
+// is kept (it needs no staging and, on several GPUs, no second exchange).
+// With M < W one owner would take every row, which saves nothing.
 LIBAR_EXPORT int ar_fused_prefers_two_shot(int W, int64_t M, int64_t N)
 {
     if (W < 2 || W > AR_MAX_WORLD || M < 0 || M > 0x7FFFFFFF || N < 8 ||
         N > AR_FUSED_MAX_N || N % 8 != 0)
         return -1;
-    if (W == 2 || M < W)
-        return 0;
-    const int64_t min_rows = N <= 2048 ? 16 : 32;
-    return M >= min_rows ? 1 : 0;
+    return (W >= 3 && M >= W) ? 1 : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -505,6 +504,72 @@ LIBAR_EXPORT ar_status_t ar_lamport_oneshot_residual_rmsnorm(
     return from_hip(ar::launch_lamport_fused(comms[rank], W, residual, weight, residual_out,
                                              norm_out, M, N, eps, flag, max_spins, bad_chunks,
                                              x, rank, comms, static_cast<hipStream_t>(stream)));
+}
+
+LIBAR_EXPORT ar_status_t ar_lamport_all_ranks_residual_rmsnorm(
+    const void *const *xs, void *const *comms, int W, const void *residual, const void *weight,
+    void *const *residual_outs, void *const *norm_outs, int64_t M, int64_t N, float eps,
+    uint32_t flag, uint32_t max_spins, uint32_t *bad_chunks, ar_stream_t stream)
+{
+    if (!xs || !comms || !residual || !weight || !residual_outs || !norm_outs)
+        return AR_ERR_NULL;
+    if (W < 2 || W > AR_MAX_WORLD)
+        return AR_ERR_WORLD;
+    for (int r = 0; r < W; ++r)
+        if (!xs[r] || !comms[r] || !residual_outs[r] || !norm_outs[r])
+            return AR_ERR_NULL;
+    if (!fused_shape_ok(M, N) || max_spins > AR_MAX_SPINS || !(eps >= 0.0f) || eps > 3.0e38f ||
+        flag >= AR_LAMPORT_FLAG_PERIOD)
+        return AR_ERR_ARG;
+    if (!aligned(residual, 16) || !aligned(weight, 16) || (bad_chunks && !aligned(bad_chunks, 4)))
+        return AR_ERR_ALIGN;
+    for (int r = 0; r < W; ++r)
+        if (!aligned(xs[r], 16) || !aligned(comms[r], 16) || !aligned(residual_outs[r], 16) ||
+            !aligned(norm_outs[r], 16))
+            return AR_ERR_ALIGN;
+    const int64_t mat = 2 * M * N, vec = 2 * N, cb = ar_lamport_comm_bytes(W, M, N);
+    // every rank reads the shared residual and weight while the others write
+    // their outputs, so no output may overlap any input or another output
+    for (int r = 0; r < W; ++r) {
+        const void *outs[2] = {residual_outs[r], norm_outs[r]};
+        for (const void *o : outs) {
+            if (overlaps(o, mat, residual, mat) || overlaps(o, mat, weight, vec) ||
+                (bad_chunks && overlaps(o, mat, bad_chunks, 4)))
+                return AR_ERR_ARG;
+            for (int q = 0; q < W; ++q)
+                if (overlaps(o, mat, xs[q], mat) || overlaps(o, mat, comms[q], cb))
+                    return AR_ERR_ARG;
+        }
+        if (overlaps(residual_outs[r], mat, norm_outs[r], mat))
+            return AR_ERR_ARG;
+        for (int q = 0; q < r; ++q)
+            if (overlaps(residual_outs[r], mat, residual_outs[q], mat) ||
+                overlaps(residual_outs[r], mat, norm_outs[q], mat) ||
+                overlaps(norm_outs[r], mat, residual_outs[q], mat) ||
+                overlaps(norm_outs[r], mat, norm_outs[q], mat))
+                return AR_ERR_ARG;
+        const void *c = comms[r];
+        if (overlaps(c, cb, residual, mat) || overlaps(c, cb, weight, vec) ||
+            (bad_chunks && overlaps(c, cb, bad_chunks, 4)))
+            return AR_ERR_ARG;
+        for (int q = 0; q < W; ++q)
+            if (overlaps(c, cb, xs[q], mat) || (q < r && overlaps(c, cb, comms[q], cb)))
+                return AR_ERR_ARG;
+    }
+    if (M == 0)
+        return AR_OK;
+    int resident = 0;
+    hipError_t e = ar::launch_lamport_all_ranks(xs, comms, W, residual, weight, residual_outs,
+                                                norm_outs, M, N, eps, flag, max_spins,
+                                                bad_chunks, true, &resident, nullptr);
+    if (e != hipSuccess)
+        return from_hip(e);
+    if ((int64_t)resident < M * W)
+        return AR_ERR_CAPACITY;
+    return from_hip(ar::launch_lamport_all_ranks(xs, comms, W, residual, weight, residual_outs,
+                                                 norm_outs, M, N, eps, flag, max_spins,
+                                                 bad_chunks, false, nullptr,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 // ---------------------------------------------------------------------------

@@ -49,7 +49,7 @@ EXPORTS = (
     "ll128_fifo_bytes", "ll_default_step_lines", "ll128_default_step_lines",
     "ar_fifo_stream", "ar_fifo_step_wire_bytes", "ar_fifo_steps_per_channel",
     "ar_fifo_counter_words", "ar_lamport_next_flag", "ar_fused_prefers_two_shot", "ar_copy",
-    "ar_reduce_2stage_noalloc",
+    "ar_reduce_2stage_noalloc", "ar_lamport_all_ranks_residual_rmsnorm",
 )
 AR_PROTO_LL, AR_PROTO_LL128, AR_PROTO_SIMPLE = 0, 1, 2
 AR_FIFO_MAX_CHANNELS = 256
@@ -87,6 +87,10 @@ _lib.ar_lamport_fused_residual_rmsnorm.argtypes = [_vp, _int, _vp, _vp, _vp, _vp
 _lib.ar_lamport_oneshot_residual_rmsnorm.argtypes = [_vp, _int, _pp, _int, _vp, _vp, _vp, _vp,
                                                      _i64, _i64, ctypes.c_float, _u32, _u32,
                                                      _vp, _vp]
+_lib.ar_lamport_all_ranks_residual_rmsnorm.argtypes = [_pp, _pp, _int, _vp, _vp, _pp, _pp, _i64,
+                                                       _i64, ctypes.c_float, _u32, _u32, _vp,
+                                                       _vp]
+_lib.ar_lamport_all_ranks_residual_rmsnorm.restype = _int
 for _n in ("ll_pack", "ll128_pack"):
     getattr(_lib, _n).argtypes = [_vp, _i64, _vp, _i64, _u64, _vp]
 for _n in ("ll_unpack_reduce", "ll128_unpack_reduce"):
@@ -339,6 +343,26 @@ def ar_lamport_oneshot_residual_rmsnorm(x, rank: int, comms: Sequence, residual,
         _addr(residual_out, mat, BF16, "residual_out", w),
         _addr(norm_out, mat, BF16, "norm_out", w), M, N, float(eps), _flag(flag, w), max_spins,
         _addr(bad_chunks, 4, U32, "bad_chunks", w), _stream(stream)), w)
+
+
+def ar_lamport_all_ranks_residual_rmsnorm(xs: Sequence, comms: Sequence, residual, weight,
+                                          residual_outs: Sequence, norm_outs: Sequence,
+                                          eps: float, flag: int, max_spins: int = AR_MAX_SPINS,
+                                          bad_chunks=None, M: Optional[int] = None,
+                                          N: Optional[int] = None, stream=None) -> None:
+    """Every rank's one-launch Lamport call in one launch (W = len(xs)):
+    rank r pushes xs[r] and reads comms[r] into residual_outs[r], norm_outs[r]."""
+    w = "ar_lamport_all_ranks_residual_rmsnorm"
+    if M is None or N is None:
+        M, N = residual.shape
+    mat = 2 * M * N
+    cb = _lib.ar_lamport_comm_bytes(len(xs), M, N)
+    _check(_lib.ar_lamport_all_ranks_residual_rmsnorm(
+        _table(xs, mat, BF16, "xs", w), _table(comms, cb, ANY, "comms", w), len(xs),
+        _addr(residual, mat, BF16, "residual", w), _addr(weight, 2 * N, BF16, "weight", w),
+        _table(residual_outs, mat, BF16, "residual_outs", w),
+        _table(norm_outs, mat, BF16, "norm_outs", w), M, N, float(eps), _flag(flag, w),
+        max_spins, _addr(bad_chunks, 4, U32, "bad_chunks", w), _stream(stream)), w)
 
 
 def ll_pack(src, fifo, step_lines: int, first_step: int = 0, n: Optional[int] = None,

@@ -172,8 +172,9 @@ def trace_summary(d: str) -> str:
     # back-to-back spacing of the headline kernel: consecutive dispatches in
     # start order where both are the headline's launch shape
     allv = sorted((b, e, key) for key, v in groups.items() for b, e in v)
-    head = [k for k in groups if "reduce_2stage_kernel<8, true, true" in k[0]
-            and k[1] == "524288"]
+    # the headline's launch shape: the two-stage W=8 kernel dispatched most often
+    cand = [k for k in groups if "reduce_2stage_kernel<8, true, true" in k[0]]
+    head = sorted(cand, key=lambda k: -len(groups[k]))[:1]
     for hk in head:
         iv, du, gp = [], [], []
         for (b0, e0, k0), (b1, e1, k1) in zip(allv, allv[1:]):
@@ -413,7 +414,7 @@ def main():
             "unit": "GB/s",
             "frac": round(gbps / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "reduce_2stage_kernel<8,true,true,1>",
+            "kernel": "reduce_2stage_kernel<8,true,true,256,1,2>",
             "kernel_us": round(ms_launch * 1e3, 3),
             "kernel_us_timer": "HIP events around the graph replay on the launch stream, "
                                "divided by the launches it holds",
@@ -555,6 +556,37 @@ def main():
                 [oneshot], steps=200)
             del comms
         result["lamport_m1_us_per_call"] = rows["lamport_oneshot_W4_M1_N2048"]["us_per_call"]
+
+        # the Lamport exchange of all W ranks in one launch: each rank's reader
+        # polls slots that other workgroups of the launch are still pushing,
+        # so the re-read path is timed.  Flags run through 0..5 (a multiple of
+        # 3), so every graph replay finds its regions reset as a live run would.
+        for M in fc["Ms"]:
+            fx, fr, fw = synth.fused(M)
+            Wf, N = fc["W"], fc["N"]
+            d = [to_dev(x) for x in fx]
+            dr, dw = to_dev(fr), to_dev(fw)
+            ros = [torch.empty_like(dr) for _ in range(Wf)]
+            nos = [torch.empty_like(dr) for _ in range(Wf)]
+            comms = [torch.empty(ar.ar_lamport_comm_bytes(Wf, M, N) // 4, dtype=torch.int32,
+                                 device=dev) for _ in range(Wf)]
+            for c in comms:
+                ar.ar_lamport_fill(c, Wf, M, N)
+            bad = torch.zeros(1, dtype=torch.int32, device=dev)
+            mat = M * N * 2
+            calls = [(lambda f=f, d=d, comms=comms, dr=dr, dw=dw, ros=ros, nos=nos, bad=bad:
+                      ar.ar_lamport_all_ranks_residual_rmsnorm(d, comms, dr, dw, ros, nos,
+                                                               fc["eps"], f, ar.AR_MAX_SPINS,
+                                                               bad)) for f in range(6)]
+            r = row(f"lamport_all_ranks_W4_M{M}_N2048",
+                    Wf * (mat + Wf * mat + (Wf - 1) * mat + mat + 2 * mat + Wf * mat) + 2 * N,
+                    calls, steps=60)
+            torch.cuda.synchronize()
+            r["bad_chunks"] = int(bad.item())
+            r["note"] = ("the W ranks' one-launch calls as one launch of M x W workgroups; "
+                         "bytes = per rank: its rows, the W pushes, W - 1 peer slots, the "
+                         "residual, two outputs, the W-slot reset")
+            del comms
 
         # the grid of shapes the fused operator's source page benchmarks
         # (M in {1, 8, 128} x N in {2048, 4096, 8192}, W=4, the same buffers

@@ -330,6 +330,34 @@ ar_status_t ar_lamport_oneshot_residual_rmsnorm(const void *x, int rank,
                                                 ar_stream_t stream);
 
 /*
+ * The Lamport exchange of all W ranks in one launch, as W GPUs would run
+ * their one-launch calls at the same time: for every rank r and row m, one
+ * workgroup runs ar_lamport_oneshot_residual_rmsnorm's program for rank r
+ * on row m (push row m of xs[r] into every buffer of comms, wait for the
+ * W - 1 peer slots of row m in comms[r], reduce, add the residual,
+ * normalise into residual_outs[r] and norm_outs[r], reset row m of the
+ * previous region of comms[r]).  The peers' pushes land while a reader
+ * polls, so this is the call that exercises the re-read path on one GPU.
+ * All ranks share one residual and one weight (in tensor parallelism every
+ * rank holds the same residual stream), and every rank's outputs equal what
+ * ar_lamport_fused_residual_rmsnorm gives after all W pushes.
+ *   xs, comms, residual_outs, norm_outs  host tables of W device pointers
+ *            (bf16 [M, N] rows, comm buffers, outputs), 16-byte aligned
+ *   flag, max_spins, bad_chunks, M, N, eps  as the one-launch call
+ *   no output may overlap any input, buffer or other output   else AR_ERR_ARG
+ *   the M * W workgroups must all be resident on the device at once (a
+ *   waiting workgroup must never hold back a push): AR_ERR_CAPACITY when the
+ *   device cannot hold them (M * W above about 2,000 on MI355X at N = 2048)
+ */
+ar_status_t ar_lamport_all_ranks_residual_rmsnorm(const void *const *xs, void *const *comms,
+                                                  int W, const void *residual,
+                                                  const void *weight,
+                                                  void *const *residual_outs,
+                                                  void *const *norm_outs, int64_t M, int64_t N,
+                                                  float eps, uint32_t flag, uint32_t max_spins,
+                                                  uint32_t *bad_chunks, ar_stream_t stream);
+
+/*
  * LL wire format ([NCCL14] "LL's 16-byte FIFO line", "How LL publishes and
  * waits for flags", "Prerequisite mental model").
  * A FIFO is a ring of 8 steps of step_lines 16-byte lines.  The payload

@@ -303,7 +303,7 @@ def test_fused_form_choice():
     assert f(8, 7, 2048) == 0 and f(4, 3, 8192) == 0
     for W in (3, 4, 8):
         assert f(W, 1, 2048) == 0
-        assert f(W, 8192, 2048) == 1 and f(W, 2048, 8192) == 1
+        assert all(f(W, M, N) == 1 for M in (W, 16, 128, 2048, 8192) for N in (2048, 8192))
 
 
 @cpu_only
@@ -327,3 +327,36 @@ def test_reduce_2stage_noalloc_argument_errors():
     big = 8 * ((ar.AR_SCRATCH_BYTES // 16 // W + 1) * W)
     assert st(f, ins, 0, B, 0, big, 0) == ar.AR_ERR_CAPACITY
     assert st(f, ins, 0, None, ar.AR_STAGE_RS, 0, 0) == ar.AR_OK     # nothing to launch
+
+
+@cpu_only
+def test_lamport_all_ranks_argument_errors():
+    f = ar.ar_lamport_all_ranks_residual_rmsnorm
+    W, M, N = 4, 2, 64
+    mat = 2 * M * N
+    G = 1 << 24                                   # spacing of the fake buffers
+    xs = [A + i * G for i in range(W)]
+    comms = [B + i * G for i in range(W)]
+    ros = [C + i * G for i in range(W)]
+    nos = [D + i * G for i in range(W)]
+    res, wt = E, F
+
+    def call(xs=xs, comms=comms, ros=ros, nos=nos, res=res, wt=wt, flag=0, spins=0, M=M, N=N,
+             eps=1e-6):
+        return st(f, xs, comms, res, wt, ros, nos, eps, flag, spins, None, M, N, 0)
+
+    assert call() == ar.AR_ERR_HIP                       # valid: reaches the device
+    assert call(M=0) == ar.AR_OK
+    assert call(xs=xs[:1], comms=comms[:1], ros=ros[:1], nos=nos[:1]) == ar.AR_ERR_WORLD
+    assert call(xs=xs[:-1] + [None]) == ar.AR_ERR_NULL
+    assert call(nos=nos[:-1] + [None]) == ar.AR_ERR_NULL
+    assert call(flag=ar.AR_LAMPORT_FLAG_PERIOD) == ar.AR_ERR_ARG
+    assert call(spins=ar.AR_MAX_SPINS + 1) == ar.AR_ERR_ARG
+    assert call(N=12) == ar.AR_ERR_ARG
+    assert call(eps=-1.0) == ar.AR_ERR_ARG
+    assert call(ros=ros[:-1] + [C + 3 * G + 8]) == ar.AR_ERR_ALIGN
+    assert call(ros=ros[:-1] + [res]) == ar.AR_ERR_ARG            # output on the residual
+    assert call(nos=nos[:-1] + [ros[0]]) == ar.AR_ERR_ARG         # two outputs overlap
+    assert call(ros=ros[:-1] + [xs[1] + mat // 2]) == ar.AR_ERR_ARG  # output inside an input
+    assert call(comms=comms[:-1] + [comms[0]]) == ar.AR_ERR_ARG   # shared comm buffer
+    assert call(xs=xs[:-1] + [comms[2]]) == ar.AR_ERR_ARG         # input inside a comm buffer

@@ -240,3 +240,92 @@ def test_lamport_flag_past_the_period_is_refused(gpu):
     sync()
     for c, b in zip(comms, before):
         assert np.array_equal(host_words(c), b)
+
+
+def run_all_ranks(xs, res, w, comms, hcomms, flag, device, eps=1e-6):
+    """One all-ranks launch (every rank pushes and reads at once), checked
+    against the oracle's pushes of every rank followed by every reader."""
+    W = len(xs)
+    dx = [dev_u16(x, device) for x in xs]
+    dr, dw = dev_u16(res, device), dev_u16(w, device)
+    ros = [torch.empty_like(dr) for _ in range(W)]
+    nos = [torch.empty_like(dr) for _ in range(W)]
+    bad = torch.zeros(1, dtype=torch.int32, device=device)
+    ar.ar_lamport_all_ranks_residual_rmsnorm(dx, comms, dr, dw, ros, nos, eps, flag,
+                                             ar.AR_MAX_SPINS, bad)
+    sync()
+    assert int(bad.item()) == 0, "a peer slot never arrived"
+    for r in range(W):
+        orc.lamport_push(xs[r], r, hcomms, flag)
+    for p in range(W):
+        wro, _, exact, wbad = orc.lamport_fused_residual_rmsnorm(hcomms[p], W, res, w, eps, flag)
+        assert wbad == 0
+        assert np.array_equal(host_u16(ros[p]), wro), f"residual_out, rank {p}"
+        ok, _ = norm_within_tolerance(host_u16(nos[p]), exact)
+        assert ok.all(), f"norm_out, rank {p}"
+    for p in range(W):
+        assert np.array_equal(host_words(comms[p]), hcomms[p]), f"comm buffer of rank {p}"
+
+
+@pytest.mark.parametrize("W,M,N", [(4, 1, 2048), (4, 16, 2048), (4, 128, 2048), (2, 3, 8),
+                                   (8, 5, 1000), (3, 7, 16384)])
+def test_lamport_all_ranks_in_one_launch(gpu, W, M, N):
+    """All ranks' one-launch programs in one launch, over consecutive flags:
+    each rank's reader polls peer slots that other workgroups of the same
+    launch are pushing, and every rank's outputs and buffer match the
+    oracle's call sequence."""
+    comms = new_comms(W, M, N, gpu)
+    hcomms = [orc.lamport_comm(W, M, N) for _ in range(W)]
+    for f in range(4):
+        xs, res, w = synth.fused_inputs(W, M, N, [98, W, M, N, f])
+        run_all_ranks(xs, res, w, comms, hcomms, f, gpu)
+
+
+def test_lamport_all_ranks_graph_replays(gpu):
+    """The all-ranks launch captured for flags 0..5 and replayed three times
+    (with eager work between): every replay leaves outputs equal to the
+    eager launch's and no chunk missing."""
+    W, M, N, eps = 4, 16, 2048, 1e-6
+    xs, res, w = synth.fused_inputs(W, M, N, [99])
+    dx = [dev_u16(x, gpu) for x in xs]
+    dr, dw = dev_u16(res, gpu), dev_u16(w, gpu)
+    comms = new_comms(W, M, N, gpu)
+    ros = [torch.empty_like(dr) for _ in range(W)]
+    nos = [torch.empty_like(dr) for _ in range(W)]
+    bad = torch.zeros(1, dtype=torch.int32, device=gpu)
+    calls = [lambda f=f: ar.ar_lamport_all_ranks_residual_rmsnorm(
+        dx, comms, dr, dw, ros, nos, eps, f, ar.AR_MAX_SPINS, bad) for f in range(6)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in calls:
+            c()
+    torch.cuda.current_stream().wait_stream(s)
+    sync()
+    want = [(host_u16(a), host_u16(b)) for a, b in zip(ros, nos)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    for rep in range(3):
+        for t in ros + nos:
+            t.zero_()
+        sync()
+        g.replay()
+        sync()
+        assert int(bad.item()) == 0, f"replay {rep}: a slot never arrived"
+        for p in range(W):
+            assert np.array_equal(host_u16(ros[p]), want[p][0]), (rep, p)
+            assert np.array_equal(host_u16(nos[p]), want[p][1]), (rep, p)
+
+
+def test_lamport_all_ranks_refuses_what_cannot_be_resident(gpu):
+    W, M, N = 8, 4096, 2048
+    x = torch.zeros((M, N), dtype=torch.int16, device=gpu)
+    comms = [torch.empty(ar.ar_lamport_comm_bytes(W, M, N) // 4, dtype=torch.int32, device=gpu)
+             for _ in range(W)]
+    outs = [torch.empty_like(x) for _ in range(2 * W)]
+    with pytest.raises(ar.ArError) as e:
+        ar.ar_lamport_all_ranks_residual_rmsnorm([x] * W, comms, x.clone(), x[0].clone(),
+                                                 outs[:W], outs[W:], 1e-6, 0)
+    assert e.value.status == ar.AR_ERR_CAPACITY
