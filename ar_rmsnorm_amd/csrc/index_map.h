@@ -1,8 +1,9 @@
-// Block and lane index map of the two-stage reduce, as plain C++17 constexpr
-// functions.  HIP device code may call constexpr functions, so the kernel
-// uses exactly these; the host can compile them with any C++17 compiler, so
-// every (block, lane) of a launch can be enumerated and bounds-checked on a
-// CPU.  No HIP header is needed here.
+// Index maps as plain C++17 constexpr functions: the block and lane map of
+// the two-stage reduce, and the slices that the producer/consumer pairs of a
+// streaming channel own.  HIP device code may call constexpr functions, so
+// the kernels use exactly these; the host can compile them with any C++17
+// compiler, so every (block, lane) of a launch and every slice of a ring can
+// be enumerated and checked on a CPU.  No HIP header is needed here.
 //
 // Source (web page; cited by tag and section):
 //   [SGLv1] "SGLang Custom AllReduce v1 线程模型和工作原理细节" (todaynews.cc),
@@ -97,6 +98,52 @@ constexpr TwoStageLane two_stage_lane(const TwoStageGrid &g, int W, int rank, bo
         l.out = (int64_t)s * g.part + idx;
     }
     return l;
+}
+
+// ---------------------------------------------------------------------------
+// Streaming: a channel's steps may be shared by `pairs` producer/consumer
+// pairs.  Pair g owns the same region of every ring slot: items
+// [g * span, (g + 1) * span) of a full step of `full` items, span being
+// ceil(full / pairs) rounded up to whole `unit`s (16 items = one LL128 line
+// pair).  In a step of `total` <= full items (only the last step of a
+// payload can be shorter) the slice is that region cut to [0, total), so it
+// may be empty for the later pairs.
+constexpr int64_t fifo_span(int64_t full, int64_t unit, int pairs)
+{
+    return ((full + pairs - 1) / pairs + unit - 1) / unit * unit;
+}
+
+// Pair `pair`'s slice of a step of `total` items, given the span.
+constexpr void fifo_slice_at(int64_t span, int64_t total, int pair, int64_t *lo, int64_t *hi)
+{
+    const int64_t start = (int64_t)pair * span;
+    *lo = start < total ? start : total;
+    *hi = *lo + span < total ? *lo + span : total;
+}
+
+constexpr void fifo_slice(int64_t full, int64_t total, int64_t unit, int pairs, int pair,
+                          int64_t *lo, int64_t *hi)
+{
+    fifo_slice_at(fifo_span(full, unit, pairs), total, pair, lo, hi);
+}
+
+// Pairs per channel when `resident` workgroups fit on the device at once: as
+// many as fit (two workgroups per pair), at most max_pairs, and no more than
+// leave every pair a slice of a full step of at least min_slice items (one
+// pair always).  0 when not even one pair per channel fits.
+constexpr int fifo_pairs_for(int64_t full, int64_t unit, int channels, int resident,
+                             int max_pairs, int64_t min_slice)
+{
+    int g = resident / (2 * channels);
+    if (g > max_pairs)
+        g = max_pairs;
+    for (; g > 1; --g) {
+        int64_t lo = 0, hi = 0;
+        fifo_slice(full, full, unit, g, g - 1, &lo, &hi);
+        if (hi - lo >= min_slice)
+            break;
+    }
+    return g;
 }
 
 }  // namespace ar

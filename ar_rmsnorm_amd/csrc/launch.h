@@ -49,14 +49,18 @@ hipError_t launch_lamport_all_ranks(const void *const *xs, void *const *comms, i
                                     uint32_t max_spins, uint32_t *bad, bool check_only,
                                     int *resident, hipStream_t s);
 
-// One launch of 2 * channels workgroups (producers, then consumers), all of
-// which the caller has checked can be resident at once in the chosen
+// Producer/consumer pairs a channel can have; the counters hold a head and a
+// tail for each of them.
+constexpr int kFifoMaxPairs = 8;
+
+// One launch of 2 * channels * pairs workgroups (producers, then consumers),
+// all of which the caller has checked can be resident at once in the chosen
 // geometry (wide: 1,024 lanes per workgroup, else 512).
 hipError_t launch_fifo_stream(int proto, const float *src, const float *local, float *out,
                               int64_t n, void *fifo, uint64_t *counters, int channels,
                               int64_t step_bytes, int64_t wire_bytes, uint64_t first_step,
                               bool from_state, uint32_t max_spins, uint32_t *errors,
-                              bool wide, hipStream_t s);
+                              bool wide, int pairs, hipStream_t s);
 // Workgroups of the streaming kernel, in the given geometry, that the current
 // device holds at once.
 hipError_t fifo_stream_resident_workgroups(int proto, bool local, bool wide, int *workgroups);

@@ -9,6 +9,7 @@
 
 #include <atomic>
 
+#include "index_map.h"
 #include "launch.h"
 
 #define LIBAR_EXPORT extern "C" __attribute__((visibility("default")))
@@ -741,9 +742,12 @@ LIBAR_EXPORT int64_t ar_fifo_steps_per_channel(int64_t n, int64_t step_bytes, in
     return (total + channels - 1) / channels;
 }
 
+static_assert(ar::kFifoMaxPairs == AR_FIFO_MAX_PAIRS, "pairs per channel");
+
 LIBAR_EXPORT int64_t ar_fifo_counter_words(int channels)
 {
-    return channels < 1 || channels > AR_FIFO_MAX_CHANNELS ? 0 : 2 * (int64_t)channels + 2;
+    return channels < 1 || channels > AR_FIFO_MAX_CHANNELS
+               ? 0 : 2 * (int64_t)channels * AR_FIFO_MAX_PAIRS + 2;
 }
 
 namespace {
@@ -769,6 +773,32 @@ int resident_workgroups(int proto, bool local, bool wide, int *workgroups)
     if (e == hipSuccess && dev >= 0 && dev < kDevices)
         cache[dev][proto][local][wide].store(*workgroups, std::memory_order_relaxed);
     return (int)e;
+}
+
+// Producer/consumer pairs per channel (ar::fifo_pairs_for) for a full step
+// of this protocol's items: LL lines, LL128 16-byte chunks (whole line pairs
+// per slice), Simple 16-byte chunks.  A pair's slice of a full step is at
+// least 512 items, and a channel gets one pair per 2,048 items it carries
+// in the call (at least one): extra pairs only add workgroups when there is
+// little to move (32 channels, LL: an 8 KiB message took 7.5 us with four
+// pairs against 5.1 us with one, a 512 KiB one 8.2 against 6.4 us, while a
+// 16 MiB one took 140 against 195 us).
+int fifo_pairs(int proto, int64_t step_bytes, int64_t n, int channels, int resident)
+{
+    const int64_t items = proto == AR_PROTO_LL      ? step_bytes / 8
+                          : proto == AR_PROTO_LL128 ? step_bytes / 120 * 8
+                                                    : step_bytes / 16;
+    const int64_t steps = ar_fifo_steps_per_channel(n, step_bytes, channels);
+    int64_t bytes = steps * step_bytes;                 // payload of the busiest channel
+    if (bytes > 4 * n)
+        bytes = 4 * n;
+    const int64_t per_item = proto == AR_PROTO_LL ? 8 : proto == AR_PROTO_LL128 ? 15 : 16;
+    int64_t by_work = bytes / per_item / 2048;
+    if (by_work < 1)
+        by_work = 1;
+    const int most = by_work < AR_FIFO_MAX_PAIRS ? (int)by_work : AR_FIFO_MAX_PAIRS;
+    return ar::fifo_pairs_for(items, proto == AR_PROTO_LL128 ? 16 : 1, channels, resident, most,
+                              512);
 }
 
 }  // namespace
@@ -807,21 +837,26 @@ LIBAR_EXPORT ar_status_t ar_fifo_stream(int proto, const float *src, const float
         return AR_ERR_ARG;
     if (n == 0)
         return AR_OK;
-    // the wide geometry when every workgroup fits at once, else the narrow one
-    bool wide = true;
-    for (;;) {
-        int resident = 0;
-        const int he = resident_workgroups(proto, local != nullptr, wide, &resident);
-        if (he != 0)
-            return from_hip((hipError_t)he);
-        if (resident >= 2 * channels)
-            break;
-        if (!wide)
-            return AR_ERR_CAPACITY;
-        wide = false;
-    }
+    // Geometry and pairs: 1,024-lane workgroups with as many pairs as fit,
+    // unless that leaves one pair per channel (or none) where 512-lane ones
+    // fit at least two.  Measured on 16 Mi fp32 at NCCL's steps: at 128
+    // channels two narrow pairs beat one wide pair (LL 86 against 99 us,
+    // LL128 67 against 71 us), at 32 channels four wide pairs beat eight
+    // narrow ones (LL 147 against 154 us).
+    int wide_res = 0, narrow_res = 0;
+    int he = resident_workgroups(proto, local != nullptr, true, &wide_res);
+    if (he == 0)
+        he = resident_workgroups(proto, local != nullptr, false, &narrow_res);
+    if (he != 0)
+        return from_hip((hipError_t)he);
+    const int wide_pairs = fifo_pairs(proto, step_bytes, n, channels, wide_res);
+    const int narrow_pairs = fifo_pairs(proto, step_bytes, n, channels, narrow_res);
+    const bool wide = wide_pairs >= 2 || (wide_pairs == 1 && narrow_pairs < 2);
+    const int pairs = wide ? wide_pairs : narrow_pairs;
+    if (pairs < 1)
+        return AR_ERR_CAPACITY;
     return from_hip(ar::launch_fifo_stream(proto, src, local, out, n, fifo, counters, channels,
                                            step_bytes, wire, first_step,
                                            first_step == AR_FIFO_CONTINUE, max_spins, errors,
-                                           wide, static_cast<hipStream_t>(stream)));
+                                           wide, pairs, static_cast<hipStream_t>(stream)));
 }

@@ -1,6 +1,6 @@
 // Streaming a payload through 8-step FIFOs on one device: producer and
-// consumer workgroups run concurrently in one launch, one pair per channel,
-// each channel with its own 8-slot ring.
+// consumer workgroups run concurrently in one launch, each channel with its
+// own 8-slot ring and one or more producer/consumer pairs.
 //
 // Source (web page; cited by tag and section):
 //   [NCCL14] "NCCL 专家课程 14：Simple、LL、LL128 的线格式、同步与真实性能边界"
@@ -29,6 +29,17 @@
 // will consume) after each step, and the producer reuses slot k mod 8 only
 // once head >= k - 7.
 //
+// Pairs per channel.  A channel's steps may be shared by P producer/consumer
+// workgroup pairs: pair g owns the same contiguous slice of every step
+// (items [g * span, (g + 1) * span), span a whole number of LL128 line pairs),
+// in the same 8-slot ring, with its own head and tail counters.  Producer g
+// writes only its slice of a slot and consumer g reads only that slice, so a
+// pair is a complete FIFO of its own and the pairs of a channel need no
+// common counter.  More pairs keep more CUs busy when there are few channels,
+// and shorten each pair's part of a step when a channel carries only one.
+// The host picks P so that every full step gives every pair a slice; only a
+// channel's last step, if partial, can leave a pair without one.
+//
 // Memory-level parallelism: every lane issues a batch of loads (source words,
 // ring chunks, local addends) before it checks or stores any of them, items
 // not yet ready are re-polled together, and the consumer releases a slot
@@ -56,6 +67,7 @@
 // failed (errors[0] != 0), so the launch always drains; its outputs are then
 // unspecified.
 #include "device.h"
+#include "index_map.h"
 #include "launch.h"
 
 namespace ar {
@@ -70,6 +82,7 @@ constexpr int kNarrowThreads = 512;
 template <int T>
 constexpr int kBatchOf = (int)(kPerBatch / T);   // items in flight per lane
 constexpr uint32_t kAbortCheck = 16;   // spins between looks at the error count
+constexpr int kMaxPairs = kFifoMaxPairs;      // producer/consumer pairs per channel
 
 struct StreamArgs {
     const uint32_t *src;    // n fp32 payload values (as words)
@@ -77,8 +90,8 @@ struct StreamArgs {
     float *out;             // n fp32
     int64_t n;
     uint8_t *fifo;          // channels x 8 slots x wire bytes
-    uint64_t *head;         // per channel: next ring step the consumer needs
-    uint64_t *tail;         // per channel (Simple): ring steps published
+    uint64_t *head;         // per pair: next ring step its consumer needs
+    uint64_t *tail;         // per pair (Simple): ring steps published
     uint64_t *state;        // {next first step, finished consumers}
     uint32_t *errors;       // [0]: failed waits
     int64_t step_bytes;     // payload bytes per step
@@ -86,6 +99,8 @@ struct StreamArgs {
     int64_t total_steps;    // T = ceil(4n / step_bytes)
     int64_t steps_per_channel;
     int channels;
+    int pairs;              // producer/consumer pairs per channel
+    int64_t span;           // items of a full step per pair (fifo_span)
     int from_state;         // the first step comes from state[0]
     uint64_t first_step;
     uint32_t max_spins;
@@ -285,13 +300,31 @@ struct Step {
     Rsrc slot;        // the step's ring slot
     int64_t w0;       // first payload word
     int64_t words;    // payload words
+    int64_t lo;       // the pair's slice of the step's items: [lo, items)
     int64_t items;
     uint64_t k;       // ring step
 };
 
+// Items of a step of `len` payload bytes (`words` words).
+template <int PROTO>
+__device__ __forceinline__ int64_t items_of(int64_t len, int64_t words)
+{
+    return PROTO == 0 ? (len + 7) / 8 : PROTO == 1 ? (len + 119) / 120 * 8 : (words + 3) / 4;
+}
+
+// The slice of pair `pair` in a step of `total` items (fifo_slice: the same
+// region of every ring slot, cut from a full step, so a partial last step
+// keeps the regions of the full steps that used its slot before).  The span
+// comes from the host, which computed it with fifo_span.
+__device__ __forceinline__ void slice_of(const StreamArgs &a, int64_t total, int pair,
+                                         int64_t *lo, int64_t *hi)
+{
+    fifo_slice_at(a.span, total, pair, lo, hi);
+}
+
 template <int PROTO>
 __device__ __forceinline__ Step step_at(const StreamArgs &a, uint8_t *ring, int64_t s0,
-                                        uint64_t first, int64_t j)
+                                        uint64_t first, int64_t j, int pair)
 {
     Step g;
     g.k = first + (uint64_t)j;
@@ -301,7 +334,7 @@ __device__ __forceinline__ Step step_at(const StreamArgs &a, uint8_t *ring, int6
     const int64_t len = left < a.step_bytes ? left : a.step_bytes;
     g.w0 = b0 / 4;
     g.words = len / 4;
-    g.items = PROTO == 0 ? (len + 7) / 8 : PROTO == 1 ? (len + 119) / 120 * 8 : (g.words + 3) / 4;
+    slice_of(a, items_of<PROTO>(len, g.words), pair, &g.lo, &g.items);
     return g;
 }
 
@@ -311,20 +344,38 @@ struct Cursor {
     Step g;
 };
 
-// The batch after cur; false past the channel's last step.
+// The pair's first batch; false when it has nothing to move (its slice of
+// the channel's only step is empty).
+template <int PROTO>
+__device__ __forceinline__ bool start(const StreamArgs &a, uint8_t *ring, int64_t s0,
+                                      uint64_t first, int64_t steps, int pair, Cursor *cur)
+{
+    if (steps <= 0)
+        return false;
+    cur->j = 0;
+    cur->g = step_at<PROTO>(a, ring, s0, first, 0, pair);
+    cur->base = cur->g.lo;
+    return cur->g.lo < cur->g.items;
+}
+
+// The batch after cur; false past the pair's last batch (an empty slice can
+// only be that of the channel's last step).
 template <int PROTO>
 __device__ __forceinline__ bool advance(const StreamArgs &a, uint8_t *ring, int64_t s0,
-                                        uint64_t first, int64_t steps, const Cursor &cur,
-                                        Cursor *nxt)
+                                        uint64_t first, int64_t steps, int pair,
+                                        const Cursor &cur, Cursor *nxt)
 {
     nxt->j = cur.j;
     nxt->base = cur.base + kPerBatch;
     nxt->g = cur.g;
     if (nxt->base >= cur.g.items) {
         nxt->j = cur.j + 1;
-        nxt->base = 0;
-        if (nxt->j < steps)
-            nxt->g = step_at<PROTO>(a, ring, s0, first, nxt->j);
+        if (nxt->j < steps) {
+            nxt->g = step_at<PROTO>(a, ring, s0, first, nxt->j, pair);
+            nxt->base = nxt->g.lo;
+            if (nxt->g.lo >= nxt->g.items)
+                nxt->j = steps;
+        }
     }
     return nxt->j < steps;
 }
@@ -511,25 +562,26 @@ __device__ __forceinline__ void loads_returned(const u32x4 v[kBatchOf<T>])
 // ---------------------------------------------------------------------------
 // Producer: the batches of the channel's steps in order, each batch's source
 // loads issued before the previous batch's ring stores.
+// Pair `pair` of channel c; its counters are head[p] and tail[p].
 template <int T, int PROTO>
-__device__ void produce(const StreamArgs &a, int c, int64_t s0, int64_t steps, uint64_t first,
-                        Shared *sh)
+__device__ void produce(const StreamArgs &a, int c, int pair, int p, int64_t s0, int64_t steps,
+                        uint64_t first, Shared *sh)
 {
-    if (steps <= 0)
-        return;
     uint8_t *ring = a.fifo + (int64_t)c * 8 * a.wire_bytes;
     uint64_t head_seen = first;      // the consumer has taken every step before `first`
-    Cursor cur{0, 0, step_at<PROTO>(a, ring, s0, first, 0)};
+    Cursor cur;
+    if (!start<PROTO>(a, ring, s0, first, steps, pair, &cur))
+        return;
     u32x4 d[kBatchOf<T>];
-    load_src<T, PROTO>(a, cur.g, 0, d);
+    load_src<T, PROTO>(a, cur.g, cur.base, d);
     for (;;) {
         Cursor nxt;
-        const bool more = advance<PROTO>(a, ring, s0, first, steps, cur, &nxt);
+        const bool more = advance<PROTO>(a, ring, s0, first, steps, pair, cur, &nxt);
         u32x4 nd[kBatchOf<T>];
         if (more)
             load_src<T, PROTO>(a, nxt.g, nxt.base, nd);
-        if (cur.base == 0 && cur.j >= 8 &&
-            !wait_counter(a, sh, a.head + c, cur.g.k - 7, &head_seen))
+        if (cur.base == cur.g.lo && cur.j >= 8 &&
+            !wait_counter(a, sh, a.head + p, cur.g.k - 7, &head_seen))
             return;
         store_ring<T, PROTO>(cur.g, cur.base, d);
         if (PROTO == 1) {
@@ -548,7 +600,7 @@ __device__ void produce(const StreamArgs &a, int c, int64_t s0, int64_t steps, u
             drain_memory();
             __syncthreads();
             if (threadIdx.x == 0)
-                store_counter(a.tail + c, cur.g.k + 1);
+                store_counter(a.tail + p, cur.g.k + 1);
         }
         if (!more)
             return;
@@ -564,11 +616,11 @@ __device__ void produce(const StreamArgs &a, int c, int64_t s0, int64_t steps, u
 // returned: the workgroup agrees on success and lane 0 publishes head = k + 1,
 // before the step's last batch is delivered from registers.  A failed wait
 // is counted where it happens.  Returns false once the launch must stop.
-__device__ bool close_step(const StreamArgs &a, int c, uint64_t k, bool failed)
+__device__ bool close_step(const StreamArgs &a, int p, uint64_t k, bool failed)
 {
     const bool any_failed = __syncthreads_or(failed ? 1 : 0) != 0;
     if (threadIdx.x == 0 && !any_failed)
-        store_counter(a.head + c, k + 1);
+        store_counter(a.head + p, k + 1);
     return !any_failed;
 }
 
@@ -615,15 +667,16 @@ __device__ bool poll_batch(const StreamArgs &a, u32x4 v[kBatchOf<T>], bool ok[kB
 // is loaded before this batch is delivered; lines not yet written are
 // re-polled.
 template <int T, bool LOCAL>
-__device__ void consume_ll(const StreamArgs &a, int c, int64_t s0, int64_t steps, uint64_t first)
+__device__ void consume_ll(const StreamArgs &a, int c, int pair, int p, int64_t s0, int64_t steps,
+                           uint64_t first)
 {
-    if (steps <= 0)
-        return;
     uint8_t *ring = a.fifo + (int64_t)c * 8 * a.wire_bytes;
-    Cursor cur{0, 0, step_at<0>(a, ring, s0, first, 0)};
+    Cursor cur;
+    if (!start<0>(a, ring, s0, first, steps, pair, &cur))
+        return;
     u32x4 v[kBatchOf<T>], lv[kBatchOf<T>];
-    load_ring<T, 0>(cur.g, 0, v);
-    load_local<T, 0, LOCAL>(a, cur.g, 0, lv);
+    load_ring<T, 0>(cur.g, cur.base, v);
+    load_local<T, 0, LOCAL>(a, cur.g, cur.base, lv);
     bool failed = false;
     for (;;) {
         const uint32_t flag = (uint32_t)(cur.g.k + 1);
@@ -642,9 +695,9 @@ __device__ void consume_ll(const StreamArgs &a, int c, int64_t s0, int64_t steps
                 [&](int u) { return (uint32_t)(16 * (i0 + (int64_t)u * T)); },
                 valid);
         Cursor nxt;
-        const bool more = advance<0>(a, ring, s0, first, steps, cur, &nxt);
+        const bool more = advance<0>(a, ring, s0, first, steps, pair, cur, &nxt);
         loads_returned<T>(v);
-        if (nxt.j != cur.j && !close_step(a, c, cur.g.k, failed))
+        if (nxt.j != cur.j && !close_step(a, p, cur.g.k, failed))
             return;
         // With the producer ahead, the next batch is loaded before this one
         // is delivered; a lane that had to wait delivers first, so that its
@@ -700,24 +753,24 @@ __device__ __forceinline__ uint64_t read_flag64(Rsrc slot, uint32_t off)
 // re-read.  Lane 0 reads the next batch's first flag together with this
 // batch's data, and the next batch is loaded before this one is delivered.
 template <int T, bool LOCAL>
-__device__ void consume_ll128(const StreamArgs &a, int c, int64_t s0, int64_t steps,
-                              uint64_t first, Shared *sh)
+__device__ void consume_ll128(const StreamArgs &a, int c, int pair, int p, int64_t s0,
+                              int64_t steps, uint64_t first, Shared *sh)
 {
-    if (steps <= 0)
-        return;
     uint8_t *ring = a.fifo + (int64_t)c * 8 * a.wire_bytes;
     auto flag_at = [](int64_t base) { return (uint32_t)(128 * (base >> 3) + 120); };
-    Cursor cur{0, 0, step_at<1>(a, ring, s0, first, 0)};
-    uint64_t pre = threadIdx.x == 0 ? read_flag64(cur.g.slot, flag_at(0)) : 0;
-    if (!wait_flag64(a, sh, cur.g.slot, flag_at(0), cur.g.k + 1, pre))
+    Cursor cur;
+    if (!start<1>(a, ring, s0, first, steps, pair, &cur))
+        return;
+    uint64_t pre = threadIdx.x == 0 ? read_flag64(cur.g.slot, flag_at(cur.base)) : 0;
+    if (!wait_flag64(a, sh, cur.g.slot, flag_at(cur.base), cur.g.k + 1, pre))
         return;
     u32x4 v[kBatchOf<T>], lv[kBatchOf<T>];
-    load_ring<T, 1>(cur.g, 0, v);
-    load_local<T, 1, LOCAL>(a, cur.g, 0, lv);
+    load_ring<T, 1>(cur.g, cur.base, v);
+    load_local<T, 1, LOCAL>(a, cur.g, cur.base, lv);
     bool failed = false;
     for (;;) {
         Cursor nxt;
-        const bool more = advance<1>(a, ring, s0, first, steps, cur, &nxt);
+        const bool more = advance<1>(a, ring, s0, first, steps, pair, cur, &nxt);
         if (threadIdx.x == 0 && more)
             pre = read_flag64(nxt.g.slot, flag_at(nxt.base));
         const uint64_t flag = cur.g.k + 1;
@@ -740,7 +793,7 @@ __device__ void consume_ll128(const StreamArgs &a, int c, int64_t s0, int64_t st
                 },
                 valid);
         loads_returned<T>(v);
-        if (nxt.j != cur.j && !close_step(a, c, cur.g.k, failed))
+        if (nxt.j != cur.j && !close_step(a, p, cur.g.k, failed))
             return;
         if (more && !wait_flag64(a, sh, nxt.g.slot, flag_at(nxt.base), nxt.g.k + 1, pre))
             return;
@@ -766,27 +819,27 @@ __device__ void consume_ll128(const StreamArgs &a, int c, int64_t s0, int64_t st
 // step boundary when the tail already covers the next step) the next batch
 // is loaded before this one is delivered.
 template <int T, bool LOCAL>
-__device__ void consume_simple(const StreamArgs &a, int c, int64_t s0, int64_t steps,
-                               uint64_t first, Shared *sh)
+__device__ void consume_simple(const StreamArgs &a, int c, int pair, int p, int64_t s0,
+                               int64_t steps, uint64_t first, Shared *sh)
 {
-    if (steps <= 0)
-        return;
     uint8_t *ring = a.fifo + (int64_t)c * 8 * a.wire_bytes;
     uint64_t tail_seen = first;      // the producer has written every step before `first`
-    Cursor cur{0, 0, step_at<2>(a, ring, s0, first, 0)};
-    if (!wait_counter(a, sh, a.tail + c, cur.g.k + 1, &tail_seen))
+    Cursor cur;
+    if (!start<2>(a, ring, s0, first, steps, pair, &cur))
+        return;
+    if (!wait_counter(a, sh, a.tail + p, cur.g.k + 1, &tail_seen))
         return;
     u32x4 v[kBatchOf<T>], lv[kBatchOf<T>];
-    load_ring<T, 2>(cur.g, 0, v);
-    load_local<T, 2, LOCAL>(a, cur.g, 0, lv);
+    load_ring<T, 2>(cur.g, cur.base, v);
+    load_local<T, 2, LOCAL>(a, cur.g, cur.base, lv);
     for (;;) {
         Cursor nxt;
-        const bool more = advance<2>(a, ring, s0, first, steps, cur, &nxt);
+        const bool more = advance<2>(a, ring, s0, first, steps, pair, cur, &nxt);
         loads_returned<T>(v);
-        if (nxt.j != cur.j && !close_step(a, c, cur.g.k, false))
+        if (nxt.j != cur.j && !close_step(a, p, cur.g.k, false))
             return;
         if (more && nxt.j != cur.j &&
-            !wait_counter(a, sh, a.tail + c, nxt.g.k + 1, &tail_seen))
+            !wait_counter(a, sh, a.tail + p, nxt.g.k + 1, &tail_seen))
             return;
         u32x4 nv[kBatchOf<T>], nlv[kBatchOf<T>];
         if (more) {
@@ -805,7 +858,8 @@ __device__ void consume_simple(const StreamArgs &a, int c, int64_t s0, int64_t s
     }
 }
 
-// Blocks [0, channels) produce, [channels, 2 * channels) consume.  Without
+// Blocks [0, channels * pairs) produce, the next channels * pairs consume;
+// block q of either half is pair q mod pairs of channel q / pairs.  Without
 // a local addend the kernel keeps to 128 VGPRs (4 wavefronts per SIMD), so
 // two workgroups fit on a CU and up to 256 channels can run at once; with one
 // it has two wavefronts per SIMD.
@@ -814,8 +868,10 @@ __global__ __launch_bounds__(T, T == kWideThreads || !LOCAL ? 4 : 2) void stream
 {
     __shared__ Shared sh;
     const int b = blockIdx.x;
-    const bool producer = b < a.channels;
-    const int c = producer ? b : b - a.channels;
+    const int pairs_total = a.channels * a.pairs;
+    const bool producer = b < pairs_total;
+    const int p = producer ? b : b - pairs_total;
+    const int c = p / a.pairs, pair = p % a.pairs;
     // Every block reads the stored first step before its channel moves, and
     // the last consumer advances it only after every step of every channel
     // has been written and read; a channel with no steps may read either
@@ -830,20 +886,20 @@ __global__ __launch_bounds__(T, T == kWideThreads || !LOCAL ? 4 : 2) void stream
     const int64_t s0 = (int64_t)c * a.total_steps / a.channels;
     const int64_t s1 = (int64_t)(c + 1) * a.total_steps / a.channels;
     if (producer) {
-        produce<T, PROTO>(a, c, s0, s1 - s0, first, &sh);
+        produce<T, PROTO>(a, c, pair, p, s0, s1 - s0, first, &sh);
         return;
     }
     if (PROTO == 0)
-        consume_ll<T, LOCAL>(a, c, s0, s1 - s0, first);
+        consume_ll<T, LOCAL>(a, c, pair, p, s0, s1 - s0, first);
     else if (PROTO == 1)
-        consume_ll128<T, LOCAL>(a, c, s0, s1 - s0, first, &sh);
+        consume_ll128<T, LOCAL>(a, c, pair, p, s0, s1 - s0, first, &sh);
     else
-        consume_simple<T, LOCAL>(a, c, s0, s1 - s0, first, &sh);
+        consume_simple<T, LOCAL>(a, c, pair, p, s0, s1 - s0, first, &sh);
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint64_t done = __hip_atomic_fetch_add(a.state + 1, (uint64_t)1, __ATOMIC_ACQ_REL,
                                                      __HIP_MEMORY_SCOPE_AGENT);
-        if (done == (uint64_t)a.channels - 1) {
+        if (done == (uint64_t)pairs_total - 1) {
             __hip_atomic_store(a.state + 1, (uint64_t)0, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(a.state, first + (uint64_t)a.steps_per_channel, __ATOMIC_RELEASE,
@@ -886,7 +942,7 @@ hipError_t launch_fifo_stream(int proto, const float *src, const float *local, f
                               int64_t n, void *fifo, uint64_t *counters, int channels,
                               int64_t step_bytes, int64_t wire_bytes, uint64_t first_step,
                               bool from_state, uint32_t max_spins, uint32_t *errors,
-                              bool wide, hipStream_t s)
+                              bool wide, int pairs, hipStream_t s)
 {
     StreamArgs a;
     a.src = reinterpret_cast<const uint32_t *>(src);
@@ -895,19 +951,25 @@ hipError_t launch_fifo_stream(int proto, const float *src, const float *local, f
     a.n = n;
     a.fifo = static_cast<uint8_t *>(fifo);
     a.head = counters;
-    a.tail = counters + channels;
-    a.state = counters + 2 * channels;
+    a.tail = counters + (int64_t)channels * kMaxPairs;
+    a.state = counters + 2 * (int64_t)channels * kMaxPairs;
     a.errors = errors;
     a.step_bytes = step_bytes;
     a.wire_bytes = wire_bytes;
     a.total_steps = (4 * n + step_bytes - 1) / step_bytes;
     a.steps_per_channel = (a.total_steps + channels - 1) / channels;
     a.channels = channels;
+    a.pairs = pairs;
+    {
+        const int64_t full = proto == 0 ? step_bytes / 8 : proto == 1 ? step_bytes / 120 * 8
+                                                                     : step_bytes / 16;
+        a.span = fifo_span(full, proto == 1 ? 16 : 1, pairs);
+    }
     a.from_state = from_state ? 1 : 0;
     a.first_step = first_step;
     a.max_spins = max_spins;
     void *args[] = {&a};
-    return hipLaunchKernel(stream_fn(proto, local != nullptr, wide), dim3(2 * channels),
+    return hipLaunchKernel(stream_fn(proto, local != nullptr, wide), dim3(2 * channels * pairs),
                            dim3(wide ? kWideThreads : kNarrowThreads), args, 0, s);
 }
 

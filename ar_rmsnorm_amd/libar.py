@@ -53,6 +53,7 @@ EXPORTS = (
 )
 AR_PROTO_LL, AR_PROTO_LL128, AR_PROTO_SIMPLE = 0, 1, 2
 AR_FIFO_MAX_CHANNELS = 256
+AR_FIFO_MAX_PAIRS = 8
 AR_FIFO_CONTINUE = (1 << 64) - 1
 
 _vp, _i64, _u64, _u32, _int = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,

@@ -428,9 +428,14 @@ ar_status_t ll128_unpack_reduce(const void *const *fifos, int W, float *out,
  * into steps of step_bytes payload bytes; the T = ceil(4n / step_bytes)
  * steps are dealt to `channels` channels in contiguous runs (channel c takes
  * steps [c*T/channels, (c+1)*T/channels)).  Each channel has an 8-slot ring
- * and a producer and a consumer workgroup that run concurrently in one
- * launch.  Local step j of a channel is ring step k = first + j, in slot
- * k mod 8:
+ * and one or more producer/consumer workgroup pairs that run concurrently in
+ * one launch; with P pairs, pair g owns the same contiguous slice of every
+ * step (items [g*span, (g+1)*span), whole LL128 line pairs) and keeps its own
+ * head and tail.  The library picks P: as many pairs as the device holds at
+ * once, up to AR_FIFO_MAX_PAIRS, at most one per 2,048 items a channel
+ * carries in the call, and no more than leave every pair a slice of at
+ * least 512 items of a full step.  Local step j of a channel is ring step
+ * k = first + j, in slot k mod 8:
  *   AR_PROTO_LL      16-byte lines of 8 payload bytes + two 32-bit flags
  *                    (k + 1), ready when both flags match
  *   AR_PROTO_LL128   128-byte lines of 120 payload bytes + a 64-bit flag
@@ -440,8 +445,8 @@ ar_status_t ll128_unpack_reduce(const void *const *fifos, int W, float *out,
  *                    first flag, then reads every line and checks its flag
  *   AR_PROTO_SIMPLE  raw payload; ready when the channel's tail counter
  *                    reaches k + 1
- * After each step the consumer sets the channel's head counter to k + 1; the
- * producer reuses slot k mod 8 only once head >= k - 7.  A step writes only
+ * After each step a pair's consumer sets the pair's head counter to k + 1;
+ * its producer reuses its slice of slot k mod 8 only once head >= k - 7.  A step writes only
  * the lines (or bytes) that carry payload.  The consumer delivers
  * out[e] = src[e], or local[e] + src[e] in fp32 when local is given.
  *   proto       AR_PROTO_LL / AR_PROTO_LL128 / AR_PROTO_SIMPLE
@@ -450,9 +455,9 @@ ar_status_t ll128_unpack_reduce(const void *const *fifos, int W, float *out,
  *   fifo        channels * 8 * ar_fifo_step_wire_bytes(proto, step_bytes)
  *               bytes, 16-byte aligned (128 for LL128)
  *   counters    ar_fifo_counter_words(channels) u64, 8-byte aligned: the
- *               heads, the tails, then {stored first step, finished
- *               consumers}.  Zero fifo and counters together before the
- *               first call on them.
+ *               heads (channels * AR_FIFO_MAX_PAIRS), the tails (as many),
+ *               then {stored first step, finished consumers}.  Zero fifo
+ *               and counters together before the first call on them.
  *   channels    1..AR_FIFO_MAX_CHANNELS
  *   first_step  the first ring step of every channel, or AR_FIFO_CONTINUE
  *               for the stored first step.  Each call ends by storing
@@ -467,10 +472,11 @@ ar_status_t ll128_unpack_reduce(const void *const *fifos, int W, float *out,
  *               is unspecified and fifo/counters must be zeroed before reuse
  *   src, local, out  n fp32, 4-byte aligned; out may equal local, no other
  *               overlap among the buffers                 else AR_ERR_ARG
- * The 2 * channels workgroups must be resident together.  They have 1,024
- * lanes when the device holds 2 * channels such workgroups at once, else
- * 512 lanes; AR_ERR_CAPACITY if it cannot hold them in either form (with
- * local, more than 128 channels on MI355X).  Work from other streams that holds
+ * The 2 * channels * P workgroups must be resident together.  They have
+ * 1,024 lanes, or 512 when the device holds two or more pairs per channel
+ * of those but only one of the wider ones; AR_ERR_CAPACITY if it cannot hold
+ * one pair per channel in either form (with local, more than 128 channels
+ * on MI355X).  Work from other streams that holds
  * compute units while a call runs can delay a consumer or producer; the
  * bounded waits then end the launch with errors[0] != 0.
  */
@@ -478,6 +484,7 @@ ar_status_t ll128_unpack_reduce(const void *const *fifos, int W, float *out,
 #define AR_PROTO_LL128 1
 #define AR_PROTO_SIMPLE 2
 #define AR_FIFO_MAX_CHANNELS 256
+#define AR_FIFO_MAX_PAIRS 8           /* producer/consumer pairs per channel */
 #define AR_FIFO_CONTINUE UINT64_MAX
 
 ar_status_t ar_fifo_stream(int proto, const float *src, const float *local,
@@ -486,8 +493,8 @@ ar_status_t ar_fifo_stream(int proto, const float *src, const float *local,
                            uint32_t max_spins, uint32_t *errors,
                            ar_stream_t stream);
 
-/* u64 words of the counters of `channels` channels: 2 * channels + 2
- * (0 if channels is out of range). */
+/* u64 words of the counters of `channels` channels:
+ * 2 * channels * AR_FIFO_MAX_PAIRS + 2 (0 if channels is out of range). */
 int64_t ar_fifo_counter_words(int channels);
 
 /* Ring bytes per step for a protocol (0 if step_bytes is not valid). */

@@ -177,7 +177,8 @@ def test_stream_geometry_helpers():
     assert ar.ar_fifo_steps_per_channel(16_777_229, 32768, 32) == 65
     assert ar.ar_fifo_steps_per_channel(2048, 32768, 32) == 1
     assert ar.ar_fifo_steps_per_channel(0, 32768, 4) == 0
-    assert [ar.ar_fifo_counter_words(c) for c in (0, 1, 256, 257)] == [0, 4, 514, 0]
+    # a head and a tail per pair (up to 8 pairs per channel), then two state words
+    assert [ar.ar_fifo_counter_words(c) for c in (0, 1, 256, 257)] == [0, 18, 4098, 0]
     assert ar.AR_FIFO_CONTINUE == (1 << 64) - 1
 
 
@@ -197,9 +198,10 @@ def test_stream_argument_errors():
     assert st(f, LL, A, A + 16, C, D, 2, 1024, 0, 8, E, None, 8, 0) == ar.AR_ERR_ARG
     assert st(f, LL, A, B, C, D, 2, 1024, 0, 8, E, B + 4, 8, 0) == ar.AR_ERR_ARG   # local partial
     assert st(f, LL, A, B, C, C + 64, 2, 1024, 0, 8, E, None, 8, 0) == ar.AR_ERR_ARG  # counters
-    # the two state words follow the 2 * channels heads and tails
-    assert st(f, LL, A, B, C, D, 2, 1024, 0, 8, D + 40, None, 8, 0) == ar.AR_ERR_ARG
-    assert st(f, LL, A, B, C, D, 2, 1024, 0, 8, D + 48, None, 0, 0) == ar.AR_OK
+    # the two state words follow the 2 * channels * 8 heads and tails
+    words = 2 * 2 * ar.AR_FIFO_MAX_PAIRS + 2
+    assert st(f, LL, A, B, C, D, 2, 1024, 0, 8, D + 8 * words - 8, None, 8, 0) == ar.AR_ERR_ARG
+    assert st(f, LL, A, B, C, D, 2, 1024, 0, 8, D + 8 * words, None, 0, 0) == ar.AR_OK
     assert st(f, LL, A, B, C, D, 2, 1024, 0, 8, E, None, 0, 0) == ar.AR_OK       # n = 0
 
 

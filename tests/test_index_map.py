@@ -74,3 +74,18 @@ def test_the_checker_catches_a_planted_out_of_range_map(checker, tmp_path):
                     str(tests_dir / "index_map_check.cpp")], check=True)
     r = subprocess.run([exe, "256", "8", str(8 * 100 + 5)], capture_output=True, text=True)
     assert r.returncode == 1 and "FAIL" in r.stdout
+
+
+def test_streaming_slices_cover_every_step(tmp_path):
+    """tests/fifo_slice_check.cpp compiles the slice functions the streaming
+    kernel and the host's pair choice use, and checks that the pairs of a
+    channel cut every step (full, or a shorter last step) into disjoint,
+    aligned pieces that cover it, each pair staying in its region of the
+    ring slot, and that the chosen pair count fits the device."""
+    if shutil.which("g++") is None:
+        pytest.skip("g++ not available")
+    exe = str(tmp_path / "fifo_slice_check")
+    subprocess.run(["g++", "-std=c++17", "-O2", "-Wall", "-o", exe,
+                    os.path.join(HERE, "fifo_slice_check.cpp")], check=True)
+    out = run(exe)
+    assert out.endswith("0 failures\n"), out

@@ -51,7 +51,7 @@ class Fifo:
         assert np.array_equal(got[:n].view(np.uint32), want.view(np.uint32)), "payload"
         assert np.array_equal(self.fifo.cpu().numpy(), self.host), "ring bytes"
         self.first += ar.ar_fifo_steps_per_channel(n, self.step, self.channels)
-        state = self.counters.cpu().numpy()[2 * self.channels:]
+        state = self.counters.cpu().numpy()[-2:]
         assert state[0] == self.first and state[1] == 0, "stored step"
 
     def run(self, src, local=None, cont=False, max_spins=ar.AR_MAX_SPINS):
