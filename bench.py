@@ -28,7 +28,8 @@ all-core aggregate is `value`, the single-thread rate `single_core`.
 Context row: the launch floor (a one-pack reduce).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                       [--rows all|none|stream|wire] [--eager] [--calib-copy] [--warm]
+                       [--rows all|none|stream|wire|sets] [--eager] [--calib-copy] [--warm]
+                       [--trace-summary DIR]
 """
 from __future__ import annotations
 
@@ -65,9 +66,9 @@ def parse():
                    help="headline steps timed; a step is one call on each rotated buffer set")
     p.add_argument("--warmup", type=int, default=2, help="untimed headline steps first")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--rows", choices=["all", "none", "stream", "wire"], default="all",
-                   help="which rows besides the headline: all, none, or only the streaming "
-                        "or the wire-format rows")
+    p.add_argument("--rows", choices=["all", "none", "stream", "wire", "sets"], default="all",
+                   help="which rows besides the headline: all, none, or only the streaming, "
+                        "the wire-format or the rotated-set rows")
     p.add_argument("--eager", action="store_true",
                    help="time eager launches instead of a HIP graph replay")
     p.add_argument("--calib-copy", action="store_true",
@@ -296,10 +297,10 @@ def main():
         del g
         return ms, each
 
-    def rank_buffers(count, nbytes, dtype, fill=None):
-        """`count` buffers of `nbytes` each, RANK_GAP bytes apart in one
+    def rank_buffers(count, nbytes, dtype, fill=None, gap=RANK_GAP):
+        """`count` buffers of `nbytes` each, `gap` bytes apart in one
         allocation (fill[i] copied into buffer i when given)."""
-        stride = -(-nbytes // 256) * 256 + RANK_GAP
+        stride = -(-nbytes // 256) * 256 + gap
         arena = torch.empty(count * stride + 4096, dtype=torch.uint8, device=dev)
         start = (-arena.data_ptr()) % 4096
         bufs = [arena[start + i * stride: start + i * stride + nbytes].view(dtype)
@@ -750,6 +751,17 @@ def main():
         row("1stage_W8_n4194304_separate_allocations", nb,
             [lambda s=s: ar.ar_reduce_1stage(s[0], s[1]) for s in s1], steps=8 * k1)
         del s1
+        # the rank-buffer gap: with 0 or 32 KiB between the 8 MiB buffers the
+        # W streams read at the same offset start on the same HBM channels
+        for gap in (0, 32768, 2048, RANK_GAP):
+            s1 = []
+            for k in range(k1):
+                s1.append((rank_buffers(W, 2 * n, torch.int16, base, gap=gap),
+                           torch.empty(n, dtype=torch.int16, device=dev)))
+            row(f"1stage_W8_n4194304_gap{gap}", nb,
+                [lambda s=s: ar.ar_reduce_1stage(s[0], s[1]) for s in s1], steps=8 * k1,
+                extra={"layout": f"rank buffers {gap} B apart in one allocation"})
+            del s1
 
         # the same per-rank two-stage call over message sizes of 1 to 32 MiB per
         # rank buffer (cold sets): a straight-line fit of us per launch against
@@ -801,6 +813,28 @@ def main():
                 extra={"note": "ar_copy of %d MiB into %d MiB, cold sets" % (half_mib, half_mib)})
             del cs
             torch.cuda.empty_cache()
+
+    if args.rows in ("all", "sets"):
+        # what the rotated buffer sets measure: the headline call over 1 to 40
+        # sets (one rotation touches 24 MiB per set; the Infinity Cache holds
+        # 256 MB), each set with its own 8 input and 8 staging buffers
+        sweep = {}
+        for count in (1, 2, 3, 4, 6, 12, 23, 40):
+            sw = []
+            for k in range(count):
+                ins = rank_buffers(W, 2 * n, torch.int16, base)
+                tmps = rank_buffers(W, (part + rem) * 16, torch.int16)
+                for r in range(1, W):
+                    ar.ar_reduce_2stage(ins, tmps, r, None, flags=ar.AR_STAGE_RS)
+                sw.append((ins, tmps, torch.empty(n, dtype=torch.int16, device=dev)))
+            k = -(-230 // count) * count
+            t = graph_time([lambda q=q: ar.ar_reduce_2stage(q[0], q[1], 0, q[2]) for q in sw],
+                           k, args.warmup)
+            sweep[str(count)] = round(t * 1e3, 3)
+            log(f"headline over {count} rotated sets: {t * 1e3:.3f} us")
+            del sw
+            torch.cuda.empty_cache()
+        rows["2stage_W8_n4194304_rotated_sets_us_per_launch"] = sweep
 
     if args.rows in ("all", "wire"):
         # wire formats: W=4 fp32 payloads of 16 Mi values (and the +13 tail);
