@@ -625,9 +625,12 @@ __device__ bool close_step(const StreamArgs &a, int p, uint64_t k, bool failed)
 }
 
 // Wait until every item of a batch is valid (bounded; gives up early once
-// any wait of the launch has failed).  While items are missing, only the
-// earliest of them is polled, since the producer stores a lane's items in
-// that order; once it is valid the missing items are all read again.
+// any wait of the launch has failed).  While items are missing, one lane of
+// the wavefront (the first still waiting) polls the earliest of its missing
+// items, since the producer stores a lane's items in that order and the
+// producer's lanes write together; a miss backs off briefly.  Once that item
+// is valid, every waiting lane reads its missing items again.  One poll per
+// wavefront instead of one per lane keeps the polls from adding traffic.
 template <int T, typename Offset, typename Valid>
 __device__ bool poll_batch(const StreamArgs &a, u32x4 v[kBatchOf<T>], bool ok[kBatchOf<T>], Rsrc slot,
                            Offset off, Valid valid)
@@ -645,8 +648,14 @@ __device__ bool poll_batch(const StreamArgs &a, u32x4 v[kBatchOf<T>], bool ok[kB
         for (int u = kBatchOf<T> - 1; u >= 0; --u)
             if (!ok[u])
                 lead = u;
-        if (!valid(load16_sys(slot, off(lead))))
+        const int first = __builtin_amdgcn_readfirstlane((int)threadIdx.x);
+        int hit = 0;
+        if ((int)threadIdx.x == first)
+            hit = valid(load16_sys(slot, off(lead))) ? 1 : 0;
+        if (!__builtin_amdgcn_readfirstlane(hit)) {
+            __builtin_amdgcn_s_sleep(1);
             continue;
+        }
 #pragma unroll
         for (int u = 0; u < kBatchOf<T>; ++u)
             if (!ok[u])

@@ -77,6 +77,10 @@ def parse():
                    help="no GPU work: summarize the rocprofv3 kernel trace (kernel_trace.csv) "
                         "under DIR per kernel and launch shape, and the back-to-back spacing "
                         "of the headline kernel's dispatches")
+    p.add_argument("--counter-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="no GPU work: HBM bytes per dispatch from two rocprofv3 --pmc runs "
+                        "(FETCH_SIZE, then WRITE_SIZE) of a bench run with --calib-copy, scaled "
+                        "by what each counter reads for the trailing 256 MiB copies")
     p.add_argument("--warm", action="store_true",
                    help="also time the headline call on one reused buffer set (its bytes "
                         "then come from the Infinity Cache); off by default so that a "
@@ -106,28 +110,23 @@ def traffic_from_profile(source_hash: str):
 
 
 WIRE_COUNTERS = os.path.join(ROOT, "profiles", "wire_16Mi_counters.txt")
-WIRE_SOURCES = [os.path.join(ROOT, "ar_rmsnorm_amd", "csrc", f) for f in ("wire.hip", "device.h")]
 
 
 def wire_traffic():
     """Scaled HBM bytes per dispatch of the wire kernels from the committed
-    counter summary, keyed by (kernel, grid lanes); empty when the wire
-    kernel sources changed since the counters were taken."""
+    counter summary (written by --counter-summary), keyed by (kernel, grid
+    lanes); empty when the kernel sources changed since it was taken."""
     try:
         text = open(WIRE_COUNTERS).read()
     except OSError:
         return {}
-    h = hashlib.sha256()
-    for f in WIRE_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
-    m = re.search(r"^wire\.hip \+ device\.h sha256\[:16\]: (\S+)", text, re.M)
-    if not m or m.group(1) != h.hexdigest()[:16]:
+    m = re.search(r"^kernel sources sha256\[:16\]: (\S+)", text, re.M)
+    if not m or m.group(1) != all_source_hash():
         return {}
     out = {}
     for line in text.splitlines():
-        t = re.match(r"\s*\d+\s+\d+\s+[\d.]+\s+[\d.]+\s+(\d+)\s+\S+\s+\S+\s+(ar::\S+) "
-                     r"\[(\d+), \d+\]", line)
+        t = re.match(r"\s*\d+\s+\d+\s+[\d.]+\s+[\d.]+\s+(\d+)\s+\S+\s+\S+\s+(ar::.+?) "
+                     r"\[(\d+), \d+\]$", line)
         if t:
             out[(t.group(2), int(t.group(3)))] = float(t.group(1))
     return out
@@ -195,6 +194,110 @@ def trace_summary(d: str) -> str:
     return "\n".join(out)
 
 
+ALL_SOURCES = [os.path.join(ROOT, "ar_rmsnorm_amd", "csrc", f)
+               for f in ("reduce.hip", "wire.hip", "stream.hip", "copy.hip", "device.h",
+                         "index_map.h")]
+
+
+def all_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ALL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes():
+    """What a launch must move, by (kernel, grid lanes), for the kernels the
+    counter runs cover: the headline (the method's bytes and the bytes the
+    kernel moves), the wire formats at 16 Mi (+13) fp32, W=4, and the plain
+    copy."""
+    n, W = 4_194_304, 8
+    shard = n // 8 // W * 16
+    out = {("ar::reduce_2stage_kernel<8, true, true, 256, 1, 2>", 256 * 256 + 7 * 128 * 256):
+           (W * shard + 2 * shard + 2 * (W - 1) * shard, "moved; the method's count is "
+            f"{(3 * W + 1) * shard}")}
+    for nn in (16_777_216, 16_777_229):
+        ll, l128 = -(-4 * nn // 8), -(-4 * nn // 120)
+        out[("ar::ll_unpack_reduce_kernel<4>", -(-ll // 128) * 128)] = (4 * ll * 16 + 4 * nn, "")
+        out[("ar::ll128_unpack_reduce_kernel<4>", -(-8 * l128 // 256) * 256)] = (
+            4 * l128 * 128 + 4 * nn, "")
+        out[("ar::ll_pack_kernel", -(-ll // 256) * 256)] = (4 * nn + ll * 16, "")
+        out[("ar::ll128_pack_kernel", -(-16 * ((l128 + 1) // 2) // 256) * 256)] = (
+            4 * nn + l128 * 128, "")
+    for mib in (12, 256):
+        out[("ar::copy_kernel", (mib << 20) // 16)] = (2 * (mib << 20), "")
+    return out
+
+
+def counter_summary(fetch_dir: str, write_dir: str) -> str:
+    """HBM bytes per dispatch of every kernel and grid in two rocprofv3 --pmc
+    runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each counter scaled
+    by its reading for the run's last three dispatches, plain 256 MiB copies
+    of the library's copy kernel (262,144 KiB read + 262,144 KiB written)."""
+    import csv
+    import glob
+    import numpy as np
+
+    def load(d):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"bench.py: no counter_collection.csv under {d}")
+        recs = []
+        for f in files:
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    name = r["Kernel_Name"]
+                    name = (name[5:] if name.startswith("void ") else name).split("(")[0]
+                    recs.append((int(r["Dispatch_Id"]), name, int(r["Grid_Size"]),
+                                 int(r["Workgroup_Size"]), float(r["Counter_Value"])))
+        recs.sort()
+        return recs
+
+    f, w = load(fetch_dir), load(write_dir)
+    kib = 256 * 1024
+    cal_f = [x[4] for x in f if x[1] == "ar::copy_kernel" and x[2] == (256 << 20) // 16][-3:]
+    cal_w = [x[4] for x in w if x[1] == "ar::copy_kernel" and x[2] == (256 << 20) // 16][-3:]
+    if len(cal_f) < 3 or len(cal_w) < 3:
+        raise SystemExit("bench.py: the runs end without the three calibration copies "
+                         "(run the bench with --calib-copy)")
+    sf, sw = kib / float(np.mean(cal_f)), kib / float(np.mean(cal_w))
+
+    def groups(d):
+        g = {}
+        for _, name, grid, wg, v in d[:-3]:
+            g.setdefault((name, grid, wg), []).append(v)
+        return g
+
+    gf, gw = groups(f), groups(w)
+    alg = algorithmic_bytes()
+    out = [f"kernel sources sha256[:16]: {all_source_hash()}",
+           f"calibration (last three 256 MiB copies): FETCH_SIZE KiB "
+           f"{[round(x, 1) for x in cal_f]} -> scale {sf:.4f}; WRITE_SIZE KiB "
+           f"{[round(x, 1) for x in cal_w]} -> scale {sw:.4f}",
+           "%6s %6s %12s %12s %14s %14s %8s  %s" % ("n(f)", "n(w)", "fetch MiB", "write MiB",
+                                                   "scaled bytes", "algorithmic", "ratio",
+                                                   "kernel [grid lanes, wg]")]
+    head = None
+    for key in sorted(gf, key=lambda k: -float(np.mean(gf[k]))):
+        name, grid, wg = key
+        if not name.startswith("ar::") or key not in gw:
+            continue
+        fb = float(np.mean(gf[key])) * sf * 1024
+        wb = float(np.mean(gw[key])) * sw * 1024
+        a = alg.get((name, grid))
+        out.append("%6d %6d %12.2f %12.2f %14.0f %14s %8s  %s [%d, %d]" % (
+            len(gf[key]), len(gw[key]), fb / 2 ** 20, wb / 2 ** 20, fb + wb,
+            a[0] if a else "-", f"{(fb + wb) / a[0]:.4f}" if a else "-", name, grid, wg))
+        if name.startswith("ar::reduce_2stage_kernel<8, true, true") and a:
+            head = (fb + wb, a)
+    if head:
+        out += ["", f"source_hash: {kernel_source_hash()}",
+                f"hbm_bytes_per_launch: {head[0]:.0f}",
+                f"headline traffic / bytes moved: {head[0] / head[1][0]:.4f} ({head[1][1]})"]
+    return "\n".join(out)
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -213,6 +316,9 @@ def main():
     args = parse()
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
+        return
+    if args.counter_summary:
+        print(counter_summary(*args.counter_summary))
         return
     if args.gpus != 1:
         print(f"bench.py: libar runs on one GPU only; --gpus {args.gpus} is not "
@@ -594,6 +700,8 @@ def main():
         # every call as in its CUDA-graph replays): the one-shot fused call
         # and the one-launch Lamport call, median of 5 graph replays each
         def med_us(fns, steps=200):
+            if args.eager:
+                return round(graph_time(fns, steps, args.warmup) * 1e3, 3)
             first, each = graph_time_stats(fns, steps, args.warmup, extra=4)
             return round(float(np.median([first] + each)) * 1e3, 3)
 
@@ -819,11 +927,12 @@ def main():
         # sets (one rotation touches 24 MiB per set; the Infinity Cache holds
         # 256 MB), each set with its own 8 input and 8 staging buffers
         sweep = {}
+        cap_packs = n // 8 // W + (n // 8) % W       # staging packs per shard
         for count in (1, 2, 3, 4, 6, 12, 23, 40):
             sw = []
             for k in range(count):
                 ins = rank_buffers(W, 2 * n, torch.int16, base)
-                tmps = rank_buffers(W, (part + rem) * 16, torch.int16)
+                tmps = rank_buffers(W, cap_packs * 16, torch.int16)
                 for r in range(1, W):
                     ar.ar_reduce_2stage(ins, tmps, r, None, flags=ar.AR_STAGE_RS)
                 sw.append((ins, tmps, torch.empty(n, dtype=torch.int16, device=dev)))
@@ -1011,10 +1120,12 @@ def main():
         result["rows"] = rows
 
     if args.calib_copy:
-        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        # counter calibration: three plain 256 MiB copies with the library's
+        # copy kernel (262,144 KiB read + 262,144 KiB written each)
+        a = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
         for _ in range(3):
-            b.copy_(a)
+            ar.ar_copy(a, b)
         torch.cuda.synchronize()
 
     # ------------------------------------------------------------------
