@@ -127,6 +127,30 @@ constexpr void fifo_slice(int64_t full, int64_t total, int64_t unit, int pairs, 
     fifo_slice_at(fifo_span(full, unit, pairs), total, pair, lo, hi);
 }
 
+// Steps per batch on the LL path.  A batch holds per_batch lines; when a
+// pair's slice of a full step (span lines) is half a batch or less, a batch
+// takes that many whole consecutive steps instead, at most max_steps, so
+// that every lane keeps several lines in flight; 1 otherwise.  A producer
+// waits for the head that frees the last slot of its batch, so it can work
+// a batch ahead of its consumer in the 8-step ring only while 2 * S <= 8.
+constexpr int fifo_batch_steps(int64_t span, int64_t per_batch, int max_steps)
+{
+    if (span <= 0)
+        return 1;
+    const int64_t s = per_batch / span;
+    return s < 2 ? 1 : s > max_steps ? max_steps : (int)s;
+}
+
+// Lane slot v (u * lanes + lane) of a batch of whole steps whose slices are
+// len lines long: the slot carries line `line` of the pair's slice of the
+// batch's step `step` (no line when step is past the batch).  The same slot
+// every batch; 32-bit division, once per workgroup.
+constexpr void fifo_batch_slot(uint32_t v, uint32_t len, int *step, uint32_t *line)
+{
+    *step = (int)(v / len);
+    *line = v % len;
+}
+
 // Pairs per channel when `resident` workgroups fit on the device at once: as
 // many as fit (two workgroups per pair), at most max_pairs, and no more than
 // leave every pair a slice of a full step of at least min_slice items (one

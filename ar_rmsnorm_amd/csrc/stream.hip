@@ -17,12 +17,14 @@
 //   LL128   128-byte lines, 120 payload bytes + a 64-bit flag.  gfx950 does
 //           not promise that a line written by eight lanes becomes visible
 //           as a whole, so the producer makes the order explicit per batch
-//           of 4,096 chunks: the batch's data, then a wait until those
-//           stores are acknowledged and a barrier, then the batch's flag
-//           words.  The consumer waits for the flag of the batch's first
-//           line (after which every data byte of the batch is visible), then
+//           of 4,096 chunks (512 lines): every line of the batch goes out
+//           whole, flag included, except that the batch's first line
+//           carries a zero flag word; then a wait until those stores are
+//           acknowledged and a barrier; then the first line's flag.  The
+//           consumer waits for that flag (after which every byte of the
+//           batch, every other line's flag included, is visible), then
 //           reads every line and checks every line's flag, re-reading the
-//           flag chunk of lines whose flag has not arrived yet.
+//           flag chunk of a line whose flag has not arrived yet.
 //   Simple  raw payload; the producer publishes a tail step once the step's
 //           data is acknowledged, and the consumer waits for it.
 // For every protocol the consumer publishes a head step (the next step it
@@ -83,6 +85,7 @@ template <int T>
 constexpr int kBatchOf = (int)(kPerBatch / T);   // items in flight per lane
 constexpr uint32_t kAbortCheck = 16;   // spins between looks at the error count
 constexpr int kMaxPairs = kFifoMaxPairs;      // producer/consumer pairs per channel
+constexpr int kMaxBatchSteps = 4;              // LL: whole steps per batch, 2 * 4 <= 8 slots
 
 struct StreamArgs {
     const uint32_t *src;    // n fp32 payload values (as words)
@@ -101,6 +104,7 @@ struct StreamArgs {
     int channels;
     int pairs;              // producer/consumer pairs per channel
     int64_t span;           // items of a full step per pair (fifo_span)
+    int batch_steps;        // LL: whole steps per batch (fifo_batch_steps), else 1
     int from_state;         // the first step comes from state[0]
     uint64_t first_step;
     uint32_t max_spins;
@@ -464,13 +468,19 @@ __device__ __forceinline__ void store_ring(const Step &g, int64_t base, const u3
             const uint32_t f = (uint32_t)(g.k + 1);
             store16_sys(g.slot, p, u32x4{d[u].x, f, d[u].y, f});
         } else if (PROTO == 1) {
-            // chunk 7 goes out whole with a zero flag word (no step's flag is
-            // 0), so each line is written by one full-line store
+            // every line goes out whole, chunk 7 with the step's flag, except
+            // the batch's first line (chunk 7 of the row's line A), whose flag
+            // word is zero (no step's flag is 0) until the batch is
+            // acknowledged
             const int c = (int)(i & 15);
+            const uint64_t f = g.k + 1;
+            const bool first_line = (i >> 3) == (base >> 3);
+            const uint32_t flo = first_line ? 0u : (uint32_t)f;
+            const uint32_t fhi = first_line ? 0u : (uint32_t)(f >> 32);
             store16_sys(g.slot, p, c < 7    ? d[u]
-                           : c == 7 ? u32x4{d[u].x, d[u].y, 0u, 0u}
+                           : c == 7 ? u32x4{d[u].x, d[u].y, flo, fhi}
                            : c < 15 ? u32x4{hz, hw, d[u].x, d[u].y}
-                                    : u32x4{hz, hw, 0u, 0u});
+                                    : u32x4{hz, hw, (uint32_t)f, (uint32_t)(f >> 32)});
         } else if (4 * i + 4 <= g.words) {
             store16_sys(g.slot, p, d[u]);
         } else {
@@ -585,14 +595,13 @@ __device__ void produce(const StreamArgs &a, int c, int pair, int p, int64_t s0,
             return;
         store_ring<T, PROTO>(cur.g, cur.base, d);
         if (PROTO == 1) {
-            // this batch's data is acknowledged before any of its flags
+            // every line of the batch, flags included, is acknowledged
+            // before the flag of its first line
             drain_memory();
             __syncthreads();
-            const int64_t end = cur.base + kPerBatch < cur.g.items ? cur.base + kPerBatch
-                                                                    : cur.g.items;
             const uint64_t f = cur.g.k + 1;
-            for (int64_t l = cur.base / 8 + threadIdx.x; l < end / 8; l += T)
-                store8_sys(cur.g.slot, (uint32_t)(128 * l + 120),
+            if (threadIdx.x == 0)
+                store8_sys(cur.g.slot, (uint32_t)(128 * (cur.base / 8) + 120),
                            u32x2{(uint32_t)f, (uint32_t)(f >> 32)});
         }
         if (PROTO == 2 && nxt.j != cur.j) {
@@ -624,14 +633,14 @@ __device__ bool close_step(const StreamArgs &a, int p, uint64_t k, bool failed)
     return !any_failed;
 }
 
-// Wait until every item of a batch is valid (bounded; gives up early once
+// Wait until every item of a batch is valid(u, item) (bounded; gives up early once
 // any wait of the launch has failed).  While items are missing, one lane of
 // the wavefront (the first still waiting) polls the earliest of its missing
 // items, since the producer stores a lane's items in that order and the
 // producer's lanes write together; a miss backs off briefly.  Once that item
 // is valid, every waiting lane reads its missing items again.  One poll per
 // wavefront instead of one per lane keeps the polls from adding traffic.
-template <int T, typename Offset, typename Valid>
+template <int T, bool BY_SLOT = false, typename Offset, typename Valid>
 __device__ bool poll_batch(const StreamArgs &a, u32x4 v[kBatchOf<T>], bool ok[kBatchOf<T>], Rsrc slot,
                            Offset off, Valid valid)
 {
@@ -643,15 +652,39 @@ __device__ bool poll_batch(const StreamArgs &a, u32x4 v[kBatchOf<T>], bool ok[kB
         respin();
         if (s % kAbortCheck == 0 && aborted(a.errors))
             break;
-        int lead = 0;
-#pragma unroll
-        for (int u = kBatchOf<T> - 1; u >= 0; --u)
-            if (!ok[u])
-                lead = u;
+        // the polling lane looks at its earliest missing item
         const int first = __builtin_amdgcn_readfirstlane((int)threadIdx.x);
         int hit = 0;
-        if ((int)threadIdx.x == first)
-            hit = valid(load16_sys(slot, off(lead))) ? 1 : 0;
+        if constexpr (BY_SLOT) {
+            // callbacks that read per-slot arrays are called with constant
+            // slots only, so those arrays stay in registers
+            if ((int)threadIdx.x == first) {
+                uint32_t o = 0;
+                int lead = -1;
+#pragma unroll
+                for (int u = kBatchOf<T> - 1; u >= 0; --u) {
+                    if (!ok[u]) {
+                        o = off(u);
+                        lead = u;
+                    }
+                }
+                const u32x4 x = load16_sys(slot, o);
+                bool h = false;
+#pragma unroll
+                for (int u = 0; u < kBatchOf<T>; ++u)
+                    if (u == lead)
+                        h = valid(u, x);
+                hit = h ? 1 : 0;
+            }
+        } else {
+            int lead = 0;
+#pragma unroll
+            for (int u = kBatchOf<T> - 1; u >= 0; --u)
+                if (!ok[u])
+                    lead = u;
+            if ((int)threadIdx.x == first)
+                hit = valid(lead, load16_sys(slot, off(lead))) ? 1 : 0;
+        }
         if (!__builtin_amdgcn_readfirstlane(hit)) {
             __builtin_amdgcn_s_sleep(1);
             continue;
@@ -663,7 +696,7 @@ __device__ bool poll_batch(const StreamArgs &a, u32x4 v[kBatchOf<T>], bool ok[kB
         all = true;
 #pragma unroll
         for (int u = 0; u < kBatchOf<T>; ++u) {
-            ok[u] = ok[u] || valid(v[u]);
+            ok[u] = ok[u] || valid(u, v[u]);
             all = all && ok[u];
         }
     }
@@ -702,7 +735,7 @@ __device__ void consume_ll(const StreamArgs &a, int c, int pair, int p, int64_t 
             failed = !poll_batch<T>(
                 a, v, ok, cur.g.slot,
                 [&](int u) { return (uint32_t)(16 * (i0 + (int64_t)u * T)); },
-                valid);
+                [&](int, u32x4 x) { return valid(x); });
         Cursor nxt;
         const bool more = advance<0>(a, ring, s0, first, steps, pair, cur, &nxt);
         loads_returned<T>(v);
@@ -725,6 +758,237 @@ __device__ void consume_ll(const StreamArgs &a, int c, int pair, int p, int64_t 
         if (!more)
             return;
         cur = nxt;
+#pragma unroll
+        for (int u = 0; u < kBatchOf<T>; ++u) {
+            v[u] = nv[u];
+            lv[u] = nlv[u];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// LL with whole steps per batch.  With several pairs per channel a pair's
+// slice of NCCL's 32 KiB LL step is 512-1,024 lines, a quarter of a batch or
+// less, so a batch kept inside one step left most lanes one line in flight
+// per round trip.  When the host sets batch_steps S > 1, a batch is S
+// consecutive whole steps of the pair instead: lane slot v = u * T + lane
+// carries line v mod L of the batch's step v / L (fifo_batch_slot; L is the
+// pair's slice of a full step), the same slot every batch.  LL lines
+// validate themselves, so the protocol is unchanged: the producer waits for
+// the head that frees the slot of the batch's last step (with S <= 4 it can
+// work a batch ahead of its consumer), the consumer re-polls missing lines
+// and publishes the head once per batch.  A batch's lines lie in several
+// ring slots, so these paths address the channel's whole ring through one
+// descriptor (the host sets S > 1 only for rings under 2 GiB).
+template <int T>
+struct LLSteps {
+    Rsrc ring;                      // the channel's 8 slots
+    int64_t lo;                     // first line of the pair's slice
+    uint32_t len_full, len_last;    // lines of the pair's slice of a full step and of
+                                    // the channel's last step
+    int64_t last;                   // local index of the channel's last step
+    int64_t steps;                  // steps that give the pair a slice
+    uint32_t slot[kBatchOf<T>];     // per lane slot: step within the batch << 16 | line
+                                    // within the slice (a slice is under 2^16 lines
+                                    // whenever a batch takes two steps or more)
+};
+
+// False when the pair has nothing to move (no steps, or its slice of the
+// channel's only step is empty).
+template <int T>
+__device__ __forceinline__ bool ll_steps_setup(const StreamArgs &a, int c, int pair, int64_t s0,
+                                               int64_t steps, LLSteps<T> *m)
+{
+    m->ring = slot_rsrc(a.fifo + (int64_t)c * 8 * a.wire_bytes, 8 * a.wire_bytes);
+    int64_t hi_full = 0;
+    fifo_slice_at(a.span, a.step_bytes / 8, pair, &m->lo, &hi_full);
+    const int64_t len = hi_full - m->lo;
+    m->len_full = len > 0 ? (uint32_t)len : 0u;
+    m->len_last = 0;
+    m->last = steps - 1;
+    m->steps = steps;
+    if (steps > 0) {
+        const int64_t left = 4 * a.n - (s0 + steps - 1) * a.step_bytes;
+        const int64_t bytes = left < a.step_bytes ? left : a.step_bytes;
+        int64_t lo_last = 0, hi_last = 0;
+        fifo_slice_at(a.span, items_of<0>(bytes, bytes / 4), pair, &lo_last, &hi_last);
+        if (hi_last > lo_last)
+            m->len_last = (uint32_t)(hi_last - lo_last);   // lo_last == lo then
+        else
+            m->steps = steps - 1;   // only a channel's last step can leave a pair no slice
+    }
+    if (len <= 0)
+        m->steps = 0;
+#pragma unroll
+    for (int u = 0; u < kBatchOf<T>; ++u) {
+        int step = kMaxBatchSteps;
+        uint32_t line = 0;
+        if (len > 0)
+            fifo_batch_slot((uint32_t)(u * T) + threadIdx.x, (uint32_t)len, &step, &line);
+        m->slot[u] = (uint32_t)(step < kMaxBatchSteps ? step : kMaxBatchSteps) << 16 | line;
+    }
+    return m->steps > 0;
+}
+
+// One batch, the same for every lane: what the lane slots need from it.
+struct LLBatch {
+    int n_in;          // steps in the batch
+    int dj_last;       // the channel's last step as a step of the batch, or -1
+    uint32_t k0;       // low 32 bits of the batch's first ring step
+    int64_t word0;     // payload word of line lo of the batch's first step
+};
+template <int T>
+__device__ __forceinline__ LLBatch ll_batch(const StreamArgs &a, const LLSteps<T> &m, int64_t s0,
+                                            uint64_t first, int64_t j0)
+{
+    LLBatch b;
+    b.n_in = m.steps - j0 < a.batch_steps ? (int)(m.steps - j0) : a.batch_steps;
+    b.dj_last = m.last - j0 < b.n_in ? (int)(m.last - j0) : -1;
+    b.k0 = (uint32_t)(first + (uint64_t)j0);
+    b.word0 = (s0 + j0) * (a.step_bytes / 4) + 2 * m.lo;
+    return b;
+}
+template <int T>
+__device__ __forceinline__ bool ll_has(const LLSteps<T> &m, const LLBatch &b, int u)
+{
+    const int dj = (int)(m.slot[u] >> 16);
+    const uint32_t line = m.slot[u] & 0xFFFFu;
+    return dj < b.n_in && line < (dj == b.dj_last ? m.len_last : m.len_full);
+}
+// Lane parts in 32 bits: a step is at most 2^30 bytes and dj <= 3.
+template <int T>
+__device__ __forceinline__ int64_t ll_word(const StreamArgs &a, const LLSteps<T> &m,
+                                           const LLBatch &b, int u)
+{
+    return b.word0 + (int64_t)((m.slot[u] >> 16) * (uint32_t)(a.step_bytes / 4) +
+                               2u * (m.slot[u] & 0xFFFFu));
+}
+template <int T>
+__device__ __forceinline__ uint32_t ll_off(const StreamArgs &a, const LLSteps<T> &m,
+                                           const LLBatch &b, int u)
+{
+    return ((b.k0 + (m.slot[u] >> 16)) & 7u) * (uint32_t)a.wire_bytes +
+           16u * ((uint32_t)m.lo + (m.slot[u] & 0xFFFFu));
+}
+template <int T>
+__device__ __forceinline__ uint32_t ll_flag(const LLSteps<T> &m, const LLBatch &b, int u)
+{
+    return b.k0 + (m.slot[u] >> 16) + 1u;
+}
+
+template <int T>
+__device__ __forceinline__ void ll_steps_load_src(const StreamArgs &a, const LLSteps<T> &m,
+                                                  const LLBatch &b, u32x4 d[kBatchOf<T>])
+{
+#pragma unroll
+    for (int u = 0; u < kBatchOf<T>; ++u) {
+        d[u] = u32x4{0u, 0u, 0u, 0u};
+        if (ll_has(m, b, u)) {
+            const u32x2 p = pair_at(a, ll_word(a, m, b, u));
+            d[u] = u32x4{p.x, p.y, 0u, 0u};
+        }
+    }
+}
+
+template <int T, bool LOCAL>
+__device__ __forceinline__ void ll_steps_load(const StreamArgs &a, const LLSteps<T> &m,
+                                              const LLBatch &b, u32x4 v[kBatchOf<T>],
+                                              u32x4 lv[kBatchOf<T>])
+{
+#pragma unroll
+    for (int u = 0; u < kBatchOf<T>; ++u) {
+        const bool has = ll_has(m, b, u);
+        v[u] = has ? load16_sys(m.ring, ll_off(a, m, b, u)) : u32x4{0u, 0u, 0u, 0u};
+        lv[u] = LOCAL && has ? local_at(a, ll_word(a, m, b, u), 2) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+template <int T>
+__device__ void produce_ll_steps(const StreamArgs &a, int c, int pair, int p, int64_t s0,
+                                 int64_t steps, uint64_t first, Shared *sh)
+{
+    LLSteps<T> m;
+    if (!ll_steps_setup<T>(a, c, pair, s0, steps, &m))
+        return;
+    const int S = a.batch_steps;
+    uint64_t head_seen = first;      // the consumer has taken every step before `first`
+    LLBatch b = ll_batch<T>(a, m, s0, first, 0);
+    u32x4 d[kBatchOf<T>];
+    ll_steps_load_src<T>(a, m, b, d);
+    for (int64_t j0 = 0;; j0 += S) {
+        const int64_t nj = j0 + S;
+        const bool more = nj < m.steps;
+        const LLBatch nb = ll_batch<T>(a, m, s0, first, nj);
+        u32x4 nd[kBatchOf<T>];
+        if (more)
+            ll_steps_load_src<T>(a, m, nb, nd);
+        const int64_t jl = j0 + b.n_in - 1;   // the batch's last step
+        if (jl >= 8 && !wait_counter(a, sh, a.head + p, first + (uint64_t)jl - 7, &head_seen))
+            return;
+#pragma unroll
+        for (int u = 0; u < kBatchOf<T>; ++u) {
+            if (!ll_has(m, b, u))
+                continue;
+            const uint32_t f = ll_flag(m, b, u);
+            store16_sys(m.ring, ll_off(a, m, b, u), u32x4{d[u].x, f, d[u].y, f});
+        }
+        if (!more)
+            return;
+        b = nb;
+#pragma unroll
+        for (int u = 0; u < kBatchOf<T>; ++u)
+            d[u] = nd[u];
+    }
+}
+
+template <int T, bool LOCAL>
+__device__ void consume_ll_steps(const StreamArgs &a, int c, int pair, int p, int64_t s0,
+                                 int64_t steps, uint64_t first)
+{
+    LLSteps<T> m;
+    if (!ll_steps_setup<T>(a, c, pair, s0, steps, &m))
+        return;
+    const int S = a.batch_steps;
+    LLBatch b = ll_batch<T>(a, m, s0, first, 0);
+    u32x4 v[kBatchOf<T>], lv[kBatchOf<T>];
+    ll_steps_load<T, LOCAL>(a, m, b, v, lv);
+    bool failed = false;
+    for (int64_t j0 = 0;; j0 += S) {
+        auto valid = [&](int u, u32x4 x) {
+            const uint32_t f = ll_flag(m, b, u);
+            return x.y == f && x.w == f;
+        };
+        bool ok[kBatchOf<T>];
+        bool ahead = true;       // every line was there on the first look
+#pragma unroll
+        for (int u = 0; u < kBatchOf<T>; ++u) {
+            ok[u] = !ll_has(m, b, u) || valid(u, v[u]);
+            ahead = ahead && ok[u];
+        }
+        if (!failed)
+            failed = !poll_batch<T, true>(
+                a, v, ok, m.ring, [&](int u) { return ll_off(a, m, b, u); }, valid);
+        const int64_t nj = j0 + S;
+        const bool more = nj < m.steps;
+        loads_returned<T>(v);
+        if (!close_step(a, p, first + (uint64_t)(j0 + b.n_in - 1), failed))
+            return;
+        const LLBatch nb = ll_batch<T>(a, m, s0, first, nj);
+        u32x4 nv[kBatchOf<T>], nlv[kBatchOf<T>];
+        if (more && ahead)
+            ll_steps_load<T, LOCAL>(a, m, nb, nv, nlv);
+        if (!failed) {
+#pragma unroll
+            for (int u = 0; u < kBatchOf<T>; ++u)
+                if (ll_has(m, b, u))
+                    deliver<LOCAL>(a, ll_word(a, m, b, u), 2, u32x4{v[u].x, v[u].z, 0u, 0u},
+                                   lv[u]);
+        }
+        if (more && !ahead)
+            ll_steps_load<T, LOCAL>(a, m, nb, nv, nlv);
+        if (!more)
+            return;
+        b = nb;
 #pragma unroll
         for (int u = 0; u < kBatchOf<T>; ++u) {
             v[u] = nv[u];
@@ -800,7 +1064,7 @@ __device__ void consume_ll128(const StreamArgs &a, int c, int pair, int p, int64
                     const int64_t q = q0 + (int64_t)u * T;
                     return (uint32_t)(128 * (q >> 3) + 112);
                 },
-                valid);
+                [&](int, u32x4 x) { return valid(x); });
         loads_returned<T>(v);
         if (nxt.j != cur.j && !close_step(a, p, cur.g.k, failed))
             return;
@@ -895,10 +1159,21 @@ __global__ __launch_bounds__(T, T == kWideThreads || !LOCAL ? 4 : 2) void stream
     const int64_t s0 = (int64_t)c * a.total_steps / a.channels;
     const int64_t s1 = (int64_t)(c + 1) * a.total_steps / a.channels;
     if (producer) {
+        if constexpr (PROTO == 0 && T == kWideThreads) {
+            if (a.batch_steps > 1) {
+                produce_ll_steps<T>(a, c, pair, p, s0, s1 - s0, first, &sh);
+                return;
+            }
+        }
         produce<T, PROTO>(a, c, pair, p, s0, s1 - s0, first, &sh);
         return;
     }
-    if (PROTO == 0)
+    if constexpr (PROTO == 0 && T == kWideThreads) {
+        if (a.batch_steps > 1)
+            consume_ll_steps<T, LOCAL>(a, c, pair, p, s0, s1 - s0, first);
+        else
+            consume_ll<T, LOCAL>(a, c, pair, p, s0, s1 - s0, first);
+    } else if (PROTO == 0)
         consume_ll<T, LOCAL>(a, c, pair, p, s0, s1 - s0, first);
     else if (PROTO == 1)
         consume_ll128<T, LOCAL>(a, c, pair, p, s0, s1 - s0, first, &sh);
@@ -973,6 +1248,9 @@ hipError_t launch_fifo_stream(int proto, const float *src, const float *local, f
         const int64_t full = proto == 0 ? step_bytes / 8 : proto == 1 ? step_bytes / 120 * 8
                                                                      : step_bytes / 16;
         a.span = fifo_span(full, proto == 1 ? 16 : 1, pairs);
+        a.batch_steps = proto == 0 && wide && 8 * wire_bytes <= (int64_t)INT32_MAX
+                            ? fifo_batch_steps(a.span, kPerBatch, kMaxBatchSteps)
+                            : 1;
     }
     a.from_state = from_state ? 1 : 0;
     a.first_step = first_step;

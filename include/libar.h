@@ -439,14 +439,18 @@ ar_status_t ll128_unpack_reduce(const void *const *fifos, int W, float *out,
  *   AR_PROTO_LL      16-byte lines of 8 payload bytes + two 32-bit flags
  *                    (k + 1), ready when both flags match
  *   AR_PROTO_LL128   128-byte lines of 120 payload bytes + a 64-bit flag
- *                    (k + 1); per batch of 512 lines the producer writes the
- *                    data, waits until those stores are acknowledged, then
- *                    writes the flags; the consumer waits for the batch's
- *                    first flag, then reads every line and checks its flag
+ *                    (k + 1); per batch of 512 lines the producer writes
+ *                    every line whole with its flag, except a zero flag in
+ *                    the batch's first line, waits until those stores are
+ *                    acknowledged, then writes the first line's flag; the
+ *                    consumer waits for that flag, then reads every line and
+ *                    checks its flag
  *   AR_PROTO_SIMPLE  raw payload; ready when the channel's tail counter
  *                    reaches k + 1
- * After each step a pair's consumer sets the pair's head counter to k + 1;
- * its producer reuses its slice of slot k mod 8 only once head >= k - 7.  A step writes only
+ * After each step a pair's consumer sets the pair's head counter to k + 1
+ * (on the LL path where a batch spans S <= 4 whole steps, once per batch,
+ * to its last step's k + 1); its producer reuses its slice of slot k mod 8
+ * only once head >= k - 7.  A step writes only
  * the lines (or bytes) that carry payload.  The consumer delivers
  * out[e] = src[e], or local[e] + src[e] in fp32 when local is given.
  *   proto       AR_PROTO_LL / AR_PROTO_LL128 / AR_PROTO_SIMPLE

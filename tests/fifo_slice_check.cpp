@@ -54,6 +54,63 @@ static void check(int64_t full, int64_t unit, int pairs)
     }
 }
 
+// Batches of whole steps (the LL path with fifo_batch_steps() > 1): over a
+// channel of `steps` steps whose last one has last_total lines, every line
+// of every pair's slice of every step is carried by exactly one lane slot
+// (fifo_batch_slot(), as the kernel computes it) of exactly one batch, no
+// slot carries a line outside its step's slice, a batch's lines fit its
+// 4,096 lane slots, and the batch stays within half the 8-step ring.
+static void check_batches(int64_t full, int pairs, int64_t last_total, int64_t steps)
+{
+    const int64_t unit = 1;
+    const int64_t span = ar::fifo_span(full, 1, pairs);
+    const int S = ar::fifo_batch_steps(span, 4096, 4);
+    CHECK(S >= 1 && S <= 4, "batch of %d steps", S);
+    if (S == 1)
+        return;
+    for (int g = 0; g < pairs; ++g) {
+        int64_t lo = 0, hi_full = 0, lo_last = 0, hi_last = 0;
+        ar::fifo_slice_at(span, full, g, &lo, &hi_full);
+        ar::fifo_slice_at(span, last_total, g, &lo_last, &hi_last);
+        const int64_t len = hi_full - lo;
+        if (len <= 0)
+            continue;                       // the host never leaves a pair without a slice
+        CHECK(S * len <= 4096, "pair %d: %d steps of %lld lines exceed a batch", g, S,
+              (long long)len);
+        int64_t eff = steps;
+        if (hi_last <= lo_last)
+            --eff;
+        std::vector<std::vector<int>> seen(steps, std::vector<int>(full, 0));
+        for (int64_t j0 = 0; j0 < eff; j0 += S) {
+            const int n_in = eff - j0 < S ? (int)(eff - j0) : S;
+            for (uint32_t v = 0; v < 4096; ++v) {
+                int step = 0;
+                uint32_t line = 0;
+                ar::fifo_batch_slot(v, (uint32_t)len, &step, &line);
+                if (step >= n_in)
+                    continue;
+                const int64_t j = j0 + step;
+                const int64_t hi = j == steps - 1 ? hi_last : hi_full;
+                const int64_t i = lo + (int64_t)line;
+                if (i >= hi)
+                    continue;
+                CHECK(i >= lo && i < full, "pair %d step %lld line %lld outside", g,
+                      (long long)j, (long long)i);
+                if (i >= 0 && i < full)
+                    ++seen[j][i];
+            }
+        }
+        for (int64_t j = 0; j < steps; ++j) {
+            const int64_t a = j == steps - 1 ? lo_last : lo, b = j == steps - 1 ? hi_last : hi_full;
+            for (int64_t i = 0; i < full; ++i) {
+                const int want = i >= a && i < b ? 1 : 0;
+                CHECK(seen[j][i] == want, "pair %d step %lld line %lld carried %d times",
+                      g, (long long)j, (long long)i, seen[j][i]);
+            }
+        }
+    }
+}
+
 int main()
 {
     long cases = 0;
@@ -86,6 +143,16 @@ int main()
                             CHECK(pairs == 1 || hi - lo >= min_slice, "slice under the minimum");
                         }
                     }
+                    ++cases;
+                }
+            }
+        }
+    }
+    for (int64_t full : {600, 1000, 1024, 2048, 2049, 4096, 8192, 16384}) {
+        for (int pairs = 1; pairs <= 8; ++pairs) {
+            for (int64_t steps : {1, 2, 3, 4, 5, 7, 8, 9, 13, 16}) {
+                for (int64_t last : {full, full - 1, full / 2, (int64_t)1, full * 3 / 4 + 1}) {
+                    check_batches(full, pairs, last, steps);
                     ++cases;
                 }
             }

@@ -89,3 +89,30 @@ def test_streaming_slices_cover_every_step(tmp_path):
                     os.path.join(HERE, "fifo_slice_check.cpp")], check=True)
     out = run(exe)
     assert out.endswith("0 failures\n"), out
+
+
+@pytest.mark.parametrize("old,new", [
+    # a batch of whole steps one step too long for the ring window
+    ("return s < 2 ? 1 : s > max_steps ? max_steps : (int)s;",
+     "return s < 2 ? 1 : s > max_steps ? max_steps + 1 : (int)s + 1;"),
+    # the step of a lane slot changing one slot early
+    ("*step = (int)(v / len);", "*step = (int)((v + 1) / len);"),
+])
+def test_the_slice_check_catches_planted_batch_mistakes(tmp_path, old, new):
+    """Plant a mistake in a copy of the batch-of-steps functions and make
+    sure tests/fifo_slice_check.cpp reports it."""
+    if shutil.which("g++") is None:
+        pytest.skip("g++ not available")
+    src = open(os.path.join(HERE, "..", "ar_rmsnorm_amd", "csrc", "index_map.h")).read()
+    assert src.count(old) == 1
+    bad_dir = tmp_path / "ar_rmsnorm_amd" / "csrc"
+    bad_dir.mkdir(parents=True)
+    (bad_dir / "index_map.h").write_text(src.replace(old, new))
+    tests_dir = tmp_path / "tests"
+    tests_dir.mkdir()
+    shutil.copy(os.path.join(HERE, "fifo_slice_check.cpp"), tests_dir)
+    exe = str(tmp_path / "bad_slice_check")
+    subprocess.run(["g++", "-std=c++17", "-O2", "-o", exe,
+                    str(tests_dir / "fifo_slice_check.cpp")], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 1 and "FAIL" in r.stdout
