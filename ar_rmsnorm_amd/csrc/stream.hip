@@ -768,8 +768,8 @@ __device__ void consume_ll(const StreamArgs &a, int c, int pair, int p, int64_t 
 
 // ---------------------------------------------------------------------------
 // LL with whole steps per batch.  With several pairs per channel a pair's
-// slice of NCCL's 32 KiB LL step is 512-1,024 lines, a quarter of a batch or
-// less, so a batch kept inside one step left most lanes one line in flight
+// slice of NCCL's 32 KiB LL step is 512-2,048 lines, half a batch or less,
+// so a batch kept inside one step left lanes one or a few lines in flight
 // per round trip.  When the host sets batch_steps S > 1, a batch is S
 // consecutive whole steps of the pair instead: lane slot v = u * T + lane
 // carries line v mod L of the batch's step v / L (fifo_batch_slot; L is the
@@ -974,8 +974,13 @@ __device__ void consume_ll_steps(const StreamArgs &a, int c, int pair, int p, in
         if (!close_step(a, p, first + (uint64_t)(j0 + b.n_in - 1), failed))
             return;
         const LLBatch nb = ll_batch<T>(a, m, s0, first, nj);
+        // With the producer ahead, 1,024-lane workgroups load the next
+        // batch before delivering this one; 512-lane ones (twice the lines
+        // per lane) always deliver first, which keeps them in their
+        // registers.
+        const bool load_first = T == kWideThreads && ahead;
         u32x4 nv[kBatchOf<T>], nlv[kBatchOf<T>];
-        if (more && ahead)
+        if (more && load_first)
             ll_steps_load<T, LOCAL>(a, m, nb, nv, nlv);
         if (!failed) {
 #pragma unroll
@@ -984,7 +989,7 @@ __device__ void consume_ll_steps(const StreamArgs &a, int c, int pair, int p, in
                     deliver<LOCAL>(a, ll_word(a, m, b, u), 2, u32x4{v[u].x, v[u].z, 0u, 0u},
                                    lv[u]);
         }
-        if (more && !ahead)
+        if (more && !load_first)
             ll_steps_load<T, LOCAL>(a, m, nb, nv, nlv);
         if (!more)
             return;
@@ -1135,8 +1140,10 @@ __device__ void consume_simple(const StreamArgs &a, int c, int pair, int p, int6
 // block q of either half is pair q mod pairs of channel q / pairs.  Without
 // a local addend the kernel keeps to 128 VGPRs (4 wavefronts per SIMD), so
 // two workgroups fit on a CU and up to 256 channels can run at once; with one
-// it has two wavefronts per SIMD.
-template <int T, int PROTO, bool LOCAL>
+// it has two wavefronts per SIMD.  STEPS (LL only) selects the whole-step
+// batch paths, a kernel of its own so that the one-step-batch kernel keeps
+// its registers and code.
+template <int T, int PROTO, bool LOCAL, bool STEPS = false>
 __global__ __launch_bounds__(T, T == kWideThreads || !LOCAL ? 4 : 2) void stream_kernel(StreamArgs a)
 {
     __shared__ Shared sh;
@@ -1159,21 +1166,15 @@ __global__ __launch_bounds__(T, T == kWideThreads || !LOCAL ? 4 : 2) void stream
     const int64_t s0 = (int64_t)c * a.total_steps / a.channels;
     const int64_t s1 = (int64_t)(c + 1) * a.total_steps / a.channels;
     if (producer) {
-        if constexpr (PROTO == 0 && T == kWideThreads) {
-            if (a.batch_steps > 1) {
-                produce_ll_steps<T>(a, c, pair, p, s0, s1 - s0, first, &sh);
-                return;
-            }
-        }
-        produce<T, PROTO>(a, c, pair, p, s0, s1 - s0, first, &sh);
+        if constexpr (PROTO == 0 && STEPS)
+            produce_ll_steps<T>(a, c, pair, p, s0, s1 - s0, first, &sh);
+        else
+            produce<T, PROTO>(a, c, pair, p, s0, s1 - s0, first, &sh);
         return;
     }
-    if constexpr (PROTO == 0 && T == kWideThreads) {
-        if (a.batch_steps > 1)
-            consume_ll_steps<T, LOCAL>(a, c, pair, p, s0, s1 - s0, first);
-        else
-            consume_ll<T, LOCAL>(a, c, pair, p, s0, s1 - s0, first);
-    } else if (PROTO == 0)
+    if constexpr (PROTO == 0 && STEPS)
+        consume_ll_steps<T, LOCAL>(a, c, pair, p, s0, s1 - s0, first);
+    else if constexpr (PROTO == 0)
         consume_ll<T, LOCAL>(a, c, pair, p, s0, s1 - s0, first);
     else if (PROTO == 1)
         consume_ll128<T, LOCAL>(a, c, pair, p, s0, s1 - s0, first, &sh);
@@ -1193,8 +1194,11 @@ __global__ __launch_bounds__(T, T == kWideThreads || !LOCAL ? 4 : 2) void stream
 }
 
 template <int T>
-static const void *stream_fn_t(int proto, bool local)
+static const void *stream_fn_t(int proto, bool local, bool steps)
 {
+    if (proto == 0 && steps)
+        return local ? reinterpret_cast<const void *>(&stream_kernel<T, 0, true, true>)
+                     : reinterpret_cast<const void *>(&stream_kernel<T, 0, false, true>);
     if (local)
         return proto == 0   ? reinterpret_cast<const void *>(&stream_kernel<T, 0, true>)
                : proto == 1 ? reinterpret_cast<const void *>(&stream_kernel<T, 1, true>)
@@ -1204,20 +1208,32 @@ static const void *stream_fn_t(int proto, bool local)
                         : reinterpret_cast<const void *>(&stream_kernel<T, 2, false>);
 }
 
-static const void *stream_fn(int proto, bool local, bool wide)
+static const void *stream_fn(int proto, bool local, bool wide, bool steps)
 {
-    return wide ? stream_fn_t<kWideThreads>(proto, local) : stream_fn_t<kNarrowThreads>(proto, local);
+    return wide ? stream_fn_t<kWideThreads>(proto, local, steps)
+                : stream_fn_t<kNarrowThreads>(proto, local, steps);
 }
 
+// Workgroups of the kernel the call may launch that fit on the device at
+// once; for LL the smaller count of its two kernels, since the pair count
+// that depends on it also decides which of them runs.
 hipError_t fifo_stream_resident_workgroups(int proto, bool local, bool wide, int *workgroups)
 {
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess)
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int lanes = wide ? kWideThreads : kNarrowThreads;
     if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, stream_fn(proto, local, wide), wide ? kWideThreads : kNarrowThreads, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stream_fn(proto, local, wide, false),
+                                                         lanes, 0);
+    if (e == hipSuccess && proto == 0) {
+        int steps_per_cu = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&steps_per_cu,
+                                                         stream_fn(proto, local, wide, true), lanes, 0);
+        if (steps_per_cu < per_cu)
+            per_cu = steps_per_cu;
+    }
     *workgroups = e == hipSuccess ? cus * per_cu : 0;
     return e;
 }
@@ -1248,7 +1264,9 @@ hipError_t launch_fifo_stream(int proto, const float *src, const float *local, f
         const int64_t full = proto == 0 ? step_bytes / 8 : proto == 1 ? step_bytes / 120 * 8
                                                                      : step_bytes / 16;
         a.span = fifo_span(full, proto == 1 ? 16 : 1, pairs);
-        a.batch_steps = proto == 0 && wide && 8 * wire_bytes <= (int64_t)INT32_MAX
+        // whole-step batches only pay where a channel carries several steps
+        a.batch_steps = proto == 0 && a.steps_per_channel >= 2 &&
+                                8 * wire_bytes <= (int64_t)INT32_MAX
                             ? fifo_batch_steps(a.span, kPerBatch, kMaxBatchSteps)
                             : 1;
     }
@@ -1256,7 +1274,8 @@ hipError_t launch_fifo_stream(int proto, const float *src, const float *local, f
     a.first_step = first_step;
     a.max_spins = max_spins;
     void *args[] = {&a};
-    return hipLaunchKernel(stream_fn(proto, local != nullptr, wide), dim3(2 * channels * pairs),
+    return hipLaunchKernel(stream_fn(proto, local != nullptr, wide, a.batch_steps > 1),
+                           dim3(2 * channels * pairs),
                            dim3(wide ? kWideThreads : kNarrowThreads), args, 0, s);
 }
 
