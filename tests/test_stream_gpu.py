@@ -215,6 +215,39 @@ def test_stream_producers_and_consumers_on_different_xcds(gpu, name, step, with_
     del g
 
 
+# LL configurations whose pairs get slices of at most half a batch, so the
+# library runs them as batches of S whole steps, with the reasoning that
+# picks each case (the host takes as many pairs as fit, at most one per
+# 2,048 lines a channel carries, none with a slice under 512 lines):
+#   16 channels, 32 KiB steps (4,096 lines), 3 steps a channel and a
+#     20-byte last step: 8 pairs of 512 lines, S = 4 on 1,024-lane
+#     workgroups; the last step gives only pair 0 a slice
+#   32 channels, 40 KiB steps, 3 steps a channel and 28 bytes more: 4 pairs
+#     (all that fit) of 1,280 lines, S = 3
+#   64 channels, 32 KiB steps, 2 steps a channel and 12 bytes more: 2 pairs
+#     of 2,048 lines on 1,024-lane workgroups, S = 2
+#   128 channels, 32 KiB steps, 2 steps a channel: one 1,024-lane pair fits
+#     per channel, two 512-lane ones do: S = 2 on 512-lane workgroups
+# Each runs twice on the same rings (the second call from the stored step),
+# with and without a local addend where the addend still leaves S > 1.
+WHOLE_STEP_CASES = [
+    (16, 32768, 16 * 3 * 8192 + 5, True),
+    (32, 40960, 32 * 3 * 10240 + 7, True),
+    (64, 32768, 64 * 2 * 8192 + 3, False),
+    (128, 32768, 128 * 2 * 8192, False),
+]
+
+
+@pytest.mark.parametrize("channels,step,n,with_local", WHOLE_STEP_CASES)
+def test_stream_ll_batches_of_whole_steps(gpu, channels, step, n, with_local):
+    f = Fifo(ar.AR_PROTO_LL, step, channels, gpu)
+    for call in range(2):
+        src, local = synth.wire_payloads(2, n, [111, channels, call])
+        f.run(src, cont=call == 1)
+        if with_local:
+            f.run(src, local=local, cont=True)
+
+
 @pytest.mark.parametrize("case", range(12))
 def test_stream_seeded_random_configurations(gpu, case):
     """Seeded random protocol, channel count (1..200), step size, payload
