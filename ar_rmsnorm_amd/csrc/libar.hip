@@ -801,7 +801,57 @@ int fifo_pairs(int proto, int64_t step_bytes, int64_t n, int channels, int resid
                               512);
 }
 
+// Geometry and pairs: 1,024-lane workgroups with as many pairs as fit,
+// unless that leaves one pair per channel (or none) where 512-lane ones fit
+// at least two.  Measured on 16 Mi fp32 at NCCL's steps: at 128 channels two
+// narrow pairs beat one wide pair (LL 86 against 99 us, LL128 67 against
+// 71 us), at 32 channels four wide pairs beat eight narrow ones (LL 147
+// against 154 us).  Arguments already checked; n >= 1.
+ar_status_t fifo_plan(int proto, bool local, int64_t n, int channels, int64_t step_bytes,
+                      bool *wide, int *pairs)
+{
+    int wide_res = 0, narrow_res = 0;
+    int he = resident_workgroups(proto, local, true, &wide_res);
+    if (he == 0)
+        he = resident_workgroups(proto, local, false, &narrow_res);
+    if (he != 0)
+        return from_hip((hipError_t)he);
+    const int wide_pairs = fifo_pairs(proto, step_bytes, n, channels, wide_res);
+    const int narrow_pairs = fifo_pairs(proto, step_bytes, n, channels, narrow_res);
+    *wide = wide_pairs >= 2 || (wide_pairs == 1 && narrow_pairs < 2);
+    *pairs = *wide ? wide_pairs : narrow_pairs;
+    return *pairs < 1 ? AR_ERR_CAPACITY : AR_OK;
+}
+
 }  // namespace
+
+LIBAR_EXPORT ar_status_t ar_fifo_plan(int proto, int64_t n, int channels, int64_t step_bytes,
+                                      int with_local, int *lanes, int *pairs, int *batch_steps)
+{
+    if (lanes)
+        *lanes = 0;
+    if (pairs)
+        *pairs = 0;
+    if (batch_steps)
+        *batch_steps = 0;
+    if (ar_fifo_step_wire_bytes(proto, step_bytes) == 0 || n < 0 || n > kMaxElems ||
+        channels < 1 || channels > AR_FIFO_MAX_CHANNELS)
+        return AR_ERR_ARG;
+    if (n == 0)
+        return AR_OK;
+    bool wide = false;
+    int p = 0;
+    const ar_status_t ps = fifo_plan(proto, with_local != 0, n, channels, step_bytes, &wide, &p);
+    if (ps != AR_OK)
+        return ps;
+    if (lanes)
+        *lanes = wide ? 1024 : 512;
+    if (pairs)
+        *pairs = p;
+    if (batch_steps)
+        *batch_steps = ar::fifo_stream_batch_steps(proto, step_bytes, n, channels, p);
+    return AR_OK;
+}
 
 LIBAR_EXPORT ar_status_t ar_fifo_stream(int proto, const float *src, const float *local,
                                         float *out, int64_t n, void *fifo, uint64_t *counters,
@@ -837,24 +887,12 @@ LIBAR_EXPORT ar_status_t ar_fifo_stream(int proto, const float *src, const float
         return AR_ERR_ARG;
     if (n == 0)
         return AR_OK;
-    // Geometry and pairs: 1,024-lane workgroups with as many pairs as fit,
-    // unless that leaves one pair per channel (or none) where 512-lane ones
-    // fit at least two.  Measured on 16 Mi fp32 at NCCL's steps: at 128
-    // channels two narrow pairs beat one wide pair (LL 86 against 99 us,
-    // LL128 67 against 71 us), at 32 channels four wide pairs beat eight
-    // narrow ones (LL 147 against 154 us).
-    int wide_res = 0, narrow_res = 0;
-    int he = resident_workgroups(proto, local != nullptr, true, &wide_res);
-    if (he == 0)
-        he = resident_workgroups(proto, local != nullptr, false, &narrow_res);
-    if (he != 0)
-        return from_hip((hipError_t)he);
-    const int wide_pairs = fifo_pairs(proto, step_bytes, n, channels, wide_res);
-    const int narrow_pairs = fifo_pairs(proto, step_bytes, n, channels, narrow_res);
-    const bool wide = wide_pairs >= 2 || (wide_pairs == 1 && narrow_pairs < 2);
-    const int pairs = wide ? wide_pairs : narrow_pairs;
-    if (pairs < 1)
-        return AR_ERR_CAPACITY;
+    bool wide = false;
+    int pairs = 0;
+    const ar_status_t ps = fifo_plan(proto, local != nullptr, n, channels, step_bytes, &wide,
+                                     &pairs);
+    if (ps != AR_OK)
+        return ps;
     return from_hip(ar::launch_fifo_stream(proto, src, local, out, n, fifo, counters, channels,
                                            step_bytes, wire, first_step,
                                            first_step == AR_FIFO_CONTINUE, max_spins, errors,

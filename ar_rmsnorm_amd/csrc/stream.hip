@@ -1214,6 +1214,28 @@ static const void *stream_fn(int proto, bool local, bool wide, bool steps)
                 : stream_fn_t<kNarrowThreads>(proto, local, steps);
 }
 
+int64_t fifo_full_items(int proto, int64_t step_bytes)
+{
+    return proto == 0 ? step_bytes / 8 : proto == 1 ? step_bytes / 120 * 8 : step_bytes / 16;
+}
+
+// Whole steps per LL batch (fifo_batch_steps) for a call with these
+// arguments and pair count; 1 for the other protocols, for channels of one
+// step (where whole-step batches do not pay), and for rings of 2 GiB or more
+// (one buffer descriptor addresses a batch's slots).
+int fifo_stream_batch_steps(int proto, int64_t step_bytes, int64_t n, int channels, int pairs)
+{
+    if (proto != 0 || n <= 0 || channels < 1 || pairs < 1)
+        return 1;
+    const int64_t total = (4 * n + step_bytes - 1) / step_bytes;
+    const int64_t per_channel = (total + channels - 1) / channels;
+    const int64_t wire_bytes = step_bytes / 8 * 16;
+    if (per_channel < 2 || 8 * wire_bytes > (int64_t)INT32_MAX)
+        return 1;
+    return fifo_batch_steps(fifo_span(fifo_full_items(proto, step_bytes), 1, pairs), kPerBatch,
+                            kMaxBatchSteps);
+}
+
 // Workgroups of the kernel the call may launch that fit on the device at
 // once; for LL the smaller count of its two kernels, since the pair count
 // that depends on it also decides which of them runs.
@@ -1260,16 +1282,8 @@ hipError_t launch_fifo_stream(int proto, const float *src, const float *local, f
     a.steps_per_channel = (a.total_steps + channels - 1) / channels;
     a.channels = channels;
     a.pairs = pairs;
-    {
-        const int64_t full = proto == 0 ? step_bytes / 8 : proto == 1 ? step_bytes / 120 * 8
-                                                                     : step_bytes / 16;
-        a.span = fifo_span(full, proto == 1 ? 16 : 1, pairs);
-        // whole-step batches only pay where a channel carries several steps
-        a.batch_steps = proto == 0 && a.steps_per_channel >= 2 &&
-                                8 * wire_bytes <= (int64_t)INT32_MAX
-                            ? fifo_batch_steps(a.span, kPerBatch, kMaxBatchSteps)
-                            : 1;
-    }
+    a.span = fifo_span(fifo_full_items(proto, step_bytes), proto == 1 ? 16 : 1, pairs);
+    a.batch_steps = fifo_stream_batch_steps(proto, step_bytes, n, channels, pairs);
     a.from_state = from_state ? 1 : 0;
     a.first_step = first_step;
     a.max_spins = max_spins;

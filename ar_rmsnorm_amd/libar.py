@@ -47,7 +47,7 @@ EXPORTS = (
     "ar_lamport_oneshot_residual_rmsnorm", "ll_pack", "ll_unpack_reduce", "ll128_pack",
     "ll128_unpack_reduce", "ll_lines", "ll128_lines", "ll_fifo_bytes",
     "ll128_fifo_bytes", "ll_default_step_lines", "ll128_default_step_lines",
-    "ar_fifo_stream", "ar_fifo_step_wire_bytes", "ar_fifo_steps_per_channel",
+    "ar_fifo_stream", "ar_fifo_step_wire_bytes", "ar_fifo_steps_per_channel", "ar_fifo_plan",
     "ar_fifo_counter_words", "ar_lamport_next_flag", "ar_fused_prefers_two_shot", "ar_copy",
     "ar_reduce_2stage_noalloc", "ar_lamport_all_ranks_residual_rmsnorm",
 )
@@ -117,6 +117,9 @@ _lib.ar_fifo_step_wire_bytes.argtypes = [_int, _i64]
 _lib.ar_fifo_step_wire_bytes.restype = _i64
 _lib.ar_fifo_steps_per_channel.argtypes = [_i64, _i64, _int]
 _lib.ar_fifo_steps_per_channel.restype = _i64
+_pint = ctypes.POINTER(ctypes.c_int)
+_lib.ar_fifo_plan.argtypes = [_int, _i64, _int, _i64, _int, _pint, _pint, _pint]
+_lib.ar_fifo_plan.restype = _int
 _lib.ar_fifo_counter_words.argtypes = [_int]
 _lib.ar_fifo_counter_words.restype = _i64
 
@@ -436,6 +439,17 @@ def ar_fifo_step_wire_bytes(proto: int, step_bytes: int) -> int:
 
 def ar_fifo_steps_per_channel(n: int, step_bytes: int, channels: int) -> int:
     return _lib.ar_fifo_steps_per_channel(n, step_bytes, channels)
+
+
+def ar_fifo_plan(proto: int, n: int, channels: int, step_bytes: int,
+                 with_local: bool = False):
+    """(lanes per workgroup, pairs per channel, whole steps per LL batch)
+    that ar_fifo_stream picks for these arguments on the current device."""
+    lanes, pairs, steps = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    _check(_lib.ar_fifo_plan(proto, n, channels, step_bytes, 1 if with_local else 0,
+                             ctypes.byref(lanes), ctypes.byref(pairs), ctypes.byref(steps)),
+           "ar_fifo_plan")
+    return lanes.value, pairs.value, steps.value
 
 
 def ar_fifo_counter_words(channels: int) -> int:

@@ -1130,9 +1130,12 @@ def main():
                         or None)
                 t_s = r["us_per_call"] * 1e-6
                 torch.cuda.synchronize()
+                lanes, pairs, bsteps = ar.ar_fifo_plan(proto, n_msg, ch, step)
                 r.update({"channels": ch,
                           "step_bytes": step, "payload_GBps": round(4 * n_msg / t_s / 1e9, 1),
                           "ring_bytes_written": ring_bytes,
+                          "plan": {"lanes": lanes, "pairs_per_channel": pairs,
+                                   "steps_per_batch": bsteps},
                           "failed_waits": int(errs.item())})
                 del fifo, cnt, calls
         # message-size sweep at 32 channels: where LL, LL128 and Simple cross.

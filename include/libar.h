@@ -508,6 +508,21 @@ int64_t ar_fifo_step_wire_bytes(int proto, int64_t step_bytes);
  * ceil(ceil(4n / step_bytes) / channels) (0 for invalid arguments). */
 int64_t ar_fifo_steps_per_channel(int64_t n, int64_t step_bytes, int channels);
 
+/* The launch shape ar_fifo_stream picks for these arguments on the current
+ * device, without launching anything: *lanes = lanes per workgroup (1,024
+ * or 512), *pairs = producer/consumer pairs per channel (P above),
+ * *batch_steps = whole ring steps an LL batch spans (1 when batches stay
+ * inside one step, and for LL128 and Simple).  Any output may be NULL; all
+ * are set to 0 first, and stay 0 for n = 0 (no launch).  with_local != 0
+ * plans for a call with a local addend.  Not an operation of the pages: it
+ * reports the one-device choices ([NCCL14] "prerequisite mental model"
+ * fixes the ring and steps, not how workgroups share them).
+ *   AR_ERR_ARG       proto, step_bytes, n or channels as ar_fifo_stream
+ *   AR_ERR_CAPACITY  not one pair per channel fits
+ *   AR_ERR_HIP       the device could not be queried */
+ar_status_t ar_fifo_plan(int proto, int64_t n, int channels, int64_t step_bytes,
+                         int with_local, int *lanes, int *pairs, int *batch_steps);
+
 /*
  * Plain device copy, dst[0 .. nbytes) = src[0 .. nbytes), one 16-byte load
  * and store per lane.  Not an operation of the pages: it is the

@@ -205,6 +205,20 @@ def test_stream_argument_errors():
     assert st(f, LL, A, B, C, D, 2, 1024, 0, 8, E, None, 0, 0) == ar.AR_OK       # n = 0
 
 
+@cpu_only
+def test_stream_plan_argument_errors():
+    """ar_fifo_plan refuses what ar_fifo_stream refuses before asking the
+    device anything, and plans nothing for an empty call."""
+    f = ar.ar_fifo_plan
+    LL = ar.AR_PROTO_LL
+    for args in ((3, 1024, 2, 1024), (LL, 1024, 0, 1024), (LL, 1024, 257, 1024),
+                 (LL, 1024, 2, 1020), (LL, -1, 2, 1024), (ar.AR_PROTO_LL128, 1024, 2, 1000)):
+        assert st(f, *args) == ar.AR_ERR_ARG, args
+    assert f(LL, 0, 2, 1024) == (0, 0, 0)
+    # the outputs are optional
+    assert ar._lib.ar_fifo_plan(LL, 0, 2, 1024, 0, None, None, None) == ar.AR_OK
+
+
 def test_size_limits_of_the_wire_helpers():
     big = (1 << 62) + 3                     # 4n would not fit in 64 bits
     assert ar.ll_lines(1 << 40) == (1 << 39) and ar.ll_lines((1 << 40) + 1) == 0

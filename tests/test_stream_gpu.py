@@ -97,6 +97,23 @@ def test_stream_bench_configurations(gpu, name, step, channels):
     f.run(src, cont=True)
 
 
+def test_stream_plans_of_the_bench_rows(gpu):
+    """The launch shapes the bench rows run with (lanes, pairs per channel,
+    whole steps per LL batch) on a 256-CU MI355X: 32 channels take four
+    1,024-lane pairs, 128 channels two 512-lane pairs; LL spans 4 and 2
+    steps per batch there, one-step messages stay in one step."""
+    n = synth.WIRE["n"]
+    want = {("ll", 32): (1024, 4, 4), ("ll", 128): (512, 2, 2),
+            ("ll128", 32): (1024, 4, 1), ("ll128", 128): (512, 2, 1),
+            ("simple", 32): (1024, 4, 1), ("simple", 128): (512, 2, 1)}
+    steps = {"ll": 32768, "ll128": 576000, "simple": 524288}
+    for (name, ch), plan in want.items():
+        assert ar.ar_fifo_plan(PROTOS[name], n, ch, steps[name]) == plan, (name, ch)
+    # 8 KiB over 32 channels at the 32 KiB step: one step on one channel,
+    # one pair, one step per batch
+    assert ar.ar_fifo_plan(ar.AR_PROTO_LL, 2048, 32, 32768) == (1024, 1, 1)
+
+
 @pytest.mark.parametrize("name,step", [("ll", 1024), ("ll128", 1200), ("simple", 1024)])
 def test_stream_256_channels(gpu, name, step):
     """256 channels need two workgroups per CU: the 512-lane geometry where
@@ -230,16 +247,20 @@ def test_stream_producers_and_consumers_on_different_xcds(gpu, name, step, with_
 #     per channel, two 512-lane ones do: S = 2 on 512-lane workgroups
 # Each runs twice on the same rings (the second call from the stored step),
 # with and without a local addend where the addend still leaves S > 1.
+# (channels, step, n, with_local, the plan: lanes, pairs, steps per batch)
 WHOLE_STEP_CASES = [
-    (16, 32768, 16 * 3 * 8192 + 5, True),
-    (32, 40960, 32 * 3 * 10240 + 7, True),
-    (64, 32768, 64 * 2 * 8192 + 3, False),
-    (128, 32768, 128 * 2 * 8192, False),
+    (16, 32768, 16 * 3 * 8192 + 5, True, (1024, 8, 4)),
+    (32, 40960, 32 * 3 * 10240 + 7, True, (1024, 4, 3)),
+    (64, 32768, 64 * 2 * 8192 + 3, False, (1024, 2, 2)),
+    (128, 32768, 128 * 2 * 8192, False, (512, 2, 2)),
 ]
 
 
-@pytest.mark.parametrize("channels,step,n,with_local", WHOLE_STEP_CASES)
-def test_stream_ll_batches_of_whole_steps(gpu, channels, step, n, with_local):
+@pytest.mark.parametrize("channels,step,n,with_local,plan", WHOLE_STEP_CASES)
+def test_stream_ll_batches_of_whole_steps(gpu, channels, step, n, with_local, plan):
+    assert ar.ar_fifo_plan(ar.AR_PROTO_LL, n, channels, step) == plan
+    if with_local:
+        assert ar.ar_fifo_plan(ar.AR_PROTO_LL, n, channels, step, with_local=True) == plan
     f = Fifo(ar.AR_PROTO_LL, step, channels, gpu)
     for call in range(2):
         src, local = synth.wire_payloads(2, n, [111, channels, call])
