@@ -806,7 +806,12 @@ int fifo_pairs(int proto, int64_t step_bytes, int64_t n, int channels, int resid
 // at least two.  Measured on 16 Mi fp32 at NCCL's steps: at 128 channels two
 // narrow pairs beat one wide pair (LL 86 against 99 us, LL128 67 against
 // 71 us), at 32 channels four wide pairs beat eight narrow ones (LL 147
-// against 154 us).  Arguments already checked; n >= 1.
+// against 154 us, with batches inside one step).  LL with batches of whole
+// steps also takes the 512-lane form where it gives at least twice the
+// pairs and every channel carries 32 steps or more: 16 Mi fp32 at 64
+// channels 101 -> 83 us, at 48 channels 107 -> 94 us, at 32 channels 95 ->
+// 92 us; with fewer steps per channel (4 Mi over 32 channels) the wider
+// form stays faster (32 against 36 us).  Arguments already checked; n >= 1.
 ar_status_t fifo_plan(int proto, bool local, int64_t n, int channels, int64_t step_bytes,
                       bool *wide, int *pairs)
 {
@@ -819,6 +824,9 @@ ar_status_t fifo_plan(int proto, bool local, int64_t n, int channels, int64_t st
     const int wide_pairs = fifo_pairs(proto, step_bytes, n, channels, wide_res);
     const int narrow_pairs = fifo_pairs(proto, step_bytes, n, channels, narrow_res);
     *wide = wide_pairs >= 2 || (wide_pairs == 1 && narrow_pairs < 2);
+    if (proto == AR_PROTO_LL && narrow_pairs >= 2 && narrow_pairs >= 2 * wide_pairs &&
+        ar_fifo_steps_per_channel(n, step_bytes, channels) >= 32)
+        *wide = false;
     *pairs = *wide ? wide_pairs : narrow_pairs;
     return *pairs < 1 ? AR_ERR_CAPACITY : AR_OK;
 }

@@ -100,10 +100,11 @@ def test_stream_bench_configurations(gpu, name, step, channels):
 def test_stream_plans_of_the_bench_rows(gpu):
     """The launch shapes the bench rows run with (lanes, pairs per channel,
     whole steps per LL batch) on a 256-CU MI355X: 32 channels take four
-    1,024-lane pairs, 128 channels two 512-lane pairs; LL spans 4 and 2
-    steps per batch there, one-step messages stay in one step."""
+    1,024-lane pairs, except LL, whose 64 steps per channel take eight
+    512-lane pairs; 128 channels two 512-lane pairs; LL spans 4 and 2 steps
+    per batch there, one-step messages stay in one step."""
     n = synth.WIRE["n"]
-    want = {("ll", 32): (1024, 4, 4), ("ll", 128): (512, 2, 2),
+    want = {("ll", 32): (512, 8, 4), ("ll", 128): (512, 2, 2),
             ("ll128", 32): (1024, 4, 1), ("ll128", 128): (512, 2, 1),
             ("simple", 32): (1024, 4, 1), ("simple", 128): (512, 2, 1)}
     steps = {"ll": 32768, "ll128": 576000, "simple": 524288}
@@ -112,6 +113,10 @@ def test_stream_plans_of_the_bench_rows(gpu):
     # 8 KiB over 32 channels at the 32 KiB step: one step on one channel,
     # one pair, one step per batch
     assert ar.ar_fifo_plan(ar.AR_PROTO_LL, 2048, 32, 32768) == (1024, 1, 1)
+    # 4 Mi fp32 over 32 channels: 16 steps a channel keep the wider form
+    assert ar.ar_fifo_plan(ar.AR_PROTO_LL, 1 << 22, 32, 32768) == (1024, 4, 4)
+    # 16 Mi fp32 over 64 channels: 32 steps a channel, four 512-lane pairs
+    assert ar.ar_fifo_plan(ar.AR_PROTO_LL, 1 << 24, 64, 32768) == (512, 4, 4)
 
 
 @pytest.mark.parametrize("name,step", [("ll", 1024), ("ll128", 1200), ("simple", 1024)])
