@@ -478,7 +478,9 @@ ar_status_t ll128_unpack_reduce(const void *const *fifos, int W, float *out,
  *               overlap among the buffers                 else AR_ERR_ARG
  * The 2 * channels * P workgroups must be resident together.  They have
  * 1,024 lanes, or 512 when the device holds two or more pairs per channel
- * of those but only one of the wider ones; AR_ERR_CAPACITY if it cannot hold
+ * of those but only one of the wider ones (for LL also when the 512-lane
+ * form gives at least twice the pairs and every channel carries 32 steps
+ * or more; ar_fifo_plan reports the choice); AR_ERR_CAPACITY if it cannot hold
  * one pair per channel in either form (with local, more than 128 channels
  * on MI355X).  Work from other streams that holds
  * compute units while a call runs can delay a consumer or producer; the
