@@ -311,11 +311,17 @@ def counter_summary(fetch_dir: str, write_dir: str) -> str:
     def groups(d):
         # per launch shape, split into segments: runs of that shape not
         # interrupted by another kernel of the library (each bench row's
-        # dispatches form one), labelled #1, #2, ... in dispatch order
+        # dispatches form one; an eager bench run also starts every timed
+        # row with a one-workgroup copy, which ends the previous row's run
+        # and is left out of the table), labelled #1, #2, ... in dispatch
+        # order
         g, last, seen = {}, None, {}
         for _, name, grid, wg, v in d[:-3]:
             key = (name, grid, wg)
             if not name.startswith("ar::"):
+                continue
+            if name == "ar::copy_kernel" and grid == 256:
+                last = None
                 continue
             if key != last:
                 seen[key] = seen.get(key, 0) + 1
@@ -392,9 +398,21 @@ def main():
     def to_dev(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
 
+    marker = []
+
+    def row_marker():
+        """One 16-byte library copy (a one-workgroup copy_kernel dispatch)
+        ahead of every eagerly timed row, so that a counter summary can tell
+        apart consecutive rows that share a launch shape."""
+        if not marker:
+            marker.extend(torch.zeros(2, 4, dtype=torch.int32, device=dev).unbind(0))
+        ar.ar_copy(marker[0], marker[1])
+
     def graph_time(fns, steps, warmup):
         """Average ms per call of the calls fns[i % len(fns)], timed over a
         HIP graph of `steps` back-to-back launches replayed between events."""
+        if args.eager:
+            row_marker()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
