@@ -250,6 +250,11 @@ def test_stream_producers_and_consumers_on_different_xcds(gpu, name, step, with_
 #     of 2,048 lines on 1,024-lane workgroups, S = 2
 #   128 channels, 32 KiB steps, 2 steps a channel: one 1,024-lane pair fits
 #     per channel, two 512-lane ones do: S = 2 on 512-lane workgroups
+#   48 channels, 32 KiB steps, 33 steps a channel and a 44-byte step more
+#     (channel 0 carries 34): two 1,024-lane pairs fit per channel, five
+#     512-lane ones do, and with 32 steps or more a channel LL takes the
+#     narrow form: 5 pairs of 820 lines (the last 816), S = 4; the short
+#     step gives only pair 0 a slice
 # Each runs twice on the same rings (the second call from the stored step),
 # with and without a local addend where the addend still leaves S > 1.
 # (channels, step, n, with_local, the plan: lanes, pairs, steps per batch)
@@ -258,6 +263,7 @@ WHOLE_STEP_CASES = [
     (32, 40960, 32 * 3 * 10240 + 7, True, (1024, 4, 3)),
     (64, 32768, 64 * 2 * 8192 + 3, False, (1024, 2, 2)),
     (128, 32768, 128 * 2 * 8192, False, (512, 2, 2)),
+    (48, 32768, 48 * 33 * 8192 + 11, False, (512, 5, 4)),
 ]
 
 
