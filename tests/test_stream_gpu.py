@@ -251,7 +251,7 @@ def test_stream_producers_and_consumers_on_different_xcds(gpu, name, step, with_
 #   128 channels, 32 KiB steps, 2 steps a channel: one 1,024-lane pair fits
 #     per channel, two 512-lane ones do: S = 2 on 512-lane workgroups
 #   48 channels, 32 KiB steps, 33 steps a channel and a 44-byte step more
-#     (channel 0 carries 34): two 1,024-lane pairs fit per channel, five
+#     (channel 47 carries 34): two 1,024-lane pairs fit per channel, five
 #     512-lane ones do, and with 32 steps or more a channel LL takes the
 #     narrow form: 5 pairs of 820 lines (the last 816), S = 4; the short
 #     step gives only pair 0 a slice
