@@ -25,7 +25,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 @pytest.fixture(scope="module")
-def checker(tmp_path_factory):
+def map_walk(tmp_path_factory):
     if shutil.which("g++") is None:
         pytest.skip("g++ not available")
     exe = str(tmp_path_factory.mktemp("imap") / "index_map_check")
@@ -41,23 +41,23 @@ def run(exe, *args):
 
 
 @pytest.mark.parametrize("threads", [256, 512])
-def test_cap_message_every_rank_and_stage(checker, threads):
-    out = run(checker, threads, 8, 524_288)
+def test_cap_message_every_rank_and_stage(map_walk, threads):
+    out = run(map_walk, threads, 8, 524_288)
     assert "144 launches checked, 0 failures" in out     # 8 ranks x 3 stages x 6 widths
 
 
 @pytest.mark.parametrize("W", range(2, 9))
-def test_ragged_sizes_every_world_size(checker, W):
+def test_ragged_sizes_every_world_size(map_walk, W):
     sizes = [0, 1, W - 1, W, W + 1, 255 * W + W - 1, 256 * W, 257 * W + 1, 1024 * W + 3,
              8 * (8 * 300 + 5), 65_536 * W + W - 1]
     args = []
     for P in sizes:
         args += [W, P]
-    out = run(checker, 256, *args)
+    out = run(map_walk, 256, *args)
     assert f"{len(sizes) * W * 18} launches checked, 0 failures" in out
 
 
-def test_the_checker_catches_a_planted_out_of_range_map(checker, tmp_path):
+def test_the_map_walk_catches_a_planted_out_of_range_map(map_walk, tmp_path):
     """Plant an off-by-one in a copy of the map (the last shard's remainder
     given to every shard) and make sure the enumeration reports it."""
     src = open(os.path.join(HERE, "..", "ar_rmsnorm_amd", "csrc", "index_map.h")).read()
