@@ -49,10 +49,6 @@ hipError_t launch_lamport_all_ranks(const void *const *xs, void *const *comms, i
                                     uint32_t max_spins, uint32_t *bad, bool check_only,
                                     int *resident, hipStream_t s);
 
-// Producer/consumer pairs a channel can have; the counters hold a head and a
-// tail for each of them.
-constexpr int kFifoMaxPairs = 8;
-
 // One launch of 2 * channels * pairs workgroups (producers, then consumers),
 // all of which the caller has checked can be resident at once in the chosen
 // geometry (wide: 1,024 lanes per workgroup, else 512).
@@ -61,11 +57,6 @@ hipError_t launch_fifo_stream(int proto, const float *src, const float *local, f
                               int64_t step_bytes, int64_t wire_bytes, uint64_t first_step,
                               bool from_state, uint32_t max_spins, uint32_t *errors,
                               bool wide, int pairs, hipStream_t s);
-// Items (LL lines, LL128 or Simple 16-byte chunks) of a full step.
-int64_t fifo_full_items(int proto, int64_t step_bytes);
-// Whole steps per LL batch the launch uses for these arguments (1 when
-// batches stay inside one step).
-int fifo_stream_batch_steps(int proto, int64_t step_bytes, int64_t n, int channels, int pairs);
 // Workgroups of the streaming kernel, in the given geometry, that the current
 // device holds at once.
 hipError_t fifo_stream_resident_workgroups(int proto, bool local, bool wide, int *workgroups);

@@ -11,6 +11,7 @@
 
 #include "index_map.h"
 #include "launch.h"
+#include "stream_plan.h"
 
 #define LIBAR_EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -738,11 +739,12 @@ LIBAR_EXPORT int64_t ar_fifo_steps_per_channel(int64_t n, int64_t step_bytes, in
 {
     if (n <= 0 || n > kMaxElems || step_bytes <= 0 || channels < 1)
         return 0;
-    const int64_t total = (4 * n + step_bytes - 1) / step_bytes;
-    return (total + channels - 1) / channels;
+    return ar::fifo_steps_per_channel(n, step_bytes, channels);
 }
 
 static_assert(ar::kFifoMaxPairs == AR_FIFO_MAX_PAIRS, "pairs per channel");
+static_assert(AR_PROTO_LL == 0 && AR_PROTO_LL128 == 1 && AR_PROTO_SIMPLE == 2,
+              "protocol numbers of the streaming plan");
 
 LIBAR_EXPORT int64_t ar_fifo_counter_words(int channels)
 {
@@ -775,43 +777,24 @@ int resident_workgroups(int proto, bool local, bool wide, int *workgroups)
     return (int)e;
 }
 
-// Producer/consumer pairs per channel (ar::fifo_pairs_for) for a full step
-// of this protocol's items: LL lines, LL128 16-byte chunks (whole line pairs
-// per slice), Simple 16-byte chunks.  A pair's slice of a full step is at
-// least 512 items, and a channel gets one pair per 2,048 items it carries
-// in the call (at least one): extra pairs only add workgroups when there is
-// little to move (32 channels, LL: an 8 KiB message took 7.5 us with four
+// Geometry and pairs (ar::fifo_plan_pairs, ar::fifo_plan_wide) from the
+// workgroups of each size the device holds at once.  A pair's slice of a
+// full step is at least 512 items, and a channel gets one pair per 2,048
+// items it carries in the call: extra pairs only add workgroups when there
+// is little to move (32 channels, LL: an 8 KiB message took 7.5 us with four
 // pairs against 5.1 us with one, a 512 KiB one 8.2 against 6.4 us, while a
-// 16 MiB one took 140 against 195 us).
-int fifo_pairs(int proto, int64_t step_bytes, int64_t n, int channels, int resident)
-{
-    const int64_t items = proto == AR_PROTO_LL      ? step_bytes / 8
-                          : proto == AR_PROTO_LL128 ? step_bytes / 120 * 8
-                                                    : step_bytes / 16;
-    const int64_t steps = ar_fifo_steps_per_channel(n, step_bytes, channels);
-    int64_t bytes = steps * step_bytes;                 // payload of the busiest channel
-    if (bytes > 4 * n)
-        bytes = 4 * n;
-    const int64_t per_item = proto == AR_PROTO_LL ? 8 : proto == AR_PROTO_LL128 ? 15 : 16;
-    int64_t by_work = bytes / per_item / 2048;
-    if (by_work < 1)
-        by_work = 1;
-    const int most = by_work < AR_FIFO_MAX_PAIRS ? (int)by_work : AR_FIFO_MAX_PAIRS;
-    return ar::fifo_pairs_for(items, proto == AR_PROTO_LL128 ? 16 : 1, channels, resident, most,
-                              512);
-}
-
-// Geometry and pairs: 1,024-lane workgroups with as many pairs as fit,
-// unless that leaves one pair per channel (or none) where 512-lane ones fit
-// at least two.  Measured on 16 Mi fp32 at NCCL's steps: at 128 channels two
-// narrow pairs beat one wide pair (LL 86 against 99 us, LL128 67 against
-// 71 us), at 32 channels four wide pairs beat eight narrow ones (LL 147
-// against 154 us, with batches inside one step).  LL with batches of whole
-// steps also takes the 512-lane form where it gives at least twice the
-// pairs and every channel carries 32 steps or more: 16 Mi fp32 at 64
-// channels 101 -> 83 us, at 48 channels 107 -> 94 us, at 32 channels 95 ->
-// 92 us; with fewer steps per channel (4 Mi over 32 channels) the wider
-// form stays faster (32 against 36 us).  Arguments already checked; n >= 1.
+// 16 MiB one took 140 against 195 us).  1,024-lane workgroups take as many
+// pairs as fit, unless that leaves one pair per channel (or none) where
+// 512-lane ones fit at least two.  Measured on 16 Mi fp32 at NCCL's steps:
+// at 128 channels two narrow pairs beat one wide pair (LL 86 against 99 us,
+// LL128 67 against 71 us), at 32 channels four wide pairs beat eight narrow
+// ones (LL 147 against 154 us, with batches inside one step).  LL with
+// batches of whole steps also takes the 512-lane form where it gives at
+// least twice the pairs and every channel carries 32 steps or more: 16 Mi
+// fp32 at 64 channels 101 -> 83 us, at 48 channels 107 -> 94 us, at 32
+// channels 95 -> 92 us; with fewer steps per channel (4 Mi over 32
+// channels) the wider form stays faster (32 against 36 us).  Arguments
+// already checked; n >= 1.
 ar_status_t fifo_plan(int proto, bool local, int64_t n, int channels, int64_t step_bytes,
                       bool *wide, int *pairs)
 {
@@ -821,12 +804,10 @@ ar_status_t fifo_plan(int proto, bool local, int64_t n, int channels, int64_t st
         he = resident_workgroups(proto, local, false, &narrow_res);
     if (he != 0)
         return from_hip((hipError_t)he);
-    const int wide_pairs = fifo_pairs(proto, step_bytes, n, channels, wide_res);
-    const int narrow_pairs = fifo_pairs(proto, step_bytes, n, channels, narrow_res);
-    *wide = wide_pairs >= 2 || (wide_pairs == 1 && narrow_pairs < 2);
-    if (proto == AR_PROTO_LL && narrow_pairs >= 2 && narrow_pairs >= 2 * wide_pairs &&
-        ar_fifo_steps_per_channel(n, step_bytes, channels) >= 32)
-        *wide = false;
+    const int wide_pairs = ar::fifo_plan_pairs(proto, step_bytes, n, channels, wide_res);
+    const int narrow_pairs = ar::fifo_plan_pairs(proto, step_bytes, n, channels, narrow_res);
+    *wide = ar::fifo_plan_wide(proto, wide_pairs, narrow_pairs,
+                               ar::fifo_steps_per_channel(n, step_bytes, channels));
     *pairs = *wide ? wide_pairs : narrow_pairs;
     return *pairs < 1 ? AR_ERR_CAPACITY : AR_OK;
 }
@@ -857,7 +838,7 @@ LIBAR_EXPORT ar_status_t ar_fifo_plan(int proto, int64_t n, int channels, int64_
     if (pairs)
         *pairs = p;
     if (batch_steps)
-        *batch_steps = ar::fifo_stream_batch_steps(proto, step_bytes, n, channels, p);
+        *batch_steps = ar::fifo_plan_batch_steps(proto, step_bytes, n, channels, p);
     return AR_OK;
 }
 

@@ -71,6 +71,7 @@
 #include "device.h"
 #include "index_map.h"
 #include "launch.h"
+#include "stream_plan.h"
 
 namespace ar {
 
@@ -78,14 +79,14 @@ namespace ar {
 // 1,024 lanes with 4 items in flight each when the device holds 2 x channels
 // such workgroups at once, else 512 lanes with 8 each (two workgroups per CU,
 // up to 256 channels).  The wider one hides more of each batch's round trips.
-constexpr int64_t kPerBatch = 4096;
+constexpr int64_t kPerBatch = kFifoPerBatch;
 constexpr int kWideThreads = 1024;
 constexpr int kNarrowThreads = 512;
 template <int T>
 constexpr int kBatchOf = (int)(kPerBatch / T);   // items in flight per lane
 constexpr uint32_t kAbortCheck = 16;   // spins between looks at the error count
 constexpr int kMaxPairs = kFifoMaxPairs;      // producer/consumer pairs per channel
-constexpr int kMaxBatchSteps = 4;              // LL: whole steps per batch, 2 * 4 <= 8 slots
+constexpr int kMaxBatchSteps = kFifoMaxBatchSteps;   // LL: whole steps per batch
 
 struct StreamArgs {
     const uint32_t *src;    // n fp32 payload values (as words)
@@ -1214,28 +1215,6 @@ static const void *stream_fn(int proto, bool local, bool wide, bool steps)
                 : stream_fn_t<kNarrowThreads>(proto, local, steps);
 }
 
-int64_t fifo_full_items(int proto, int64_t step_bytes)
-{
-    return proto == 0 ? step_bytes / 8 : proto == 1 ? step_bytes / 120 * 8 : step_bytes / 16;
-}
-
-// Whole steps per LL batch (fifo_batch_steps) for a call with these
-// arguments and pair count; 1 for the other protocols, for channels of one
-// step (where whole-step batches do not pay), and for rings of 2 GiB or more
-// (one buffer descriptor addresses a batch's slots).
-int fifo_stream_batch_steps(int proto, int64_t step_bytes, int64_t n, int channels, int pairs)
-{
-    if (proto != 0 || n <= 0 || channels < 1 || pairs < 1)
-        return 1;
-    const int64_t total = (4 * n + step_bytes - 1) / step_bytes;
-    const int64_t per_channel = (total + channels - 1) / channels;
-    const int64_t wire_bytes = step_bytes / 8 * 16;
-    if (per_channel < 2 || 8 * wire_bytes > (int64_t)INT32_MAX)
-        return 1;
-    return fifo_batch_steps(fifo_span(fifo_full_items(proto, step_bytes), 1, pairs), kPerBatch,
-                            kMaxBatchSteps);
-}
-
 // Workgroups of the kernel the call may launch that fit on the device at
 // once; for LL the smaller count of its two kernels, since the pair count
 // that depends on it also decides which of them runs.
@@ -1283,7 +1262,7 @@ hipError_t launch_fifo_stream(int proto, const float *src, const float *local, f
     a.channels = channels;
     a.pairs = pairs;
     a.span = fifo_span(fifo_full_items(proto, step_bytes), proto == 1 ? 16 : 1, pairs);
-    a.batch_steps = fifo_stream_batch_steps(proto, step_bytes, n, channels, pairs);
+    a.batch_steps = fifo_plan_batch_steps(proto, step_bytes, n, channels, pairs);
     a.from_state = from_state ? 1 : 0;
     a.first_step = first_step;
     a.max_spins = max_spins;

@@ -241,7 +241,7 @@ def trace_summary(d: str) -> str:
 
 ALL_SOURCES = [os.path.join(ROOT, "ar_rmsnorm_amd", "csrc", f)
                for f in ("reduce.hip", "wire.hip", "stream.hip", "copy.hip", "device.h",
-                         "index_map.h")]
+                         "index_map.h", "stream_plan.h")]
 
 
 def all_source_hash() -> str:

@@ -81,7 +81,9 @@ def test_streaming_slices_cover_every_step(tmp_path):
     kernel and the host's pair choice use, and checks that the pairs of a
     channel cut every step (full, or a shorter last step) into disjoint,
     aligned pieces that cover it, each pair staying in its region of the
-    ring slot, and that the chosen pair count fits the device."""
+    ring slot, and that the chosen pair count fits the device; and that the
+    launch plan gives the shapes the measurements and GPU tests use on one
+    MI355X and, over a grid of calls, fits and leaves every pair a slice."""
     if shutil.which("g++") is None:
         pytest.skip("g++ not available")
     exe = str(tmp_path / "fifo_slice_check")
@@ -91,23 +93,36 @@ def test_streaming_slices_cover_every_step(tmp_path):
     assert out.endswith("0 failures\n"), out
 
 
-@pytest.mark.parametrize("old,new", [
+@pytest.mark.parametrize("header,old,new", [
     # a batch of whole steps one step too long for the ring window
-    ("return s < 2 ? 1 : s > max_steps ? max_steps : (int)s;",
+    ("index_map.h", "return s < 2 ? 1 : s > max_steps ? max_steps : (int)s;",
      "return s < 2 ? 1 : s > max_steps ? max_steps + 1 : (int)s + 1;"),
     # the step of a lane slot changing one slot early
-    ("*step = (int)(v / len);", "*step = (int)((v + 1) / len);"),
+    ("index_map.h", "*step = (int)(v / len);", "*step = (int)((v + 1) / len);"),
+    # LL's 512-lane form from one step more per channel than the rule says
+    ("stream_plan.h", "steps_per_channel >= kFifoNarrowSteps)",
+     "steps_per_channel > kFifoNarrowSteps)"),
+    # a pair per 2,048 payload bytes instead of 2,048 items
+    ("stream_plan.h", "int64_t by_work = bytes / per_item / kFifoItemsPerPair;",
+     "int64_t by_work = bytes / kFifoItemsPerPair;"),
+    # whole-step batches on channels that carry a single step
+    ("stream_plan.h", "if (fifo_steps_per_channel(n, step_bytes, channels) < 2 ||",
+     "if (fifo_steps_per_channel(n, step_bytes, channels) < 1 ||"),
 ])
-def test_the_slice_check_catches_planted_batch_mistakes(tmp_path, old, new):
-    """Plant a mistake in a copy of the batch-of-steps functions and make
-    sure tests/fifo_slice_check.cpp reports it."""
+def test_the_slice_check_catches_planted_batch_and_plan_mistakes(tmp_path, header, old, new):
+    """Plant a mistake in a copy of the batch-of-steps functions or of the
+    launch plan and make sure tests/fifo_slice_check.cpp reports it."""
     if shutil.which("g++") is None:
         pytest.skip("g++ not available")
-    src = open(os.path.join(HERE, "..", "ar_rmsnorm_amd", "csrc", "index_map.h")).read()
-    assert src.count(old) == 1
+    csrc = os.path.join(HERE, "..", "ar_rmsnorm_amd", "csrc")
     bad_dir = tmp_path / "ar_rmsnorm_amd" / "csrc"
     bad_dir.mkdir(parents=True)
-    (bad_dir / "index_map.h").write_text(src.replace(old, new))
+    for name in ("index_map.h", "stream_plan.h"):
+        src = open(os.path.join(csrc, name)).read()
+        if name == header:
+            assert src.count(old) == 1
+            src = src.replace(old, new)
+        (bad_dir / name).write_text(src)
     tests_dir = tmp_path / "tests"
     tests_dir.mkdir()
     shutil.copy(os.path.join(HERE, "fifo_slice_check.cpp"), tests_dir)
