@@ -97,6 +97,45 @@ def test_stream_bench_configurations(gpu, name, step, channels):
     f.run(src, cont=True)
 
 
+@pytest.mark.parametrize("name,step,channels", [("ll", 32768, 32), ("ll", 32768, 128),
+                                                ("ll128", 576000, 32), ("ll128", 576000, 128),
+                                                ("simple", 524288, 32),
+                                                ("simple", 524288, 128)])
+def test_stream_bench_configurations_over_many_calls(gpu, name, step, channels):
+    """The bench rows' configurations over 100 calls each, as the bench runs
+    them (back to back on one set of rings, each call from the stored step):
+    a graph of 20 calls, each into its own output, replayed 5 times with the
+    outputs cleared in between; every call must deliver the oracle's payload
+    bit for bit with no failed wait."""
+    proto, n, calls = PROTOS[name], synth.WIRE["n"], 20
+    src = synth.wire(n)[0]
+    want, _ = orc.fifo_stream(proto, src, channels, step, 0)
+    want = torch.from_numpy(want).to(gpu).view(torch.int32)
+    f = Fifo(proto, step, channels, gpu)
+    d = torch.from_numpy(src).to(gpu)
+    outs = [torch.zeros(n, dtype=torch.float32, device=gpu) for _ in range(calls)]
+    f.launch(d, outs[0], n, cont=True)      # warm-up call outside the graph
+    sync()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for o in outs:
+            f.launch(d, o, n, cont=True)
+    torch.cuda.current_stream().wait_stream(s)
+    sync()
+    for r in range(5):
+        for o in outs:
+            o.zero_()
+        sync()
+        g.replay()
+        sync()
+        assert int(f.errors.item()) == 0, f"replay {r}: a wait timed out"
+        bad = [i for i, o in enumerate(outs) if not torch.equal(o.view(torch.int32), want)]
+        assert not bad, f"replay {r}: calls {bad} delivered wrong payload"
+    del g
+
+
 def test_stream_plans_of_the_bench_rows(gpu):
     """The launch shapes the bench rows run with (lanes, pairs per channel,
     whole steps per LL batch) on a 256-CU MI355X: 32 channels take four
