@@ -942,6 +942,36 @@ __device__ void produce_ll_steps(const StreamArgs &a, int c, int pair, int p, in
     }
 }
 
+// Before a consumer's first batch.  Its producer starts in the same launch
+// at the same moment, so a first look at the batch would find its lines not
+// yet written and read them all twice.  Instead the first lane of each
+// wavefront polls the wavefront's last line slot of the batch (the last the
+// producer's wavefront stores) until it holds the batch's flags, then the
+// wavefront reads the batch (bounded; a batch whose last slot carries no
+// line, or a wait that runs out, goes on to the usual validation).
+template <int T>
+__device__ __forceinline__ void ll_await_last_line(const StreamArgs &a, const LLSteps<T> &m,
+                                                   const LLBatch &b)
+{
+    constexpr int u = kBatchOf<T> - 1;
+    const bool has = ll_has(m, b, u);
+    const uint32_t off = ll_off(a, m, b, u), f = ll_flag(m, b, u);
+    const int lead = __builtin_amdgcn_readfirstlane((int)threadIdx.x);
+    for (uint32_t s = 0; s < a.max_spins; ++s) {
+        respin();
+        int hit = 1;
+        if ((int)threadIdx.x == lead && has) {
+            const u32x4 x = load16_sys(m.ring, off);
+            hit = x.y == f && x.w == f ? 1 : 0;
+        }
+        if (__builtin_amdgcn_readfirstlane(hit))
+            break;
+        if (s % kAbortCheck == 0 && aborted(a.errors))
+            break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
 template <int T, bool LOCAL>
 __device__ void consume_ll_steps(const StreamArgs &a, int c, int pair, int p, int64_t s0,
                                  int64_t steps, uint64_t first)
@@ -952,6 +982,7 @@ __device__ void consume_ll_steps(const StreamArgs &a, int c, int pair, int p, in
     const int S = a.batch_steps;
     LLBatch b = ll_batch<T>(a, m, s0, first, 0);
     u32x4 v[kBatchOf<T>], lv[kBatchOf<T>];
+    ll_await_last_line<T>(a, m, b);
     ll_steps_load<T, LOCAL>(a, m, b, v, lv);
     bool failed = false;
     for (int64_t j0 = 0;; j0 += S) {

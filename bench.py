@@ -135,8 +135,8 @@ def profiled_headline(source_hash: str, nbytes: int):
     return {"source": "profiles/hot_path_kernel_trace.txt", "dispatches": n,
             "median_us": med, "mean_us": mean,
             "frac_from_mean": round(nbytes / (mean * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-            "note": "per-dispatch durations under rocprofv3, which spaces the dispatches "
-                    "apart: each starts on an idle GPU"}
+            "note": "per-dispatch durations under rocprofv3, which starts no dispatch "
+                    "before the previous one's traced end"}
 
 
 WIRE_COUNTERS = os.path.join(ROOT, "profiles", "wire_16Mi_counters.txt")
